@@ -1,0 +1,382 @@
+"""Pins of the fp64 oracle against what the pages and the mathematics fix.
+
+Each test names the part of the oracle it pins and the mistake it would
+catch.  Nothing here touches the GPU or the HIP library.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from paged_kv_cache_pa_amd import workloads as W
+from pa_testutil import embed_flex_example, load_golden, oracle_caches, to_np64
+
+
+def _paged_oracle(e):
+    return oracle.attention(e["q"], e["cu"], e["seqlens_kv"], e["block_table"],
+                            e["k_cache"], e["v_cache"], e["scale"], e["num_heads"],
+                            e["num_kv_heads"], e["block_size"])
+
+
+def _wl_inputs(wl, fill=np.nan):
+    vals = W.make_values(wl)
+    q, k_all, v_all = (to_np64(vals[n]) for n in ("q", "k_all", "v_all"))
+    kc, vc = oracle_caches(wl, k_all, v_all, fill)
+    return q, k_all, v_all, kc, vc
+
+
+def _run(wl, q, kc, vc, fn=oracle.attention, scale=None):
+    return fn(q, wl.cu_seqlens_q, wl.seqlens_kv, wl.block_table, kc, vc,
+              wl.scale if scale is None else scale, wl.num_heads, wl.num_kv_heads,
+              wl.block_size)
+
+
+# --- C1/C2: the FlexAttention page's printed examples -----------------------
+
+@pytest.mark.parametrize("name", ["flex_attention_basic.txt", "flex_attention_gqa.txt"])
+def test_printed_examples_dense(name):
+    """SDPA core, GQA mapping and the 1/sqrt(D) scale reading reproduce the
+    printed Y to 1e-6; scale 1 or 1/2 does not."""
+    g = load_golden(name)
+    y = oracle.flex_attention_dense(g["Q"], g["K"], g["V"])
+    assert np.abs(y - g["Y"]).max() <= 1e-6
+    for wrong in (1.0, 0.5):
+        y2 = oracle.flex_attention_dense(g["Q"], g["K"], g["V"], scale=wrong)
+        assert np.abs(y2 - g["Y"]).max() > 0.05
+
+
+@pytest.mark.parametrize("name", ["flex_attention_basic.txt", "flex_attention_gqa.txt"])
+@pytest.mark.parametrize("pad_to", [None, 64])
+def test_printed_examples_paged(name, pad_to):
+    """The paged path (block-table walk, packed Q, causal offset) reproduces
+    the printed Y when each query row is its own q_len=1 sequence; NaN in
+    the unused block and tail slots must not leak in."""
+    e = embed_flex_example(load_golden(name), pad_to=pad_to)
+    out = _paged_oracle(e)
+    assert np.isfinite(out).all()
+    assert np.abs(out - e["y"]).max() <= 1e-6
+
+
+def test_gqa_example_rejects_modulo_mapping():
+    """Mapping query head h to KV head h % Hk instead of floor(h / group)
+    misses the printed GQA output by more than 1."""
+    g = load_golden("flex_attention_gqa.txt")
+    k_mod = g["K"][:, [0, 1, 0, 1]]
+    v_mod = g["V"][:, [0, 1, 0, 1]]
+    y = oracle.flex_attention_dense(g["Q"], k_mod, v_mod)
+    assert np.abs(y - g["Y"]).max() > 1.0
+
+
+def test_shift_invariance_printed():
+    """Head 0 of the GQA example: the two query rows' scores differ by a
+    constant, and the printed (and oracle) outputs coincide."""
+    g = load_golden("flex_attention_gqa.txt")
+    assert np.abs(g["Y"][0, 0, 0] - g["Y"][0, 0, 1]).max() <= 1e-7
+    y = oracle.flex_attention_dense(g["Q"], g["K"], g["V"])
+    assert np.abs(y[0, 0, 0] - y[0, 0, 1]).max() <= 1e-12
+
+
+# --- C4/C5/C6: closed forms --------------------------------------------------
+
+def _one_seq(q_len, L, hq=4, hk=2, d=8, bs=4, seed=0, nb=None):
+    rng = np.random.default_rng(seed)
+    nb = nb or (-(-L // bs) + 2)
+    perm = rng.permutation(nb)
+    table = perm[None, : -(-L // bs)].astype(np.int32)
+    q = rng.uniform(-1, 1, (q_len, hq, d))
+    k_all = rng.uniform(-1, 1, (L, hk, d))
+    v_all = rng.uniform(-1, 1, (L, hk, d))
+    kc = np.full((nb, bs, hk, d), np.nan)
+    vc = np.full((nb, bs, hk, d), np.nan)
+    slots = [table[0, j // bs] * bs + j % bs for j in range(L)]
+    oracle.scatter_kv(k_all, v_all, slots, kc, vc, bs)
+    cu = np.array([0, q_len], dtype=np.int32)
+    return dict(q=q, k_all=k_all, v_all=v_all, kc=kc, vc=vc, table=table, cu=cu,
+                L=np.array([L], dtype=np.int32), hq=hq, hk=hk, bs=bs)
+
+
+def _att(s, q=None, scale=0.5, fn=oracle.attention):
+    return fn(s["q"] if q is None else q, s["cu"], s["L"], s["table"], s["kc"], s["vc"],
+              scale, s["hq"], s["hk"], s["bs"])
+
+
+def test_first_token_returns_its_value_row():
+    """q_len 1 with past 0: the only visible key is position 0, so every
+    head returns V row 0 of its KV head exactly."""
+    s = _one_seq(1, 1)
+    out = _att(s)
+    for h in range(4):
+        assert np.array_equal(out[0, h], s["v_all"][0, h // 2])
+
+
+@pytest.mark.parametrize("how", ["zero_q", "zero_scale"])
+def test_equal_scores_give_mean_of_visible_values(how):
+    """Equal scores: new row i (past 12, q_len 4) averages exactly the first
+    past+i+1 V rows; an off-by-one causal length fails this."""
+    s = _one_seq(4, 16, seed=3)
+    out = _att(s, q=np.zeros_like(s["q"])) if how == "zero_q" else _att(s, scale=0.0)
+    for i in range(4):
+        n = 12 + i + 1
+        for h in range(4):
+            np.testing.assert_allclose(out[i, h], s["v_all"][:n, h // 2].mean(axis=0),
+                                       rtol=0, atol=1e-12)
+
+
+def test_gqa_mapping_constant_values():
+    """V of KV head k is the constant k: output of query head h is floor(h/G)."""
+    hq, hk = 8, 2
+    s = _one_seq(3, 20, hq=hq, hk=hk, seed=5)
+    for blk in range(s["vc"].shape[0]):
+        for k in range(hk):
+            s["vc"][blk, :, k, :] = k
+    out = _att(s)
+    for h in range(hq):
+        np.testing.assert_allclose(out[:, h], h // (hq // hk), atol=1e-12)
+
+
+# --- C7: causality, both directions, and the clamp bug -----------------------
+
+def test_causality_no_leak_and_no_truncation():
+    """Perturbing keys beyond past+i leaves row i bitwise unchanged;
+    perturbing any key at or before past+i changes it."""
+    q_len, L = 5, 23
+    s = _one_seq(q_len, L, seed=7)
+    past = L - q_len
+    base = _att(s)
+    bs = s["bs"]
+    for j in range(L):
+        s2 = _one_seq(q_len, L, seed=7)
+        blk, off = s2["table"][0, j // bs], j % bs
+        s2["kc"][blk, off] += 0.5
+        s2["vc"][blk, off] += 0.5
+        out = _att(s2)
+        for i in range(q_len):
+            if j > past + i:
+                assert np.array_equal(out[i], base[i]), (i, j)
+            else:
+                assert np.abs(out[i] - base[i]).max() > 1e-6, (i, j)
+
+
+def test_clamp_bug_variant_disagrees_on_tiny_workload():
+    """The pre-fix past = clamp(L - max_q, 0) gives sequence 0 of the tiny
+    mixed batch (q_len 1, past 28; max q_len 4) a past of 25: the outputs
+    differ there, and agree on sequence 1 (whose q_len is the maximum)."""
+    wl = W.tiny()
+    q, _, _, kc, vc = _wl_inputs(wl)
+    good = _run(wl, q, kc, vc)
+    bad = _run(wl, q, kc, vc, fn=oracle.attention_buggy_clamp)
+    assert np.abs(good[0] - bad[0]).max() > 1e-3
+    assert np.array_equal(good[1:], bad[1:])
+
+
+# --- C8: paging is invisible -------------------------------------------------
+
+def _contiguous_reference(wl, q, k_all, v_all):
+    """Contiguous (unpaged) causal GQA SDPA, straight from the all-positions
+    K/V rows without any block table."""
+    cu, kv_cu = wl.cu_seqlens_q, wl.kv_cu
+    G = wl.num_heads // wl.num_kv_heads
+    out = np.zeros_like(q)
+    for b in range(wl.num_seqs):
+        ql, L = int(wl.q_lens[b]), int(wl.seqlens_kv[b])
+        K = k_all[kv_cu[b]:kv_cu[b + 1]]
+        V = v_all[kv_cu[b]:kv_cu[b + 1]]
+        vis = np.arange(L)[None, :] <= (L - ql) + np.arange(ql)[:, None]
+        for h in range(wl.num_heads):
+            out[cu[b]:cu[b + 1], h] = oracle.sdpa(q[cu[b]:cu[b + 1], h], K[:, h // G],
+                                                  V[:, h // G], wl.scale, vis)
+    return out
+
+
+@pytest.mark.parametrize("case", [0, 5, 40, 80])
+def test_paged_equals_contiguous(case):
+    """Paged oracle == contiguous SDPA (1e-12) and == torch CPU float64
+    scaled_dot_product_attention with an explicit boolean mask."""
+    qs, ls, hq, hk = W.small_cases()[case]
+    wl = W.small(qs, ls, hq, hk, seed=100 + case)
+    q, k_all, v_all, kc, vc = _wl_inputs(wl)
+    paged = _run(wl, q, kc, vc)
+    contig = _contiguous_reference(wl, q, k_all, v_all)
+    assert np.abs(paged - contig).max() <= 1e-12
+    G = hq // hk
+    cu, kv_cu = wl.cu_seqlens_q, wl.kv_cu
+    for b in range(wl.num_seqs):
+        ql, L = int(wl.q_lens[b]), int(wl.seqlens_kv[b])
+        qt = torch.from_numpy(q[cu[b]:cu[b + 1]].transpose(1, 0, 2).copy())
+        kt = torch.from_numpy(np.repeat(k_all[kv_cu[b]:kv_cu[b + 1]], G, axis=1).transpose(1, 0, 2).copy())
+        vt = torch.from_numpy(np.repeat(v_all[kv_cu[b]:kv_cu[b + 1]], G, axis=1).transpose(1, 0, 2).copy())
+        mask = torch.from_numpy(np.arange(L)[None, :] <= (L - ql) + np.arange(ql)[:, None])
+        ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=mask,
+                                                               scale=float(np.float32(wl.scale)))
+        assert np.abs(ref.numpy().transpose(1, 0, 2) - paged[cu[b]:cu[b + 1]]).max() <= 1e-12
+
+
+def test_block_permutation_invariance():
+    """Two different physical placements of the same sequences give equal
+    outputs."""
+    wl = W.tiny()
+    q, k_all, v_all, kc, vc = _wl_inputs(wl)
+    out1 = _run(wl, q, kc, vc)
+    perm = np.random.default_rng(9).permutation(wl.num_blocks)
+    wl2 = W.tiny()
+    wl2.block_table = np.where(wl.block_table >= 0, perm[wl.block_table], -1).astype(np.int32)
+    kc2, vc2 = oracle_caches(wl2, k_all, v_all)
+    out2 = _run(wl2, q, kc2, vc2)
+    assert np.array_equal(out1, out2)
+
+
+# --- C9/C10/C11/C12 ----------------------------------------------------------
+
+def test_split_combine_equals_unsplit():
+    """Log-sum-exp merge of partial states over random key partitions
+    (including empty and fully-masked parts) equals the unsplit output."""
+    rng = np.random.default_rng(11)
+    for trial in range(20):
+        n, L, d = 6, int(rng.integers(1, 60)), 16
+        q = rng.uniform(-1, 1, (n, d))
+        k = rng.uniform(-1, 1, (L, d))
+        v = rng.uniform(-1, 1, (L, d))
+        past = L - n if L >= n else 0
+        vis = np.arange(L)[None, :] <= past + np.arange(n)[:, None]
+        vis[:, 0] = True
+        full = oracle.sdpa(q, k, v, 0.7, vis)
+        cuts = np.sort(rng.integers(0, L + 1, size=int(rng.integers(0, 5))))
+        edges = np.concatenate([[0], cuts, [L]])
+        parts = [oracle.attention_partial(q, k[a:b], v[a:b], 0.7, vis[:, a:b])
+                 for a, b in zip(edges[:-1], edges[1:])]
+        assert np.abs(oracle.combine_partials(parts) - full).max() <= 1e-12
+
+
+def test_incremental_decoding_equals_chunk():
+    """A q_len=n chunk equals n successive q_len=1 steps with growing KV."""
+    n, L = 6, 30
+    s = _one_seq(n, L, seed=13)
+    chunk = _att(s)
+    past = L - n
+    for i in range(n):
+        step = oracle.attention(s["q"][i:i + 1], np.array([0, 1]), np.array([past + i + 1]),
+                                s["table"], s["kc"], s["vc"], 0.5, s["hq"], s["hk"], s["bs"])
+        assert np.abs(step[0] - chunk[i]).max() <= 1e-12
+
+
+def test_outputs_within_visible_value_range():
+    """Each output coordinate is a convex combination of visible V rows."""
+    wl = W.small((16, 4), (64, 32), 8, 2, seed=21)
+    q, k_all, v_all, kc, vc = _wl_inputs(wl)
+    out = _run(wl, q, kc, vc)
+    cu, kv_cu = wl.cu_seqlens_q, wl.kv_cu
+    G = wl.num_heads // wl.num_kv_heads
+    for b in range(wl.num_seqs):
+        ql, L = int(wl.q_lens[b]), int(wl.seqlens_kv[b])
+        V = v_all[kv_cu[b]:kv_cu[b + 1]]
+        for i in range(ql):
+            vis = V[: L - ql + i + 1]
+            for h in range(wl.num_heads):
+                o = out[cu[b] + i, h]
+                assert np.all(o <= vis[:, h // G].max(axis=0) + 1e-12)
+                assert np.all(o >= vis[:, h // G].min(axis=0) - 1e-12)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_bruteforce_loops_equal_vectorised(seed):
+    """Pure-loop oracle == vectorised oracle on tiny random batches,
+    including empty sequences (q_len 0)."""
+    rng = np.random.default_rng(seed)
+    B = int(rng.integers(1, 4))
+    d = int(rng.choice([2, 8]))
+    hk = int(rng.choice([1, 2]))
+    hq = hk * int(rng.choice([1, 2, 3]))
+    bs = int(rng.choice([2, 4, 8]))
+    q_lens = rng.integers(0, 5, size=B)
+    lens = q_lens + rng.integers(0, 36, size=B)
+    lens = np.maximum(lens, 1)
+    mb = int(max(-(-lens // bs)))
+    nb = int(sum(-(-lens // bs))) + 3
+    perm = rng.permutation(nb)
+    table = np.full((B, mb), -1, dtype=np.int32)
+    at = 0
+    for b in range(B):
+        k = -(-int(lens[b]) // bs)
+        table[b, :k] = perm[at:at + k]
+        at += k
+    kc = rng.uniform(-1, 1, (nb, bs, hk, d))
+    vc = rng.uniform(-1, 1, (nb, bs, hk, d))
+    q_lens[0] = max(int(q_lens[0]), 1)          # at least one token overall
+    cu = np.concatenate([[0], np.cumsum(q_lens)]).astype(np.int32)
+    lens = np.maximum(lens, q_lens)
+    q = rng.uniform(-1, 1, (int(cu[-1]), hq, d))
+    args = (q, cu, lens, table, kc, vc, 0.37, hq, hk, bs)
+    vec = oracle.attention(*args)
+    loop = oracle.attention_loops(*args)
+    assert vec.shape == (int(cu[-1]), hq, d)
+    assert np.abs(vec - loop).max() <= 1e-12
+
+
+# --- C13: scatter and slot addressing ----------------------------------------
+
+def test_scatter_round_trip_and_sentinels():
+    """Scatter is a bit copy: reading back through the block table returns
+    the inputs, and untouched NaN sentinel slots keep their bit pattern;
+    negative slots write nothing."""
+    wl = W.tiny()
+    vals = W.make_values(wl)
+    k_bits = vals["k_all"].view(torch.int16).numpy().view(np.uint16)
+    v_bits = vals["v_all"].view(torch.int16).numpy().view(np.uint16)
+    sentinel = np.uint16(0x7E01)             # a quiet-NaN payload
+    shape = (wl.num_blocks, wl.block_size, wl.num_kv_heads, wl.head_size)
+    kc = np.full(shape, sentinel, dtype=np.uint16)
+    vc = np.full(shape, sentinel, dtype=np.uint16)
+    slots = wl.kv_slots.astype(np.int64).copy()
+    slots[3] = -1
+    oracle.scatter_kv(k_bits, v_bits, slots, kc, vc, wl.block_size)
+    kv_cu = wl.kv_cu
+    for b in range(wl.num_seqs):
+        got = oracle.gather_sequence(kc, wl.block_table[b], wl.seqlens_kv[b], wl.block_size)
+        want = k_bits[kv_cu[b]:kv_cu[b + 1]]
+        if b == 0:
+            assert np.all(got[3] == sentinel)
+            got, want = np.delete(got, 3, 0), np.delete(want, 3, 0)
+        assert np.array_equal(got, want)
+    written = np.zeros(wl.num_blocks * wl.block_size, dtype=bool)
+    written[slots[slots >= 0]] = True
+    flat = kc.reshape(-1, wl.num_kv_heads * wl.head_size)
+    assert np.all(flat[~written] == sentinel)
+
+
+@pytest.mark.parametrize("make", [W.tiny, lambda: W.small((16, 1), (64, 32), 8, 2),
+                                  lambda: W.prefill(num_seqs=3)])
+def test_generator_slots_follow_block_table(make):
+    """The generator's new-token slots equal the pages' in-op addressing
+    block_table[b][pos // bs] * bs + pos % bs with pos = past_b + i."""
+    wl = make()
+    want = oracle.slots_from_block_table(wl.cu_seqlens_q, wl.seqlens_kv, wl.block_table,
+                                         wl.block_size)
+    assert np.array_equal(wl.slot_mapping.astype(np.int64), want)
+
+
+def test_token_to_sequence_scan_skips_empty_sequences():
+    cu = [0, 0, 3, 3, 3, 5]
+    assert [oracle.seq_of_token(cu, t) for t in range(5)] == [1, 1, 1, 4, 4]
+    with pytest.raises(ValueError):
+        oracle.seq_of_token(cu, 5)
+
+
+def test_validate_metadata_flags_each_violation():
+    wl = W.tiny()
+    ok = oracle.validate_metadata(wl.cu_seqlens_q, wl.seqlens_kv, wl.block_table,
+                                  wl.num_blocks, wl.block_size, wl.num_tokens, wl.slot_mapping)
+    assert ok == []
+    bad_cu = wl.cu_seqlens_q.copy(); bad_cu[0] = 1
+    assert oracle.validate_metadata(bad_cu, wl.seqlens_kv, wl.block_table, wl.num_blocks,
+                                    wl.block_size)
+    short = wl.seqlens_kv.copy(); short[1] = 2
+    assert oracle.validate_metadata(wl.cu_seqlens_q, short, wl.block_table, wl.num_blocks,
+                                    wl.block_size)
+    tbl = wl.block_table.copy(); tbl[0, 1] = wl.num_blocks
+    assert oracle.validate_metadata(wl.cu_seqlens_q, wl.seqlens_kv, tbl, wl.num_blocks,
+                                    wl.block_size)
+    dup = wl.slot_mapping.copy(); dup[1] = dup[2]
+    assert oracle.validate_metadata(wl.cu_seqlens_q, wl.seqlens_kv, wl.block_table,
+                                    wl.num_blocks, wl.block_size, slot_mapping=dup)
