@@ -1,0 +1,291 @@
+#!/usr/bin/env python3
+"""Benchmark of the paged-KV-cache attention hot path on one MI355X.
+
+One step = pa_scatter_kv of the step's new K/V rows + pa_attention over the
+whole continuous batch, on the large mixed workload (16 prefill chunks of
+512 tokens + 240 decodes with 1k-32k contexts, 64/8 heads, D 128, block 16,
+bf16).  Inputs are resident in HBM before the timed region.  The line also
+carries the pure-decode and chunked-prefill workloads' figures, the
+roofline of the dominant kernel, and the fp64 oracle timed on host cores.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload mixed|decode|prefill]
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK = 8.0e12          # B/s, MI355X HBM3E
+MFMA_PEAK = 2.5e15         # FLOP/s, dense fp16/bf16 matrix cores
+ES = 2                     # bytes per fp16/bf16 element
+WORKLOADS = {"tiny": 1, "small": 2, "decode": 3, "prefill": 4, "mixed": 5}
+
+
+# ------------------------------------------------------------- accounting
+def attention_work(wl, sel=None):
+    """Algorithmic bytes and FLOPs of pa_attention over the sequences in
+    ``sel``: every visible K/V element once, Q, O, block ids and length
+    metadata; FLOPs = 4*D per visible (query row, key, head)."""
+    q = wl.q_lens.astype(np.int64)
+    L = wl.seqlens_kv.astype(np.int64)
+    if sel is None:
+        sel = np.ones(len(q), dtype=bool)
+    q, L = q[sel], L[sel]
+    past = L - q
+    D, hq, hk, bs = wl.head_size, wl.num_heads, wl.num_kv_heads, wl.block_size
+    kv = int((L * hk * D * 2 * ES).sum())
+    qo = int(2 * q.sum() * hq * D * ES)
+    ids = int((-(-L // bs)).sum() * 4 + (2 * len(q) + 1) * 4)
+    flops = int(4 * D * hq * (q * past + q * (q + 1) // 2).sum())
+    return kv + qo + ids, flops
+
+
+def scatter_work(wl):
+    T = wl.num_tokens
+    return 2 * 2 * T * wl.num_kv_heads * wl.head_size * ES + 4 * T
+
+
+def roofline_time(nbytes, flops):
+    return max(nbytes / HBM_PEAK, flops / MFMA_PEAK)
+
+
+# ------------------------------------------------------------- GPU side
+def setup(wl, torch, pa, W):
+    vals = W.make_values(wl, device="cuda", backend="torch")
+    dt = W.torch_dtype(wl)
+    shape = (wl.num_blocks, wl.block_size, wl.num_kv_heads, wl.head_size)
+    kc = torch.zeros(shape, dtype=dt, device="cuda")
+    vc = torch.zeros_like(kc)
+    slots_all = torch.from_numpy(wl.kv_slots).cuda()
+    pa.pa_scatter_kv(vals["k_all"], vals["v_all"], slots_all, kc, vc)
+    new_rows = torch.from_numpy(wl.new_rows).cuda()
+    st = dict(q=vals["q"], k_new=vals["k_all"][new_rows].contiguous(),
+              v_new=vals["v_all"][new_rows].contiguous(), kc=kc, vc=vc,
+              slots=torch.from_numpy(wl.slot_mapping.astype(np.int32)).cuda(),
+              cu=torch.from_numpy(wl.cu_seqlens_q).cuda(),
+              lens=torch.from_numpy(wl.seqlens_kv.astype(np.int32)).cuda(),
+              table=torch.from_numpy(wl.block_table.astype(np.int32)).cuda(), vals=vals)
+    st["out"] = torch.empty((wl.num_tokens, wl.num_heads, wl.head_size), dtype=dt, device="cuda")
+    n = pa.pa_attention_workspace_size(wl.num_seqs, wl.num_tokens, wl.max_blocks_per_seq,
+                                       wl.num_heads, wl.num_kv_heads, wl.head_size,
+                                       wl.block_size)
+    st["ws"] = torch.empty(max(n, 256), dtype=torch.uint8, device="cuda")
+    torch.cuda.synchronize()
+    return st
+
+
+def step(wl, st, pa):
+    pa.pa_scatter_kv(st["k_new"], st["v_new"], st["slots"], st["kc"], st["vc"])
+    pa.pa_attention(st["q"], st["cu"], st["lens"], st["table"], st["kc"], st["vc"], wl.scale,
+                    wl.num_heads, wl.num_kv_heads, out=st["out"], workspace=st["ws"])
+
+
+def time_workload(wl, steps, warmup, torch, pa, W):
+    st = setup(wl, torch, pa, W)
+    for _ in range(warmup):
+        step(wl, st, pa)
+    torch.cuda.synchronize()
+    pa.profile_read()                       # drop anything recorded earlier
+    pa.profile_enable(True)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(steps):
+        step(wl, st, pa)
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    pa.profile_enable(False)
+    kern = pa.profile_read()
+    ms = e0.elapsed_time(e1) / steps
+    per_kernel = {k: (v[0] / v[1] if v[1] else 0.0) for k, v in kern.items()}
+    del st
+    torch.cuda.empty_cache()
+    return ms, wall / steps * 1e3, per_kernel
+
+
+def summarize(wl, ms, per_kernel):
+    """Throughputs of one step and of its decode / prefill kernels."""
+    att_bytes, att_flops = attention_work(wl)
+    nbytes = att_bytes + scatter_work(wl)
+    t = ms * 1e-3
+    dec_sel = wl.q_lens * (wl.num_heads // wl.num_kv_heads) <= 16
+    dec_bytes, dec_flops = attention_work(wl, dec_sel & (wl.q_lens > 0))
+    pf_bytes, pf_flops = attention_work(wl, ~dec_sel)
+    r = {
+        "ms_per_step": ms,
+        "roofline_pct": 100.0 * roofline_time(nbytes, att_flops) / t,
+        "tokens_per_s": wl.num_tokens / t,
+        "alg_bytes": nbytes,
+        "alg_flops": att_flops,
+        "kernel_ms": {k: round(v, 5) for k, v in per_kernel.items()},
+    }
+    if dec_bytes and per_kernel.get("decode"):
+        r["decode_TBps"] = dec_bytes / (per_kernel["decode"] * 1e-3) / 1e12
+        r["decode_hbm_frac"] = r["decode_TBps"] * 1e12 / HBM_PEAK
+        r["decode_alg_bytes"] = dec_bytes
+    if pf_flops and per_kernel.get("prefill"):
+        r["prefill_TFLOPs"] = pf_flops / (per_kernel["prefill"] * 1e-3) / 1e12
+        r["prefill_mfma_frac"] = r["prefill_TFLOPs"] * 1e12 / MFMA_PEAK
+        r["prefill_alg_flops"] = pf_flops
+    return r
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "paged_kv_cache_pa_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch recorded from rocprofv3 counters for this kernel
+    source (profiles/traffic.json); None when absent or stale."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        rec = json.load(open(path))
+    except (OSError, ValueError):
+        return None
+    ent = rec.get(f"{workload}:{kernel}")
+    if not ent or ent.get("source_hash") != kernel_source_hash():
+        return None
+    return ent.get("bytes_per_launch")
+
+
+# ------------------------------------------------------------- CPU baseline
+def cpu_baseline(wl, W, torch, budget_s=20.0):
+    """The fp64 oracle (as it stands) on a bounded sample of the workload:
+    the first decode sequences and, if any, one prefill chunk; reported in
+    the metric's unit and as tokens/s."""
+    import oracle
+    f64 = lambda t: t.float().cpu().numpy().astype(np.float64)  # noqa: E731
+    vals = W.make_values(wl, device="cuda", backend="torch")
+    kv_cu, cu = wl.kv_cu, wl.cu_seqlens_q
+    dec = [int(b) for b in np.flatnonzero(wl.q_lens == 1)]
+    pre = [int(b) for b in np.flatnonzero(wl.q_lens > 1)]
+    picks = pre[:1] + dec[:16]
+    shape = (wl.block_size, wl.num_kv_heads, wl.head_size)
+    kc, vc = {}, {}
+    for b in picks:
+        nb = -(-int(wl.seqlens_kv[b]) // wl.block_size)
+        for x in wl.block_table[b, :nb]:
+            kc.setdefault(int(x), np.zeros(shape))
+            vc.setdefault(int(x), np.zeros(shape))
+        oracle.scatter_kv(f64(vals["k_all"][kv_cu[b]:kv_cu[b + 1]]),
+                          f64(vals["v_all"][kv_cu[b]:kv_cu[b + 1]]),
+                          wl.kv_slots[kv_cu[b]:kv_cu[b + 1]], kc, vc, wl.block_size)
+    q_parts = [f64(vals["q"][cu[b]:cu[b + 1]]) for b in picks]
+    del vals
+    torch.cuda.empty_cache()
+    q_lens = np.array([wl.q_lens[b] for b in picks], dtype=np.int32)
+    sub_cu = np.concatenate([[0], np.cumsum(q_lens)]).astype(np.int32)
+    sub_lens = np.array([wl.seqlens_kv[b] for b in picks], dtype=np.int32)
+    sub_table = wl.block_table[picks]
+    q = np.concatenate(q_parts, axis=0)
+    t0 = time.perf_counter()
+    oracle.attention(q, sub_cu, sub_lens, sub_table, kc, vc, wl.scale, wl.num_heads,
+                     wl.num_kv_heads, wl.block_size)
+    t = time.perf_counter() - t0
+    sel = np.zeros(wl.num_seqs, dtype=bool)
+    sel[picks] = True
+    nbytes, flops = attention_work(wl, sel)
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:  # noqa: BLE001
+        blas = None
+    cores = len(os.sched_getaffinity(0))
+    return {"value": 100.0 * roofline_time(nbytes, flops) / t, "unit": "% of MI355X roofline",
+            "tokens_per_s": float(q_lens.sum()) / t, "seconds": t,
+            "cores": int(blas or cores), "host_cpus": os.cpu_count(), "affinity_cpus": cores,
+            "kind": "oracle",
+            "sample": f"fp64 NumPy oracle, pa_attention only, on {len(pre[:1])} prefill chunk(s) "
+                      f"of 512 tokens + {len(dec[:16])} decode sequences of the same workload "
+                      f"({int(q_lens.sum())} query tokens)"}
+
+
+# ------------------------------------------------------------- main
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="mixed", choices=sorted(WORKLOADS))
+    ap.add_argument("--no-extra", action="store_true", help="skip the decode/prefill figures")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(the paged attention hot path is measured on a single MI355X).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import paged_kv_cache_pa_amd as pa
+    from paged_kv_cache_pa_amd import workloads as W
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    pa._lib.lib()           # fail loudly when the HIP library is missing
+
+    wl = W.by_index(WORKLOADS[args.workload])
+    ms, wall_ms, per_kernel = time_workload(wl, args.steps, args.warmup, torch, pa, W)
+    head = summarize(wl, ms, per_kernel)
+    dominant = max(("decode", "prefill"), key=lambda k: per_kernel.get(k, 0.0))
+    if dominant == "decode":
+        ach = head.get("decode_TBps", 0.0) * 1e3
+        roof = {"bound": "hbm", "kernel": "decode_kernel", "achieved": ach, "peak": 8000.0,
+                "unit": "GB/s", "frac": ach / 8000.0,
+                "avg_launch_ms": per_kernel.get("decode", 0.0),
+                "alg_bytes_per_launch": head.get("decode_alg_bytes")}
+    else:
+        ach = head.get("prefill_TFLOPs", 0.0)
+        roof = {"bound": "mfma", "kernel": "prefill_kernel", "achieved": ach, "peak": 2500.0,
+                "unit": "TFLOP/s", "frac": ach / 2500.0,
+                "avg_launch_ms": per_kernel.get("prefill", 0.0),
+                "alg_flops_per_launch": head.get("prefill_alg_flops")}
+    roof["traffic"] = measured_traffic(roof["kernel"], args.workload)
+
+    extra = {}
+    if not args.no_extra and args.workload == "mixed":
+        for name in ("decode", "prefill"):
+            w2 = W.by_index(WORKLOADS[name])
+            m2, _, k2 = time_workload(w2, max(5, args.steps // 2), 3, torch, pa, W)
+            extra[name] = summarize(w2, m2, k2)
+            extra[name]["workload"] = w2.name
+
+    line = {
+        "metric": "paged-attn decode HBM TB/s + prefill TFLOP/s, % of MI355X roofline",
+        "value": head["roofline_pct"],
+        "unit": "% of MI355X roofline (max(bytes/8TB/s, flops/2.5PF) / step time)",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms, "wall_ms_per_step": wall_ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": wl.dtype, "data": "synthetic",
+        "config": {"workload": wl.name, "num_seqs": wl.num_seqs, "num_tokens": wl.num_tokens,
+                   "step": "pa_scatter_kv(new tokens) + pa_attention(whole batch)",
+                   "parallelism": "single GPU"},
+        "tokens_per_s": head["tokens_per_s"],
+        "decode_TBps": head.get("decode_TBps"),
+        "prefill_TFLOPs": head.get("prefill_TFLOPs"),
+        "kernel_ms": head["kernel_ms"],
+        "roofline": roof,
+        "extra": extra,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(wl, W, torch)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,204 @@
+/*
+ * pa.h - C ABI of the MI355X (gfx950) paged-KV-cache attention library.
+ *
+ * The library computes scaled-dot-product attention softmax(Q K^T * scale) V
+ * for continuous batching: new query tokens of many sequences arrive packed
+ * back to back, each sequence keeps its keys/values in a paged KV cache that
+ * is addressed through a per-sequence block table, query head h reads KV head
+ * floor(h / (num_heads / num_kv_heads)) (grouped-query attention), and new
+ * query row i of sequence b sees KV positions 0 .. past_b + i, where
+ * past_b = seqlens_kv[b] - q_len_b.
+ *
+ * Sources: onnxruntime pull request #31611, "[WebGPU] Initial PagedAttention
+ * implementation (1/n)" - sections "Description" (scatter of new K/V into the
+ * paged cache, packed varlen queries, packed (token_count, hidden_size)
+ * output) and "FlashAttention: optional seqlens_q input" (per-sequence past
+ * length = total KV length minus that sequence's own query length), and the
+ * maintainer review's list of checked items (token-to-sequence scan, causal
+ * length past + q + 1, scatter block addressing, GQA mapping); onnx-light
+ * operator page "FlexAttention" - sections "FlexAttention Computation" and
+ * "Grouped Query Attention (GQA)".
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Every pointer argument is DEVICE memory owned by the caller, except the
+ *   output arguments of pa_profile_read / pa_validate_metadata, which are
+ *   host memory.  The library allocates no device memory and keeps no
+ *   pointer after a call returns.
+ * - `stream` is a hipStream_t passed as void*; NULL is the null stream.  All
+ *   kernels are enqueued on it; pa_scatter_kv and pa_attention never
+ *   synchronise the host (no device-to-host copies).
+ * - Element type `dtype`: PA_F16 (IEEE binary16) or PA_BF16 (bfloat16) for
+ *   Q, new K/V, the caches and the output.  Arithmetic is fp32: QK^T and
+ *   P.V accumulate in fp32 (matrix cores), the softmax runs in fp32, P is
+ *   rounded to dtype for the P.V product, and the output is rounded to
+ *   dtype with round-to-nearest-even.
+ * - Cache layout (both caches): [num_blocks, block_size, num_kv_heads,
+ *   head_size], row-major; cache slot s = block * block_size + offset holds
+ *   one token's num_kv_heads * head_size row.
+ * - Index arrays are int32.  All address arithmetic is 64-bit.
+ * - Errors: argument checks happen on the host before any HIP call and
+ *   return PA_ERR_INVALID_ARGUMENT / PA_ERR_NOT_IMPLEMENTED /
+ *   PA_ERR_WORKSPACE_TOO_SMALL; a failed kernel launch returns PA_ERR_HIP.
+ *   pa_last_error() gives a message for the calling thread's last failure.
+ *   Device-resident metadata (cu_seqlens_q, seqlens_kv, block_table,
+ *   slot_mapping) are trusted preconditions; pa_validate_metadata checks
+ *   them (debug/test use only).  No C++ exception crosses this ABI.
+ * - Calls are stateless and re-entrant: concurrent calls on different
+ *   streams with different workspaces do not interfere.
+ */
+#ifndef PA_H_
+#define PA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum pa_status {
+  PA_OK = 0,
+  PA_ERR_INVALID_ARGUMENT = 1,
+  PA_ERR_NOT_IMPLEMENTED = 2,
+  PA_ERR_WORKSPACE_TOO_SMALL = 3,
+  PA_ERR_HIP = 4
+} pa_status_t;
+
+typedef enum pa_dtype { PA_F16 = 0, PA_BF16 = 1 } pa_dtype_t;
+
+/*
+ * pa_scatter_kv - write this step's new K/V rows into the paged caches.
+ *
+ * Defines: the scatter step of "[WebGPU] Initial PagedAttention
+ * implementation (1/n)", section "Description" (new keys/values go into
+ * their block slots before attention reads the cache).
+ *
+ *   for t in [0, num_tokens): s = slot_mapping[t]; if s >= 0:
+ *       k_cache[s / block_size][s % block_size][:][:] = k_new[t][:][:]
+ *       v_cache[s / block_size][s % block_size][:][:] = v_new[t][:][:]
+ *
+ * k_new, v_new   [num_tokens, num_kv_heads, head_size] dtype, read only.
+ * slot_mapping   [num_tokens] int32; a negative slot skips the token.
+ *                Non-negative slots must be unique and < num_blocks *
+ *                block_size (precondition; duplicates race).
+ * k_cache,
+ * v_cache        [num_blocks, block_size, num_kv_heads, head_size] dtype,
+ *                updated in place.  Bytes are copied verbatim (bit-exact).
+ * Limits: head_size % 8 == 0, num_kv_heads >= 1, block_size >= 1,
+ * num_blocks * block_size <= INT32_MAX.  num_tokens == 0 returns PA_OK
+ * without launching.
+ */
+pa_status_t pa_scatter_kv(const void* k_new, const void* v_new,
+                          const int32_t* slot_mapping, void* k_cache,
+                          void* v_cache, int64_t num_tokens,
+                          int64_t num_blocks, int32_t num_kv_heads,
+                          int32_t head_size, int32_t block_size,
+                          int32_t dtype, void* stream);
+
+/*
+ * pa_attention_workspace_size - bytes of device workspace pa_attention
+ * needs for these host-known sizes (an upper bound over every metadata the
+ * device could hold).  Returns 0 when the sizes are invalid.
+ */
+size_t pa_attention_workspace_size(int32_t num_seqs, int64_t num_tokens,
+                                   int32_t max_blocks_per_seq,
+                                   int32_t num_heads, int32_t num_kv_heads,
+                                   int32_t head_size, int32_t block_size);
+
+/*
+ * pa_attention - paged causal GQA attention over packed varlen queries.
+ *
+ * Defines: "[WebGPU] Initial PagedAttention implementation (1/n)", sections
+ * "Description" and "FlashAttention: optional seqlens_q input"; the math is
+ * the "FlexAttention Computation" of the FlexAttention operator page with
+ * its GQA head mapping and masked scores treated as -inf.
+ *
+ * For sequence b: q_len_b = cu_seqlens_q[b+1] - cu_seqlens_q[b],
+ * L_b = seqlens_kv[b], past_b = L_b - q_len_b; for new row i < q_len_b
+ * (packed token t = cu_seqlens_q[b] + i) and query head h:
+ *   K_j = k_cache[block_table[b][j / block_size]][j % block_size][h / G]
+ *   out[t][h] = sum_{j <= past_b + i} softmax_j(scale * q[t][h] . K_j) V_j
+ * with G = num_heads / num_kv_heads.
+ *
+ * q            [num_tokens, num_heads, head_size] dtype (packed tokens).
+ * cu_seqlens_q [num_seqs + 1] int32: cu[0] = 0, nondecreasing,
+ *              cu[num_seqs] = num_tokens.  Empty sequences are allowed.
+ * seqlens_kv   [num_seqs] int32: total KV length of each sequence including
+ *              this step's tokens; must be >= q_len_b (precondition) and
+ *              <= max_blocks_per_seq * block_size.
+ * block_table  [num_seqs, max_blocks_per_seq] int32 row-major; entries
+ *              0 .. ceil(L_b / block_size) - 1 of row b must be valid block
+ *              ids (< num_blocks); later entries are never read.  Blocks may
+ *              be shared between sequences.
+ * k_cache,
+ * v_cache      paged caches as above; read only.  Slots beyond L_b and
+ *              blocks not referenced are never read into the result (they
+ *              may hold NaN).
+ * out          [num_tokens, num_heads, head_size] dtype, fully written.
+ * scale        finite float, used exactly as given (0 gives the mean of the
+ *              visible V rows).
+ * workspace    device buffer of at least pa_attention_workspace_size(...)
+ *              bytes, 256-byte aligned; contents need no initialisation and
+ *              are scratch (plan lists, split-KV partial results).
+ * Limits: head_size in {64, 128}; block_size a power of two in [16, 1024];
+ * num_heads % num_kv_heads == 0 with G <= 128; num_blocks * block_size
+ * <= INT32_MAX; num_seqs <= 65536.  Other shapes return
+ * PA_ERR_NOT_IMPLEMENTED.  num_tokens == 0 returns PA_OK without launching.
+ */
+pa_status_t pa_attention(const void* q, const int32_t* cu_seqlens_q,
+                         const int32_t* seqlens_kv, const int32_t* block_table,
+                         const void* k_cache, const void* v_cache, void* out,
+                         int32_t num_seqs, int64_t num_tokens,
+                         int32_t max_blocks_per_seq, int64_t num_blocks,
+                         float scale, int32_t num_heads, int32_t num_kv_heads,
+                         int32_t head_size, int32_t block_size, int32_t dtype,
+                         void* workspace, size_t workspace_bytes,
+                         void* stream);
+
+/*
+ * pa_validate_metadata - debug/test check of the device metadata that
+ * pa_attention / pa_scatter_kv trust.  Copies the arrays to the host
+ * (synchronising `stream`) and writes a bit mask of violations to
+ * *violations (host pointer):
+ *   bit 0 cu_seqlens_q[0] != 0        bit 1 cu_seqlens_q decreasing
+ *   bit 2 cu_seqlens_q[num_seqs] != num_tokens
+ *   bit 3 seqlens_kv[b] < q_len_b     bit 4 seqlens_kv[b] beyond the table row
+ *   bit 5 a needed block id outside [0, num_blocks)
+ *   bit 6 a slot >= num_blocks * block_size
+ *   bit 7 duplicate non-negative slots
+ * slot_mapping may be NULL (bits 6-7 then stay clear).  Returns PA_OK when
+ * the check ran, whatever it found.
+ */
+pa_status_t pa_validate_metadata(const int32_t* cu_seqlens_q,
+                                 const int32_t* seqlens_kv,
+                                 const int32_t* block_table,
+                                 const int32_t* slot_mapping, int32_t num_seqs,
+                                 int64_t num_tokens, int32_t max_blocks_per_seq,
+                                 int64_t num_blocks, int32_t block_size,
+                                 uint32_t* violations, void* stream);
+
+/* Human-readable name of a status code (static storage). */
+const char* pa_status_string(int32_t status);
+
+/* Message describing the calling thread's most recent failed call
+ * (static thread-local storage; "" if none). */
+const char* pa_last_error(void);
+
+/*
+ * Kernel timing for measurement tools.  While enabled, pa_scatter_kv and
+ * pa_attention bracket each kernel launch with a pair of HIP events on the
+ * caller's stream.  pa_profile_read waits for the recorded events and
+ * returns, per kernel kind, the summed milliseconds and launch counts
+ * (host arrays of n entries; kinds: 0 scatter, 1 plan, 2 prefill,
+ * 3 decode, 4 combine), then forgets them.  Not for concurrent use.
+ */
+#define PA_PROFILE_KINDS 5
+pa_status_t pa_profile_enable(int32_t enable);
+pa_status_t pa_profile_read(double* ms, int64_t* launches, int32_t n);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H_ */

@@ -1,0 +1,135 @@
+"""Paged-KV-cache attention for MI355X (gfx950): Python binding of libpa.so.
+
+The functions mirror the C ABI in include/pa.h and take torch tensors that
+already live on the GPU.  Torch supplies device memory and the current
+stream; the library's HIP kernels do all the work, and nothing here has a
+CPU fallback: a missing library raises ImportError on first use.
+"""
+from __future__ import annotations
+
+import ctypes
+
+from ._lib import (PA_BF16, PA_F16, PROFILE_KINDS, PAError, check, lib)  # noqa: F401
+
+__all__ = ["pa_scatter_kv", "pa_attention", "pa_attention_workspace_size",
+           "pa_validate_metadata", "profile_enable", "profile_read", "PAError"]
+
+
+def _dtype_code(t):
+    import torch
+    if t.dtype == torch.float16:
+        return PA_F16
+    if t.dtype == torch.bfloat16:
+        return PA_BF16
+    raise ValueError(f"unsupported dtype {t.dtype} (float16 or bfloat16)")
+
+
+def _stream_ptr(t, stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream(t.device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _dev(t, name, dtype=None):
+    import torch
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def pa_scatter_kv(k_new, v_new, slot_mapping, k_cache, v_cache, stream=None):
+    """Write new K/V rows [T, Hk, D] into the paged caches [NB, bs, Hk, D]
+    at int32 ``slot_mapping`` [T] (negative = skip), in place."""
+    import torch
+    T, hk, d = k_new.shape
+    nb, bs = k_cache.shape[0], k_cache.shape[1]
+    if tuple(v_new.shape) != (T, hk, d) or tuple(k_cache.shape) != (nb, bs, hk, d) \
+            or tuple(v_cache.shape) != (nb, bs, hk, d) or slot_mapping.shape != (T,):
+        raise ValueError("inconsistent shapes")
+    if not (k_new.dtype == v_new.dtype == k_cache.dtype == v_cache.dtype):
+        raise ValueError("K/V and caches must share one dtype")
+    check(lib().pa_scatter_kv(
+        _dev(k_new, "k_new"), _dev(v_new, "v_new"), _dev(slot_mapping, "slot_mapping", torch.int32),
+        _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), T, nb, hk, d, bs,
+        _dtype_code(k_cache), _stream_ptr(k_cache, stream)))
+
+
+def pa_attention_workspace_size(num_seqs, num_tokens, max_blocks_per_seq, num_heads,
+                                num_kv_heads, head_size, block_size):
+    """Bytes of device workspace pa_attention needs (0 for invalid sizes)."""
+    return int(lib().pa_attention_workspace_size(num_seqs, num_tokens, max_blocks_per_seq,
+                                                 num_heads, num_kv_heads, head_size, block_size))
+
+
+def pa_attention(q, cu_seqlens_q, seqlens_kv, block_table, k_cache, v_cache, scale,
+                 num_heads, num_kv_heads, out=None, workspace=None, stream=None):
+    """Paged causal GQA attention.
+
+    q [T, Hq, D] (or [T, Hq*D]); cu_seqlens_q int32 [B+1]; seqlens_kv int32
+    [B]; block_table int32 [B, MB]; caches [NB, bs, Hk, D].  Returns out
+    [T, Hq, D].  ``workspace`` is a uint8 GPU tensor of at least
+    pa_attention_workspace_size(...) bytes; one is allocated if omitted.
+    """
+    import torch
+    T = q.shape[0]
+    d = k_cache.shape[-1]
+    nb, bs = k_cache.shape[0], k_cache.shape[1]
+    B = seqlens_kv.shape[0]
+    MB = block_table.shape[1]
+    if q.numel() != T * num_heads * d or cu_seqlens_q.shape != (B + 1,) \
+            or block_table.shape[0] != B or tuple(v_cache.shape) != tuple(k_cache.shape) \
+            or k_cache.shape[2] != num_kv_heads:
+        raise ValueError("inconsistent shapes")
+    if not (q.dtype == k_cache.dtype == v_cache.dtype):
+        raise ValueError("q and caches must share one dtype")
+    if out is None:
+        out = torch.empty((T, num_heads, d), dtype=q.dtype, device=q.device)
+    elif out.numel() != q.numel() or out.dtype != q.dtype:
+        raise ValueError("out must match q")
+    need = pa_attention_workspace_size(B, T, MB, num_heads, num_kv_heads, d, bs)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    check(lib().pa_attention(
+        _dev(q, "q"), _dev(cu_seqlens_q, "cu_seqlens_q", torch.int32),
+        _dev(seqlens_kv, "seqlens_kv", torch.int32), _dev(block_table, "block_table", torch.int32),
+        _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), _dev(out, "out"), B, T, MB, nb,
+        float(scale), num_heads, num_kv_heads, d, bs, _dtype_code(q),
+        _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+        _stream_ptr(q, stream)))
+    return out
+
+
+def pa_validate_metadata(cu_seqlens_q, seqlens_kv, block_table, num_blocks, block_size,
+                         slot_mapping=None, num_tokens=None, stream=None):
+    """Debug check of device metadata; returns the violation bit mask
+    (0 = valid).  Synchronises the stream."""
+    import torch
+    B = seqlens_kv.shape[0]
+    T = int(num_tokens if num_tokens is not None else
+            (slot_mapping.shape[0] if slot_mapping is not None else 0))
+    v = ctypes.c_uint32(0)
+    check(lib().pa_validate_metadata(
+        _dev(cu_seqlens_q, "cu_seqlens_q", torch.int32), _dev(seqlens_kv, "seqlens_kv", torch.int32),
+        _dev(block_table, "block_table", torch.int32),
+        _dev(slot_mapping, "slot_mapping", torch.int32) if slot_mapping is not None else None,
+        B, T, block_table.shape[1], num_blocks, block_size, ctypes.byref(v),
+        _stream_ptr(seqlens_kv, stream)))
+    return int(v.value)
+
+
+def profile_enable(on=True):
+    check(lib().pa_profile_enable(1 if on else 0))
+
+
+def profile_read():
+    """{kernel kind: (total ms, launches)} since the last read."""
+    n = len(PROFILE_KINDS)
+    ms = (ctypes.c_double * n)()
+    cnt = (ctypes.c_int64 * n)()
+    check(lib().pa_profile_read(ms, cnt, n))
+    return {k: (ms[i], cnt[i]) for i, k in enumerate(PROFILE_KINDS)}

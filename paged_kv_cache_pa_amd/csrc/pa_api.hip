@@ -1,0 +1,397 @@
+// Host side of the C ABI declared in include/pa.h: argument checks (all
+// before the first HIP call), workspace layout, grid sizing from host-known
+// bounds, kernel launches on the caller's stream, metadata validation and
+// per-kernel event timing.
+//
+// Sources for the checks: "[WebGPU] Initial PagedAttention implementation
+// (1/n)" - "Description" (unsupported features are rejected up front with a
+// NOT_IMPLEMENTED status), the review's cross-cutting point on the blocking
+// metadata readback (nothing here reads device metadata on the host, except
+// the debug validator), and the FlexAttention page's requirement that the
+// query head count be a multiple of the KV head count.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+#include <mutex>
+#include <vector>
+
+#include "../../include/pa.h"
+#include "pa_internal.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+pa_status_t fail(pa_status_t st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+pa_status_t fail(pa_status_t st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+pa_status_t hip_fail(hipError_t e, const char* what) {
+  return fail(PA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+bool is_pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
+
+int log2i(int64_t x) {
+  int s = 0;
+  while ((int64_t(1) << s) < x) ++s;
+  return s;
+}
+
+// ---------------------------------------------------------------- profiling
+struct ProfEvent {
+  int kind;
+  hipEvent_t start, stop;
+};
+std::mutex g_prof_mu;
+bool g_prof_on = false;
+std::vector<ProfEvent> g_prof_pending;
+std::vector<hipEvent_t> g_prof_pool;
+
+hipEvent_t prof_event() {
+  if (!g_prof_pool.empty()) {
+    hipEvent_t e = g_prof_pool.back();
+    g_prof_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+// Runs `launch` on `st`, bracketed by timing events while profiling is on.
+template <typename F>
+hipError_t timed(int kind, hipStream_t st, F&& launch) {
+  if (!g_prof_on) return launch();
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  ProfEvent pe{kind, prof_event(), prof_event()};
+  if (pe.start) (void)hipEventRecord(pe.start, st);
+  hipError_t e = launch();
+  if (pe.stop) (void)hipEventRecord(pe.stop, st);
+  if (pe.start && pe.stop) g_prof_pending.push_back(pe);
+  return e;
+}
+
+int device_cus() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+// Host-side shape checks shared by pa_attention and the workspace query.
+pa_status_t check_shape(const pa::Shape& s) {
+  if (s.num_seqs < 1 || s.num_seqs > 65536)
+    return fail(PA_ERR_INVALID_ARGUMENT, "num_seqs=%d outside [1, 65536]", s.num_seqs);
+  if (s.num_tokens < 0 || s.num_tokens > INT32_MAX)
+    return fail(PA_ERR_INVALID_ARGUMENT, "num_tokens=%lld outside [0, INT32_MAX]",
+                (long long)s.num_tokens);
+  if (s.max_blocks_per_seq < 1)
+    return fail(PA_ERR_INVALID_ARGUMENT, "max_blocks_per_seq=%d < 1", s.max_blocks_per_seq);
+  if (s.num_heads < 1 || s.num_kv_heads < 1)
+    return fail(PA_ERR_INVALID_ARGUMENT, "head counts must be >= 1");
+  if (s.num_heads % s.num_kv_heads != 0)
+    return fail(PA_ERR_INVALID_ARGUMENT, "num_heads=%d is not a multiple of num_kv_heads=%d",
+                s.num_heads, s.num_kv_heads);
+  if (s.num_heads / s.num_kv_heads > pa::kPrefillRows)
+    return fail(PA_ERR_NOT_IMPLEMENTED, "group size %d > %d", s.num_heads / s.num_kv_heads,
+                pa::kPrefillRows);
+  if (s.head_size != 64 && s.head_size != 128)
+    return fail(PA_ERR_NOT_IMPLEMENTED, "head_size=%d (supported: 64, 128)", s.head_size);
+  if (!is_pow2(s.block_size) || s.block_size < 16 || s.block_size > 1024)
+    return fail(PA_ERR_NOT_IMPLEMENTED, "block_size=%d (supported: powers of two in [16, 1024])",
+                s.block_size);
+  if ((int64_t)s.max_blocks_per_seq * s.block_size > INT32_MAX)
+    return fail(PA_ERR_NOT_IMPLEMENTED, "max_blocks_per_seq * block_size exceeds INT32_MAX");
+  return PA_OK;
+}
+
+}  // namespace
+
+namespace pa {
+
+int resident_blocks(const void* kernel, int num_cus) {
+  int per_cu = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 256, 0) != hipSuccess ||
+      per_cu < 1)
+    per_cu = 1;
+  return per_cu * num_cus;
+}
+
+Layout workspace_layout(const Shape& s) {
+  Layout L{};
+  const int G = s.num_heads / s.num_kv_heads;
+  const int64_t max_kv = (int64_t)s.max_blocks_per_seq * s.block_size;
+  const int64_t max_splits = (max_kv + kSplitKeys - 1) / kSplitKeys;
+  const int tq = prefill_tokens_per_tile(G);
+  L.max_dec_pairs = (int64_t)s.num_seqs * max_splits;
+  const int64_t cols = std::min<int64_t>((int64_t)kDecodeCols * s.num_seqs, (int64_t)G * s.num_tokens);
+  L.max_part_rows = max_splits > 1 ? max_splits * s.num_kv_heads * cols : 0;
+  L.max_pf_items = ((s.num_tokens + tq - 1) / tq + std::min<int64_t>(s.num_seqs, s.num_tokens)) *
+                   s.num_kv_heads;
+  size_t off = 0;
+  L.counters = off;
+  off = align256(off + kNumCounters * sizeof(int32_t));
+  L.seqinfo = off;
+  off = align256(off + (size_t)s.num_seqs * sizeof(SeqInfo));
+  L.dec_items = off;
+  off = align256(off + (size_t)L.max_dec_pairs * sizeof(int2));
+  L.pf_items = off;
+  off = align256(off + (size_t)L.max_pf_items * sizeof(int4));
+  L.part_ml = off;
+  off = align256(off + (size_t)L.max_part_rows * sizeof(float2));
+  L.part_acc = off;
+  off = align256(off + (size_t)L.max_part_rows * s.head_size * sizeof(float));
+  L.total = off;
+  return L;
+}
+
+}  // namespace pa
+
+extern "C" {
+
+const char* pa_status_string(int32_t status) {
+  switch (status) {
+    case PA_OK: return "PA_OK";
+    case PA_ERR_INVALID_ARGUMENT: return "PA_ERR_INVALID_ARGUMENT";
+    case PA_ERR_NOT_IMPLEMENTED: return "PA_ERR_NOT_IMPLEMENTED";
+    case PA_ERR_WORKSPACE_TOO_SMALL: return "PA_ERR_WORKSPACE_TOO_SMALL";
+    case PA_ERR_HIP: return "PA_ERR_HIP";
+    default: return "PA_ERR_UNKNOWN";
+  }
+}
+
+const char* pa_last_error(void) { return g_err; }
+
+pa_status_t pa_scatter_kv(const void* k_new, const void* v_new, const int32_t* slot_mapping,
+                          void* k_cache, void* v_cache, int64_t num_tokens, int64_t num_blocks,
+                          int32_t num_kv_heads, int32_t head_size, int32_t block_size,
+                          int32_t dtype, void* stream) {
+  g_err[0] = 0;
+  if (dtype != PA_F16 && dtype != PA_BF16)
+    return fail(PA_ERR_NOT_IMPLEMENTED, "dtype=%d (supported: PA_F16, PA_BF16)", dtype);
+  if (num_tokens < 0) return fail(PA_ERR_INVALID_ARGUMENT, "num_tokens < 0");
+  if (num_kv_heads < 1 || head_size < 1 || block_size < 1 || num_blocks < 1)
+    return fail(PA_ERR_INVALID_ARGUMENT, "sizes must be >= 1");
+  if (head_size % 8 != 0)
+    return fail(PA_ERR_NOT_IMPLEMENTED, "head_size=%d is not a multiple of 8", head_size);
+  if (num_blocks * (int64_t)block_size > INT32_MAX)
+    return fail(PA_ERR_NOT_IMPLEMENTED, "num_blocks * block_size exceeds INT32_MAX");
+  const int64_t row_bytes = (int64_t)num_kv_heads * head_size * 2;
+  if (row_bytes > INT32_MAX) return fail(PA_ERR_NOT_IMPLEMENTED, "row too large");
+  if (num_tokens == 0) return PA_OK;
+  if (!k_new || !v_new || !slot_mapping || !k_cache || !v_cache)
+    return fail(PA_ERR_INVALID_ARGUMENT, "null pointer argument");
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e = timed(0, st, [&] {
+    return pa::launch_scatter(k_new, v_new, slot_mapping, k_cache, v_cache, num_tokens,
+                              (int32_t)row_bytes, st);
+  });
+  if (e != hipSuccess) return hip_fail(e, "scatter launch");
+  return PA_OK;
+}
+
+size_t pa_attention_workspace_size(int32_t num_seqs, int64_t num_tokens, int32_t max_blocks_per_seq,
+                                   int32_t num_heads, int32_t num_kv_heads, int32_t head_size,
+                                   int32_t block_size) {
+  pa::Shape s{num_seqs, num_tokens, max_blocks_per_seq, num_heads, num_kv_heads, head_size,
+              block_size};
+  if (check_shape(s) != PA_OK) return 0;
+  return pa::workspace_layout(s).total;
+}
+
+pa_status_t pa_attention(const void* q, const int32_t* cu_seqlens_q, const int32_t* seqlens_kv,
+                         const int32_t* block_table, const void* k_cache, const void* v_cache,
+                         void* out, int32_t num_seqs, int64_t num_tokens,
+                         int32_t max_blocks_per_seq, int64_t num_blocks, float scale,
+                         int32_t num_heads, int32_t num_kv_heads, int32_t head_size,
+                         int32_t block_size, int32_t dtype, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  g_err[0] = 0;
+  if (dtype != PA_F16 && dtype != PA_BF16)
+    return fail(PA_ERR_NOT_IMPLEMENTED, "dtype=%d (supported: PA_F16, PA_BF16)", dtype);
+  const pa::Shape s{num_seqs, num_tokens, max_blocks_per_seq, num_heads, num_kv_heads, head_size,
+                    block_size};
+  pa_status_t cs = check_shape(s);
+  if (cs != PA_OK) return cs;
+  if (num_blocks < 1) return fail(PA_ERR_INVALID_ARGUMENT, "num_blocks < 1");
+  if (num_blocks * (int64_t)block_size > INT32_MAX)
+    return fail(PA_ERR_NOT_IMPLEMENTED, "num_blocks * block_size exceeds INT32_MAX");
+  if (!isfinite(scale)) return fail(PA_ERR_INVALID_ARGUMENT, "scale is not finite");
+  if (num_tokens == 0) return PA_OK;
+  if (!q || !cu_seqlens_q || !seqlens_kv || !block_table || !k_cache || !v_cache || !out)
+    return fail(PA_ERR_INVALID_ARGUMENT, "null pointer argument");
+  const pa::Layout L = pa::workspace_layout(s);
+  if (L.max_part_rows > INT32_MAX)
+    return fail(PA_ERR_NOT_IMPLEMENTED, "split-KV partial rows exceed INT32_MAX");
+  if (!workspace) return fail(PA_ERR_INVALID_ARGUMENT, "null workspace");
+  if (((uintptr_t)workspace & 255) != 0)
+    return fail(PA_ERR_INVALID_ARGUMENT, "workspace is not 256-byte aligned");
+  if (workspace_bytes < L.total)
+    return fail(PA_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < required %zu", workspace_bytes,
+                L.total);
+
+  char* ws = (char*)workspace;
+  const int G = num_heads / num_kv_heads;
+  const int tq = pa::prefill_tokens_per_tile(G);
+  hipStream_t st = (hipStream_t)stream;
+  const int cus = device_cus();
+
+  pa::PlanArgs pl{};
+  pl.cu_seqlens_q = cu_seqlens_q;
+  pl.seqlens_kv = seqlens_kv;
+  pl.counters = (int32_t*)(ws + L.counters);
+  pl.seqinfo = (pa::SeqInfo*)(ws + L.seqinfo);
+  pl.dec_items = (int2*)(ws + L.dec_items);
+  pl.pf_items = (int4*)(ws + L.pf_items);
+  pl.num_seqs = num_seqs;
+  pl.group = G;
+  pl.num_kv_heads = num_kv_heads;
+  pl.tokens_per_tile = tq;
+  hipError_t e = timed(1, st, [&] { return pa::launch_plan(pl, st); });
+  if (e != hipSuccess) return hip_fail(e, "plan launch");
+
+  pa::AttnArgs a{};
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.out = out;
+  a.block_table = block_table;
+  a.counters = pl.counters;
+  a.counters_rw = pl.counters;
+  a.seqinfo = pl.seqinfo;
+  a.dec_items = pl.dec_items;
+  a.pf_items = pl.pf_items;
+  a.part_ml = (float2*)(ws + L.part_ml);
+  a.part_acc = (float*)(ws + L.part_acc);
+  a.num_seqs = num_seqs;
+  a.num_heads = num_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.group = G;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.block_size = block_size;
+  a.block_shift = log2i(block_size);
+  a.tokens_per_tile = tq;
+  a.scale_log2 = scale * pa::kLog2e;
+
+  // Prefill first: its tiles are the long poles; decode streams behind it.
+  const bool any_prefill = (int64_t)num_tokens * G > pa::kDecodeCols;
+  if (any_prefill) {
+    e = timed(2, st, [&] {
+      return pa::launch_prefill(a, dtype, head_size, L.max_pf_items, cus, st);
+    });
+    if (e != hipSuccess) return hip_fail(e, "prefill launch");
+  }
+  const int64_t dec_waves = L.max_dec_pairs * num_kv_heads;
+  e = timed(3, st, [&] {
+    return pa::launch_decode(a, dtype, head_size, (dec_waves + 3) / 4, cus, st);
+  });
+  if (e != hipSuccess) return hip_fail(e, "decode launch");
+  if (L.max_part_rows > 0) {
+    e = timed(4, st, [&] { return pa::launch_combine(a, dtype, head_size, st); });
+    if (e != hipSuccess) return hip_fail(e, "combine launch");
+  }
+  return PA_OK;
+}
+
+pa_status_t pa_validate_metadata(const int32_t* cu_seqlens_q, const int32_t* seqlens_kv,
+                                 const int32_t* block_table, const int32_t* slot_mapping,
+                                 int32_t num_seqs, int64_t num_tokens, int32_t max_blocks_per_seq,
+                                 int64_t num_blocks, int32_t block_size, uint32_t* violations,
+                                 void* stream) {
+  g_err[0] = 0;
+  if (!violations || !cu_seqlens_q || !seqlens_kv || !block_table)
+    return fail(PA_ERR_INVALID_ARGUMENT, "null pointer argument");
+  if (num_seqs < 1 || num_tokens < 0 || max_blocks_per_seq < 1 || block_size < 1 || num_blocks < 1)
+    return fail(PA_ERR_INVALID_ARGUMENT, "invalid sizes");
+  hipStream_t st = (hipStream_t)stream;
+  std::vector<int32_t> cu(num_seqs + 1), L(num_seqs), tbl((size_t)num_seqs * max_blocks_per_seq),
+      slots(slot_mapping ? num_tokens : 0);
+  hipError_t e = hipMemcpyAsync(cu.data(), cu_seqlens_q, cu.size() * 4, hipMemcpyDeviceToHost, st);
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(L.data(), seqlens_kv, L.size() * 4, hipMemcpyDeviceToHost, st);
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(tbl.data(), block_table, tbl.size() * 4, hipMemcpyDeviceToHost, st);
+  if (e == hipSuccess && slot_mapping && num_tokens > 0)
+    e = hipMemcpyAsync(slots.data(), slot_mapping, slots.size() * 4, hipMemcpyDeviceToHost, st);
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  if (e != hipSuccess) return hip_fail(e, "metadata copy");
+  uint32_t v = 0;
+  if (cu[0] != 0) v |= 1u << 0;
+  for (int b = 0; b < num_seqs; ++b)
+    if (cu[b + 1] < cu[b]) v |= 1u << 1;
+  if (cu[num_seqs] != num_tokens) v |= 1u << 2;
+  for (int b = 0; b < num_seqs; ++b) {
+    const int64_t ql = (int64_t)cu[b + 1] - cu[b];
+    if (L[b] < ql) v |= 1u << 3;
+    const int64_t need = ((int64_t)L[b] + block_size - 1) / block_size;
+    if (need > max_blocks_per_seq) {
+      v |= 1u << 4;
+      continue;
+    }
+    for (int64_t k = 0; k < need; ++k) {
+      const int32_t id = tbl[(size_t)b * max_blocks_per_seq + k];
+      if (id < 0 || id >= num_blocks) v |= 1u << 5;
+    }
+  }
+  if (slot_mapping && num_tokens > 0) {
+    std::vector<int32_t> live;
+    for (int32_t x : slots) {
+      if (x >= (int64_t)num_blocks * block_size) v |= 1u << 6;
+      if (x >= 0) live.push_back(x);
+    }
+    std::sort(live.begin(), live.end());
+    if (std::adjacent_find(live.begin(), live.end()) != live.end()) v |= 1u << 7;
+  }
+  *violations = v;
+  return PA_OK;
+}
+
+pa_status_t pa_profile_enable(int32_t enable) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  g_prof_on = enable != 0;
+  return PA_OK;
+}
+
+pa_status_t pa_profile_read(double* ms, int64_t* launches, int32_t n) {
+  g_err[0] = 0;
+  if (!ms || !launches || n < 1) return fail(PA_ERR_INVALID_ARGUMENT, "bad output arrays");
+  for (int i = 0; i < n; ++i) {
+    ms[i] = 0.0;
+    launches[i] = 0;
+  }
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  pa_status_t rc = PA_OK;
+  for (const ProfEvent& pe : g_prof_pending) {
+    float t = 0.f;
+    hipError_t e = hipEventSynchronize(pe.stop);
+    if (e == hipSuccess) e = hipEventElapsedTime(&t, pe.start, pe.stop);
+    if (e != hipSuccess) rc = hip_fail(e, "profile event");
+    if (pe.kind >= 0 && pe.kind < n) {
+      ms[pe.kind] += t;
+      launches[pe.kind] += 1;
+    }
+    g_prof_pool.push_back(pe.start);
+    g_prof_pool.push_back(pe.stop);
+  }
+  g_prof_pending.clear();
+  return rc;
+}
+
+}  // extern "C"

@@ -1,0 +1,104 @@
+// Device-side building blocks shared by the paged-attention kernels (gfx950).
+//
+// Matrix-core operand conventions used throughout (wave64):
+//   v_mfma_f32_16x16x32_{f16,bf16}: lane l supplies row (A) / column (B)
+//     l % 16 and 8 consecutive contraction elements chosen by l / 16;
+//   v_mfma_f32_16x16x16_{f16,bf16}: the same with 4 contraction elements;
+//   both accumulate a 16x16 fp32 tile where lane l holds rows
+//   4 * (l / 16) + r (r = 0..3) of column l % 16.
+// A and B always use the same contraction-element assignment, so which
+// global index each (lane group, element) pair stands for is free; the
+// kernels pick it to make memory accesses contiguous.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef short short4_t __attribute__((ext_vector_type(4)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+
+
+struct F16 {};
+struct BF16 {};
+
+template <typename T> struct Elt;
+
+template <> struct Elt<F16> {
+  __device__ static inline float4_t mfma32(u32x4_t a, u32x4_t b, float4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, a),
+                                                  __builtin_bit_cast(half8_t, b), c, 0, 0, 0);
+  }
+  __device__ static inline float4_t mfma16(u32x2_t a, u32x2_t b, float4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(half4_t, a),
+                                                 __builtin_bit_cast(half4_t, b), c, 0, 0, 0);
+  }
+  // fp32 -> storage bits, round to nearest even.
+  __device__ static inline uint32_t bits(float x) {
+    return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)x);
+  }
+  __device__ static inline uint32_t pack2(float lo, float hi) { return bits(lo) | (bits(hi) << 16); }
+  // acc + the two packed values (exact products by 1, fp32 accumulate).
+  __device__ static inline float sum2(uint32_t packed, float acc) {
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, packed), half2_t{1, 1}, acc, false);
+  }
+};
+
+template <> struct Elt<BF16> {
+  __device__ static inline float4_t mfma32(u32x4_t a, u32x4_t b, float4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+  }
+  __device__ static inline float4_t mfma16(u32x2_t a, u32x2_t b, float4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(short4_t, a),
+                                                     __builtin_bit_cast(short4_t, b), c, 0, 0, 0);
+  }
+  __device__ static inline uint32_t bits(float x) {
+    return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)x);
+  }
+  __device__ static inline uint32_t pack2(float lo, float hi) { return bits(lo) | (bits(hi) << 16); }
+  __device__ static inline float sum2(uint32_t packed, float acc) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, packed),
+                                           bf16x2_t{1, 1}, acc, false);
+  }
+};
+
+// Element e (0..7) of 8 packed 16-bit values held in 4 dwords.
+__device__ inline uint32_t half_of(u32x4_t v, int e) {
+  uint32_t w = v[e >> 1];
+  return (e & 1) ? (w >> 16) : (w & 0xffffu);
+}
+
+// Pack element e of x (low half) and element e of y (high half) into one
+// dword; e is a compile-time constant after unrolling.
+__device__ inline uint32_t pair_elem(uint32_t xw, uint32_t yw, bool hi) {
+  // v_perm_b32 selector: bytes of {yw, xw}; result = [x.lo16 | y.lo16<<16]
+  // or [x.hi16 | y.hi16<<16].
+  return hi ? __builtin_amdgcn_perm(yw, xw, 0x07060302u) : __builtin_amdgcn_perm(yw, xw, 0x05040100u);
+}
+
+__device__ inline float wave_max_xor16_32(float v) {
+  v = fmaxf(v, __shfl_xor(v, 16));
+  v = fmaxf(v, __shfl_xor(v, 32));
+  return v;
+}
+
+__device__ inline float wave_sum_xor16_32(float v) {
+  v += __shfl_xor(v, 16);
+  v += __shfl_xor(v, 32);
+  return v;
+}
+
+__device__ inline u32x4_t ld16(const void* p) { return *reinterpret_cast<const u32x4_t*>(p); }
+__device__ inline u32x2_t ld8(const void* p) { return *reinterpret_cast<const u32x2_t*>(p); }
+
+}  // namespace pa

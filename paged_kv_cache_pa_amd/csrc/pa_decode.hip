@@ -1,0 +1,267 @@
+// Decode path: split-KV paged attention for sequences whose q_len * G query
+// columns fit one 16-wide tile (q_len == 1 decode, and short speculative
+// chunks), plus the log-sum-exp combine of the splits.
+//
+// Sources: "[WebGPU] Initial PagedAttention implementation (1/n)" -
+// "Description" (attention over the paged cache for packed varlen queries),
+// "FlashAttention: optional seqlens_q input" (past_b = total_kv_b - q_len_b;
+// row i sees keys 0..past_b+i) and "Roadmap" (phase 2: page-aware decode
+// reading K/V through the block table instead of a gather pass);
+// FlexAttention operator page - "FlexAttention Computation" and "Grouped
+// Query Attention (GQA)".
+//
+// Work item = (sequence b, split s, KV head kh), one wavefront each, fetched
+// from a device counter.  The wave walks 16-key chunks of keys
+// [s*512, min(L, (s+1)*512)) through the block table (the split's block ids
+// are prefetched into one VGPR and broadcast per chunk with readlane).  The
+// G query heads of kh (times q_len tokens) are the 16 columns n = i*G + g of
+// the score tile, so every K/V byte is read from HBM exactly once per call.
+//
+//   S^T[key][n] = K_chunk . Q^T       16x16x32 MFMA, D/32 steps
+//   online softmax per column n       fp32, exp2 with log2(e) folded in
+//   O^T[d][n]  += V_chunk^T . P^T      16x16x16 MFMA, D/16 tiles
+//
+// Lane (kq = l/16, r = l%16) loads, per chunk, 64 B of key row r (the A
+// operand of S^T: contraction elements = 16-byte chunks 4s+kq of the row)
+// and 16 B of each of value rows 4kq..4kq+3 (d range [r*D/16, (r+1)*D/16)),
+// so V needs only register permutes to become the A operand of O^T: tile t
+// row r stands for d = r*D/16 + t.  The accumulator tile of O^T keeps
+// column n in lane n%16, the same lane that owns column n's softmax state,
+// so rescaling is a per-lane multiply.
+//
+// A sequence with one split writes its normalised output directly; longer
+// sequences write (m, l, unnormalised acc) per split and column, merged by
+// combine_kernel:  O = sum_s 2^(m_s - M) acc_s / sum_s 2^(m_s - M) l_s.
+#include "pa_common.hpp"
+#include "pa_internal.hpp"
+
+namespace pa {
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void decode_kernel(AttnArgs a) {
+  constexpr int NS = D / 32;    // QK^T contraction steps (8 halfs per lane)
+  constexpr int NT = D / 16;    // O^T tiles; also halfs per lane per V row
+  const int lane = threadIdx.x & 63;
+  const int r16 = lane & 15, kq = lane >> 4;
+  const int hk = a.num_kv_heads, G = a.group, hq = a.num_heads;
+  const int64_t row_stride = (int64_t)hk * D;   // elements between token rows
+  const uint16_t* __restrict__ qp = (const uint16_t*)a.q;
+  const uint16_t* __restrict__ kc = (const uint16_t*)a.k_cache;
+  const uint16_t* __restrict__ vc = (const uint16_t*)a.v_cache;
+  uint16_t* __restrict__ op = (uint16_t*)a.out;
+  const int n_items = a.counters[kNumDecPairs] * hk;
+
+  for (;;) {
+    int it = 0;
+    if (lane == 0) it = atomicAdd(a.counters_rw + kCtrDecode, 1);
+    it = __builtin_amdgcn_readfirstlane(__shfl(it, 0));
+    if (it >= n_items) break;
+    const int pair = it / hk;
+    const int kh = it - pair * hk;
+    const int2 bsplit = a.dec_items[pair];
+    const int b = bsplit.x, split = bsplit.y;
+    const SeqInfo si = a.seqinfo[b];
+    const int L = si.kv_len, ql = si.q_len;
+    const int past = L - ql;
+    const int ncols = ql * G;
+    const int nsplit = (L + kSplitKeys - 1) / kSplitKeys;
+    const int k0 = split * kSplitKeys;
+    const int k1 = min(L, k0 + kSplitKeys);
+
+    // Q^T operand: column n = r16 -> (token n / G, head kh*G + n % G).
+    u32x4_t qreg[NS];
+    {
+      const int n = r16;
+      const bool valid = n < ncols;
+      const int tok = si.cu + (valid ? n / G : 0);
+      const int h = kh * G + (valid ? n % G : 0);
+      const uint16_t* qrow = qp + ((int64_t)tok * hq + h) * D;
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        qreg[s] = valid ? ld16(qrow + (4 * s + kq) * 8) : u32x4_t{0, 0, 0, 0};
+      }
+    }
+    // Causal limit of column n: token n / G sees keys <= past + n / G
+    // (padding columns see every key and are never stored).
+    const int col_limit = past + r16 / G;
+
+    // Block ids of this split, one per lane.
+    const int blk0 = k0 >> a.block_shift;
+    const int nblk = ((k1 - 1) >> a.block_shift) - blk0 + 1;
+    const int32_t* trow = a.block_table + (int64_t)b * a.max_blocks_per_seq + blk0;
+    const int my_blk = lane < nblk ? trow[lane] : 0;
+
+    float m = -INFINITY, l = 0.f;
+    float4_t acc[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[t] = float4_t{0.f, 0.f, 0.f, 0.f};
+
+    for (int c0 = k0; c0 < k1; c0 += 16) {
+      const int blk = __builtin_amdgcn_readlane(my_blk, (c0 >> a.block_shift) - blk0);
+      const int64_t base =
+          ((int64_t)blk * a.block_size + (c0 & (a.block_size - 1))) * row_stride + (int64_t)kh * D;
+      u32x4_t kreg[NS];
+      const uint16_t* krow = kc + base + r16 * row_stride;
+#pragma unroll
+      for (int s = 0; s < NS; ++s) kreg[s] = ld16(krow + (4 * s + kq) * 8);
+      uint32_t vreg[4][NT / 2];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint16_t* vrow = vc + base + (4 * kq + e) * row_stride + r16 * NT;
+        const bool live = c0 + 4 * kq + e < k1;   // rows past L may hold NaN
+        if constexpr (NT == 8) {
+          u32x4_t x = ld16(vrow);
+#pragma unroll
+          for (int w = 0; w < 4; ++w) vreg[e][w] = live ? x[w] : 0u;
+        } else {
+          u32x2_t x = ld8(vrow);
+#pragma unroll
+          for (int w = 0; w < 2; ++w) vreg[e][w] = live ? x[w] : 0u;
+        }
+      }
+
+      float4_t sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < NS; ++s) sc = Elt<T>::mfma32(kreg[s], qreg[s], sc);
+
+      float sv[4];
+      float cmax = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int key = c0 + 4 * kq + i;
+        const bool vis = key < k1 && key <= col_limit;
+        sv[i] = vis ? sc[i] * a.scale_log2 : -INFINITY;
+        cmax = fmaxf(cmax, sv[i]);
+      }
+      cmax = wave_max_xor16_32(cmax);
+      const float m_new = fmaxf(m, cmax);
+      const float base_m = m_new == -INFINITY ? 0.f : m_new;
+      const float alpha = exp2f(m - base_m);
+      float p[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) p[i] = exp2f(sv[i] - base_m);
+      // P enters P.V rounded to the input dtype; the denominator sums the
+      // same rounded values so the weights of each column sum to one.
+      const u32x2_t pb = {Elt<T>::pack2(p[0], p[1]), Elt<T>::pack2(p[2], p[3])};
+      l = l * alpha + Elt<T>::sum2(pb[1], Elt<T>::sum2(pb[0], 0.f));
+      m = m_new;
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const uint32_t w0 = pair_elem(vreg[0][t >> 1], vreg[1][t >> 1], t & 1);
+        const uint32_t w1 = pair_elem(vreg[2][t >> 1], vreg[3][t >> 1], t & 1);
+        acc[t] = Elt<T>::mfma16(u32x2_t{w0, w1}, pb, acc[t] * alpha);
+      }
+    }
+
+    const float l_tot = wave_sum_xor16_32(l);
+    const int n = r16;
+    if (n >= ncols) {
+      // padding column: nothing to store
+    } else if (nsplit == 1) {
+      const float inv = 1.f / l_tot;
+      const int tok = si.cu + n / G;
+      const int h = kh * G + n % G;
+      uint16_t* orow = op + ((int64_t)tok * hq + h) * D;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        uint32_t w[NT / 2];
+#pragma unroll
+        for (int t = 0; t < NT; t += 2)
+          w[t / 2] = Elt<T>::pack2(acc[t][r] * inv, acc[t + 1][r] * inv);
+        uint16_t* dst = orow + (4 * kq + r) * NT;
+        if constexpr (NT == 8) {
+          *reinterpret_cast<u32x4_t*>(dst) = u32x4_t{w[0], w[1], w[2], w[3]};
+        } else {
+          *reinterpret_cast<u32x2_t*>(dst) = u32x2_t{w[0], w[1]};
+        }
+      }
+    } else {
+      const int64_t row = (int64_t)si.pbase + ((int64_t)kh * nsplit + split) * ncols + n;
+      if (kq == 0) a.part_ml[row] = make_float2(m, l_tot);
+      float* dst = a.part_acc + row * D;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float tmp[NT];
+#pragma unroll
+        for (int t = 0; t < NT; ++t) tmp[t] = acc[t][r];
+#pragma unroll
+        for (int t = 0; t < NT; t += 4)
+          *reinterpret_cast<float4_t*>(dst + (4 * kq + r) * NT + t) =
+              float4_t{tmp[t], tmp[t + 1], tmp[t + 2], tmp[t + 3]};
+      }
+    }
+  }
+}
+
+// One work-group per (sequence, KV head); a no-op unless the sequence took
+// the decode path with more than one split.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void combine_kernel(AttnArgs a) {
+  const int b = blockIdx.x, kh = blockIdx.y;
+  const SeqInfo si = a.seqinfo[b];
+  const int G = a.group;
+  const int ncols = si.q_len * G;
+  if (si.q_len <= 0 || ncols > kDecodeCols) return;
+  const int nsplit = (si.kv_len + kSplitKeys - 1) / kSplitKeys;
+  if (nsplit <= 1) return;
+  uint16_t* __restrict__ op = (uint16_t*)a.out;
+  for (int idx = threadIdx.x; idx < ncols * (D / 2); idx += blockDim.x) {
+    const int n = idx / (D / 2);
+    const int d = (idx - n * (D / 2)) * 2;
+    const int64_t row0 = (int64_t)si.pbase + (int64_t)kh * nsplit * ncols + n;
+    float M = -INFINITY;
+    for (int s = 0; s < nsplit; ++s) M = fmaxf(M, a.part_ml[row0 + (int64_t)s * ncols].x);
+    float num0 = 0.f, num1 = 0.f, den = 0.f;
+    for (int s = 0; s < nsplit; ++s) {
+      const int64_t row = row0 + (int64_t)s * ncols;
+      const float2 ml = a.part_ml[row];
+      const float f = ml.x == -INFINITY ? 0.f : exp2f(ml.x - M);
+      const float2 v = *reinterpret_cast<const float2*>(a.part_acc + row * D + d);
+      num0 += f * v.x;
+      num1 += f * v.y;
+      den += f * ml.y;
+    }
+    const float inv = 1.f / den;
+    const int tok = si.cu + n / G;
+    const int h = kh * G + n % G;
+    *reinterpret_cast<uint32_t*>(op + ((int64_t)tok * a.num_heads + h) * D + d) =
+        Elt<T>::pack2(num0 * inv, num1 * inv);
+  }
+}
+
+template <typename T>
+static hipError_t decode_dispatch(const AttnArgs& a, int head_size, int64_t max_blocks, int num_cus,
+                                  hipStream_t st) {
+  const void* fn = head_size == 128 ? (const void*)&decode_kernel<T, 128> : (const void*)&decode_kernel<T, 64>;
+  int64_t grid = resident_blocks(fn, num_cus);
+  if (grid > max_blocks) grid = max_blocks;
+  if (grid < 1) grid = 1;
+  if (head_size == 128)
+    hipLaunchKernelGGL((decode_kernel<T, 128>), dim3((unsigned)grid), dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL((decode_kernel<T, 64>), dim3((unsigned)grid), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode(const AttnArgs& a, int dtype, int head_size, int64_t max_blocks,
+                         int num_cus, hipStream_t st) {
+  return dtype == 0 ? decode_dispatch<F16>(a, head_size, max_blocks, num_cus, st)
+                    : decode_dispatch<BF16>(a, head_size, max_blocks, num_cus, st);
+}
+
+template <typename T>
+static hipError_t combine_dispatch(const AttnArgs& a, int head_size, hipStream_t st) {
+  dim3 grid(a.num_seqs, a.num_kv_heads);
+  if (head_size == 128)
+    hipLaunchKernelGGL((combine_kernel<T, 128>), grid, dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL((combine_kernel<T, 64>), grid, dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_combine(const AttnArgs& a, int dtype, int head_size, hipStream_t st) {
+  return dtype == 0 ? combine_dispatch<F16>(a, head_size, st)
+                    : combine_dispatch<BF16>(a, head_size, st);
+}
+
+}  // namespace pa

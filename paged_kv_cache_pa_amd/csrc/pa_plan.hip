@@ -1,0 +1,158 @@
+// Plan: turn the device-resident varlen metadata into work lists, without
+// any device-to-host copy.
+//
+// Source: "[WebGPU] Initial PagedAttention implementation (1/n)", section
+// "FlashAttention: optional seqlens_q input" (per-sequence past length =
+// total KV length - that sequence's query length) and the maintainer's note
+// that the host-side metadata readback blocks every run; here the host only
+// sizes the grids from host-known bounds and one work-group derives the rest.
+//
+// Per sequence b: q_len = cu[b+1] - cu[b], L = seqlens_kv[b].  A sequence
+// whose q_len * G columns fit one 16-wide tile takes the decode path and is
+// split into ceil(L / kSplitKeys) key ranges; every other non-empty sequence
+// takes the prefill path in tiles of tokens_per_tile tokens per KV head.
+// Prefill (sequence, KV head) pairs are dealt to 8 queues, one per XCD, so
+// all tiles that reuse one K/V stream share an L2; inside a queue the
+// heaviest (last) tile of each pair comes first.
+#include "pa_common.hpp"
+#include "pa_internal.hpp"
+
+namespace pa {
+
+namespace {
+
+constexpr int kPlanThreads = 1024;
+constexpr int kPlanWaves = kPlanThreads / 64;
+
+// Block-wide exclusive scan of W ints per thread (1024 threads).
+template <int W>
+__device__ void block_scan(int (&v)[W], int (&total)[W], int* lds) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int inc[W];
+#pragma unroll
+  for (int k = 0; k < W; ++k) {
+    int x = v[k];
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      int y = __shfl_up(x, o);
+      if (lane >= o) x += y;
+    }
+    inc[k] = x;
+  }
+  if (lane == 63) {
+#pragma unroll
+    for (int k = 0; k < W; ++k) lds[wave * W + k] = inc[k];
+  }
+  __syncthreads();
+  if (threadIdx.x < W) {
+    int run = 0;
+    for (int w = 0; w < kPlanWaves; ++w) {
+      int t = lds[w * W + threadIdx.x];
+      lds[w * W + threadIdx.x] = run;
+      run += t;
+    }
+    lds[kPlanWaves * W + threadIdx.x] = run;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < W; ++k) {
+    v[k] = lds[wave * W + k] + inc[k] - v[k];
+    total[k] = lds[kPlanWaves * W + k];
+  }
+  __syncthreads();
+}
+
+struct SeqCounts {
+  int cu0, q_len, L, nsplit, prows, ntiles;
+};
+
+__device__ inline SeqCounts seq_counts(const PlanArgs& a, int b) {
+  SeqCounts c{0, 0, 0, 0, 0, 0};
+  if (b >= a.num_seqs) return c;
+  c.cu0 = a.cu_seqlens_q[b];
+  c.q_len = a.cu_seqlens_q[b + 1] - c.cu0;
+  c.L = a.seqlens_kv[b];
+  if (c.q_len <= 0) return c;
+  const int ncols = c.q_len * a.group;
+  if (ncols <= kDecodeCols) {
+    c.nsplit = (c.L + kSplitKeys - 1) / kSplitKeys;
+    if (c.nsplit > 1) c.prows = a.num_kv_heads * c.nsplit * ncols;
+  } else {
+    c.ntiles = (c.q_len + a.tokens_per_tile - 1) / a.tokens_per_tile;
+  }
+  return c;
+}
+
+// Number of KV heads kh in [0, Hk) with (b * Hk + kh) % 8 == x.
+__device__ inline int heads_in_queue(int b, int hk, int x) {
+  const int r = ((x - (int)(((int64_t)b * hk) & 7)) % 8 + 8) % 8;
+  return r < hk ? (hk - 1 - r) / 8 + 1 : 0;
+}
+
+}  // namespace
+
+__global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
+  __shared__ int lds[(kPlanWaves + 1) * 12];
+  __shared__ int qstart[kQueues];
+  const int tid = threadIdx.x;
+  if (tid <= kQueues) a.counters[kCtrDecode + tid] = 0;   // fetch counters 0..8
+
+  // Pass 1: sequence info, decode pairs, partial-row bases, queue sizes.
+  int carry[3 + kQueues] = {0};
+  for (int base = 0; base < a.num_seqs; base += kPlanThreads) {
+    const int b = base + tid;
+    const SeqCounts c = seq_counts(a, b);
+    int v[3 + kQueues], tot[3 + kQueues];
+    v[0] = c.nsplit;
+    v[1] = c.prows;
+    v[2] = c.ntiles > 0;
+#pragma unroll
+    for (int x = 0; x < kQueues; ++x) v[3 + x] = c.ntiles * heads_in_queue(b, a.num_kv_heads, x);
+    block_scan<3 + kQueues>(v, tot, lds);
+    if (b < a.num_seqs) {
+      a.seqinfo[b] = SeqInfo{c.cu0, c.q_len, c.L, carry[1] + v[1]};
+      const int off = carry[0] + v[0];
+      for (int s = 0; s < c.nsplit; ++s) a.dec_items[off + s] = make_int2(b, s);
+    }
+#pragma unroll
+    for (int k = 0; k < 3 + kQueues; ++k) carry[k] += tot[k];
+  }
+  if (tid == 0) {
+    a.counters[kNumDecPairs] = carry[0];
+    int run = 0;
+    for (int x = 0; x < kQueues; ++x) {
+      a.counters[kQueueLen + x] = carry[3 + x];
+      a.counters[kQueueStart + x] = run;
+      qstart[x] = run;
+      run += carry[3 + x];
+    }
+  }
+  __syncthreads();
+
+  // Pass 2: prefill items, heaviest tile of each (sequence, head) first.
+  int qcarry[kQueues] = {0};
+  for (int base = 0; base < a.num_seqs; base += kPlanThreads) {
+    const int b = base + tid;
+    const SeqCounts c = seq_counts(a, b);
+    int v[kQueues], tot[kQueues];
+#pragma unroll
+    for (int x = 0; x < kQueues; ++x) v[x] = c.ntiles * heads_in_queue(b, a.num_kv_heads, x);
+    block_scan<kQueues>(v, tot, lds);
+    if (c.ntiles > 0) {
+      for (int kh = 0; kh < a.num_kv_heads; ++kh) {
+        const int x = (int)(((int64_t)b * a.num_kv_heads + kh) & 7);
+        int pos = qstart[x] + qcarry[x] + v[x] + (kh >> 3) * c.ntiles;
+        for (int r = 0; r < c.ntiles; ++r) a.pf_items[pos + r] = make_int4(b, kh, c.ntiles - 1 - r, 0);
+      }
+    }
+#pragma unroll
+    for (int x = 0; x < kQueues; ++x) qcarry[x] += tot[x];
+  }
+}
+
+hipError_t launch_plan(const PlanArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace pa

@@ -1,0 +1,248 @@
+// Prefill path: causal paged attention for sequences with more than one
+// 16-column tile of (token, head-in-group) query rows, on the matrix cores.
+//
+// Sources: "[WebGPU] Initial PagedAttention implementation (1/n)" -
+// "FlashAttention: optional seqlens_q input" (row i of sequence b sees keys
+// 0..past_b+i with past_b = total_kv_b - q_len_b; the causal length is
+// past + i + 1) and "Roadmap" (phase 2: page-aware prefill kernels that read
+// K/V straight from the paged cache); FlexAttention operator page -
+// "FlexAttention Computation" and "Grouped Query Attention (GQA)".
+//
+// Work item = (sequence b, KV head kh, tile): 128 query rows, row r being
+// token i0 + r / G of the tile and query head kh*G + r % G, so the G heads
+// that share kh share every K/V tile.  Items come from 8 per-XCD queues
+// (work-group w serves queue w % 8 first, then steals from the others).
+// Each of the 4 waves owns 32 rows (two 16-row groups).  Per 64-key tile:
+//   K, V rows resolved through the block table, 128-bit loads -> LDS
+//   S^T = K . Q^T          16x16x32 MFMA (fp16/bf16 in, fp32 acc)
+//   causal mask key <= past + i, online softmax in fp32 (exp2)
+//   O^T += V^T . P^T       16x16x32 MFMA, P rounded to the input dtype
+// Key tiles beyond the tile's last visible key are never loaded, and a wave
+// skips the matrix work of key tiles that lie wholly above its rows'
+// diagonal.  Key rows past the visible range are zero-filled in LDS, so NaN
+// in unused cache slots cannot reach the P.V product.
+#include "pa_common.hpp"
+#include "pa_internal.hpp"
+
+namespace pa {
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void prefill_kernel(AttnArgs a) {
+  constexpr int NS = D / 32;            // QK^T steps
+  constexpr int NT = D / 16;            // O^T tiles (halfs per lane per V row)
+  constexpr int BN = kPrefillKeys;      // keys per K/V tile
+  constexpr int PITCH = D + 8;          // LDS row pitch (halfs): +16 B vs bank conflicts
+  constexpr int CPR = D / 8;            // 16-byte chunks per row
+  constexpr int RPP = 256 / CPR;        // rows per cooperative pass
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[BN * PITCH];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[BN * PITCH];
+  __shared__ int item_sh;
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int r16 = lane & 15, kq = lane >> 4;
+  const int hk = a.num_kv_heads, G = a.group, hq = a.num_heads;
+  const int TQ = a.tokens_per_tile;
+  const int64_t row_stride = (int64_t)hk * D;
+  const uint16_t* __restrict__ qp = (const uint16_t*)a.q;
+  const uint16_t* __restrict__ kc = (const uint16_t*)a.k_cache;
+  const uint16_t* __restrict__ vc = (const uint16_t*)a.v_cache;
+  uint16_t* __restrict__ op = (uint16_t*)a.out;
+  const int home = blockIdx.x % kQueues;
+
+  for (int qi = 0; qi < kQueues; ++qi) {
+    const int x = (home + qi) % kQueues;
+    const int qlen = a.counters[kQueueLen + x];
+    const int qstart = a.counters[kQueueStart + x];
+    for (;;) {
+      if (tid == 0) item_sh = atomicAdd(a.counters_rw + kCtrPrefill + x, 1);
+      __syncthreads();
+      const int k = item_sh;
+      __syncthreads();
+      if (k >= qlen) break;
+      const int4 itm = a.pf_items[qstart + k];
+      const int b = itm.x, kh = itm.y, tile = itm.z;
+      const SeqInfo si = a.seqinfo[b];
+      const int ql = si.q_len, L = si.kv_len;
+      const int past = L - ql;
+      const int i0 = tile * TQ;
+      const int last_tok = min(i0 + TQ, ql) - 1;
+      const int kend = past + last_tok + 1;   // keys visible to the tile's last row
+
+      // Q^T operands and causal limits of this lane's two row groups.
+      u32x4_t qreg[2][NS];
+      int limit[2], tok[2], head[2];
+#pragma unroll
+      for (int rho = 0; rho < 2; ++rho) {
+        const int row = 32 * wave + 16 * rho + r16;
+        const int ti = i0 + row / G;
+        const bool valid = row < TQ * G && ti < ql;
+        tok[rho] = valid ? si.cu + ti : -1;
+        head[rho] = kh * G + row % G;
+        limit[rho] = valid ? past + ti : -1;
+        const uint16_t* qrow = qp + ((int64_t)(valid ? tok[rho] : 0) * hq + head[rho]) * D;
+#pragma unroll
+        for (int s = 0; s < NS; ++s)
+          qreg[rho][s] = valid ? ld16(qrow + (4 * s + kq) * 8) : u32x4_t{0, 0, 0, 0};
+      }
+      int wave_kmax = max(limit[0], limit[1]);
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) wave_kmax = max(wave_kmax, __shfl_xor(wave_kmax, o));
+
+      float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f};
+      float4_t acc[2][NT];
+#pragma unroll
+      for (int rho = 0; rho < 2; ++rho)
+#pragma unroll
+        for (int t = 0; t < NT; ++t) acc[rho][t] = float4_t{0.f, 0.f, 0.f, 0.f};
+
+      const int32_t* trow = a.block_table + (int64_t)b * a.max_blocks_per_seq;
+      for (int kt = 0; kt < kend; kt += BN) {
+        __syncthreads();   // all waves are done reading the previous tile
+#pragma unroll
+        for (int p = 0; p < BN / RPP; ++p) {
+          const int jj = p * RPP + tid / CPR;
+          const int c = tid % CPR;
+          const int j = kt + jj;
+          u32x4_t kv = {0, 0, 0, 0}, vv = {0, 0, 0, 0};
+          if (j < kend) {
+            const int blk = trow[j >> a.block_shift];
+            const int64_t src = ((int64_t)blk * a.block_size + (j & (a.block_size - 1))) * row_stride +
+                                (int64_t)kh * D + c * 8;
+            kv = ld16(kc + src);
+            vv = ld16(vc + src);
+          }
+          *reinterpret_cast<u32x4_t*>(&Ks[jj * PITCH + c * 8]) = kv;
+          *reinterpret_cast<u32x4_t*>(&Vs[jj * PITCH + c * 8]) = vv;
+        }
+        __syncthreads();
+        if (kt > wave_kmax) continue;   // tile wholly above this wave's diagonal
+
+        float4_t sacc[4][2];
+#pragma unroll
+        for (int kap = 0; kap < 4; ++kap) {
+          sacc[kap][0] = float4_t{0.f, 0.f, 0.f, 0.f};
+          sacc[kap][1] = float4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int s = 0; s < NS; ++s) {
+            const u32x4_t ka = ld16(&Ks[(16 * kap + r16) * PITCH + (4 * s + kq) * 8]);
+            sacc[kap][0] = Elt<T>::mfma32(ka, qreg[0][s], sacc[kap][0]);
+            sacc[kap][1] = Elt<T>::mfma32(ka, qreg[1][s], sacc[kap][1]);
+          }
+        }
+
+        u32x4_t pb[2][2];
+#pragma unroll
+        for (int rho = 0; rho < 2; ++rho) {
+          float sv[4][4];
+          float cmax = -INFINITY;
+#pragma unroll
+          for (int kap = 0; kap < 4; ++kap)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int key = kt + 16 * kap + 4 * kq + i;
+              sv[kap][i] = key <= limit[rho] ? sacc[kap][rho][i] * a.scale_log2 : -INFINITY;
+              cmax = fmaxf(cmax, sv[kap][i]);
+            }
+          cmax = wave_max_xor16_32(cmax);
+          const float m_new = fmaxf(m[rho], cmax);
+          const float base_m = m_new == -INFINITY ? 0.f : m_new;
+          const float alpha = exp2f(m[rho] - base_m);
+#pragma unroll
+          for (int kap = 0; kap < 4; ++kap)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sv[kap][i] = exp2f(sv[kap][i] - base_m);
+#pragma unroll
+          for (int t = 0; t < NT; ++t) acc[rho][t] *= alpha;
+          // P rounded to the input dtype feeds P.V; the denominator sums
+          // the same rounded values.
+          float psum = 0.f;
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            pb[rho][u] = u32x4_t{Elt<T>::pack2(sv[2 * u][0], sv[2 * u][1]),
+                                 Elt<T>::pack2(sv[2 * u][2], sv[2 * u][3]),
+                                 Elt<T>::pack2(sv[2 * u + 1][0], sv[2 * u + 1][1]),
+                                 Elt<T>::pack2(sv[2 * u + 1][2], sv[2 * u + 1][3])};
+#pragma unroll
+            for (int w = 0; w < 4; ++w) psum = Elt<T>::sum2(pb[rho][u][w], psum);
+          }
+          l[rho] = l[rho] * alpha + psum;
+          m[rho] = m_new;
+        }
+
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          // Contraction element e of lane group kq <-> key 32u + 4kq + e
+          // (e < 4) or 32u + 16 + 4kq + (e - 4): the same keys pb holds.
+          uint32_t vr[8][NT / 2];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int rowv = 32 * u + (e < 4 ? 4 * kq + e : 16 + 4 * kq + (e - 4));
+            const uint16_t* src = &Vs[rowv * PITCH + r16 * NT];
+            if constexpr (NT == 8) {
+              const u32x4_t x = ld16(src);
+#pragma unroll
+              for (int w = 0; w < 4; ++w) vr[e][w] = x[w];
+            } else {
+              const u32x2_t x = ld8(src);
+#pragma unroll
+              for (int w = 0; w < 2; ++w) vr[e][w] = x[w];
+            }
+          }
+#pragma unroll
+          for (int t = 0; t < NT; ++t) {
+            const u32x4_t va = {pair_elem(vr[0][t >> 1], vr[1][t >> 1], t & 1),
+                                pair_elem(vr[2][t >> 1], vr[3][t >> 1], t & 1),
+                                pair_elem(vr[4][t >> 1], vr[5][t >> 1], t & 1),
+                                pair_elem(vr[6][t >> 1], vr[7][t >> 1], t & 1)};
+            acc[0][t] = Elt<T>::mfma32(va, pb[0][u], acc[0][t]);
+            acc[1][t] = Elt<T>::mfma32(va, pb[1][u], acc[1][t]);
+          }
+        }
+      }
+
+#pragma unroll
+      for (int rho = 0; rho < 2; ++rho) {
+        const float l_tot = wave_sum_xor16_32(l[rho]);
+        if (tok[rho] < 0) continue;
+        const float inv = 1.f / l_tot;
+        uint16_t* orow = op + ((int64_t)tok[rho] * hq + head[rho]) * D;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          uint32_t w[NT / 2];
+#pragma unroll
+          for (int t = 0; t < NT; t += 2)
+            w[t / 2] = Elt<T>::pack2(acc[rho][t][r] * inv, acc[rho][t + 1][r] * inv);
+          uint16_t* dst = orow + (4 * kq + r) * NT;
+          if constexpr (NT == 8) {
+            *reinterpret_cast<u32x4_t*>(dst) = u32x4_t{w[0], w[1], w[2], w[3]};
+          } else {
+            *reinterpret_cast<u32x2_t*>(dst) = u32x2_t{w[0], w[1]};
+          }
+        }
+      }
+    }
+  }
+}
+
+template <typename T>
+static hipError_t prefill_dispatch(const AttnArgs& a, int head_size, int64_t max_blocks, int num_cus,
+                                  hipStream_t st) {
+  const void* fn = head_size == 128 ? (const void*)&prefill_kernel<T, 128> : (const void*)&prefill_kernel<T, 64>;
+  int64_t grid = resident_blocks(fn, num_cus);
+  if (grid > max_blocks) grid = max_blocks;
+  if (grid < 1) grid = 1;
+  if (head_size == 128)
+    hipLaunchKernelGGL((prefill_kernel<T, 128>), dim3((unsigned)grid), dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL((prefill_kernel<T, 64>), dim3((unsigned)grid), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill(const AttnArgs& a, int dtype, int head_size, int64_t max_blocks,
+                         int num_cus, hipStream_t st) {
+  return dtype == 0 ? prefill_dispatch<F16>(a, head_size, max_blocks, num_cus, st)
+                    : prefill_dispatch<BF16>(a, head_size, max_blocks, num_cus, st);
+}
+
+}  // namespace pa

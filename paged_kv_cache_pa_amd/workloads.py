@@ -194,6 +194,21 @@ def mixed(seed=1239, n_prefill=16, n_decode=240):
                    q_lens[order], lens[order], "uniform", seed)
 
 
+def custom(q_lens, seqlens_kv, num_heads, num_kv_heads, head_size=128, block_size=16,
+           dtype="f16", spare_blocks=3, seed=7, dist="uniform", max_blocks_per_seq=None):
+    """An arbitrary batch for edge cases: given lengths, a pool with a few
+    spare (never referenced) blocks, blocks dealt from a seeded permutation."""
+    rng = np.random.default_rng(seed)
+    lens = np.asarray(seqlens_kv, dtype=np.int64)
+    need = -(-lens // block_size)
+    mb = max_blocks_per_seq or max(1, int(need.max()) if len(need) else 1)
+    nb = int(need.sum()) + spare_blocks
+    name = (f"custom: q_len {list(q_lens)}, total_kv {list(seqlens_kv)}, Hq {num_heads} / "
+            f"Hk {num_kv_heads}, D {head_size}, bs {block_size}, {dtype}")
+    return _finish(name, rng, dtype, num_heads, num_kv_heads, head_size, block_size, nb, mb,
+                   q_lens, lens, dist, seed)
+
+
 def by_index(i):
     """Workloads 1..5 (the small matrix is 2; its first GQA case stands in)."""
     if i == 1:

@@ -1,0 +1,108 @@
+"""The C-ABI library on the CPU: it loads, exports every symbol include/pa.h
+declares, and rejects bad arguments on the host before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from paged_kv_cache_pa_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_symbols():
+    text = open(os.path.join(ROOT, "include", "pa.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pa_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.fail("libpa.so is not built (python -m paged_kv_cache_pa_amd.build)")
+    return _lib.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    syms = _declared_symbols()
+    assert set(syms) == set(_lib.EXPORTS)
+    for s in syms:
+        assert getattr(L, s) is not None
+
+
+def test_status_strings(L):
+    assert L.pa_status_string(0) == b"PA_OK"
+    assert L.pa_status_string(2) == b"PA_ERR_NOT_IMPLEMENTED"
+    assert L.pa_status_string(99) == b"PA_ERR_UNKNOWN"
+
+
+def test_workspace_size(L):
+    n = L.pa_attention_workspace_size(256, 256, 512, 32, 8, 128, 16)
+    assert n > 0 and n % 256 == 0
+    assert L.pa_attention_workspace_size(2, 5, 2, 4, 3, 64, 16) == 0      # Hq % Hk
+    assert L.pa_attention_workspace_size(2, 5, 2, 4, 2, 96, 16) == 0      # head size
+    assert L.pa_attention_workspace_size(2, 5, 2, 4, 2, 64, 24) == 0      # block size
+
+
+FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: every call below fails before a launch
+
+
+def _attn(L, **kw):
+    a = dict(q=FAKE, cu=FAKE, lens=FAKE, table=FAKE, kc=FAKE, vc=FAKE, out=FAKE, B=2, T=5, MB=2,
+             NB=8, scale=0.125, hq=4, hk=2, d=64, bs=16, dtype=0, ws=FAKE, wsb=0, st=None)
+    a.update(kw)
+    return L.pa_attention(a["q"], a["cu"], a["lens"], a["table"], a["kc"], a["vc"], a["out"],
+                          a["B"], a["T"], a["MB"], a["NB"], a["scale"], a["hq"], a["hk"], a["d"],
+                          a["bs"], a["dtype"], a["ws"], a["wsb"], a["st"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(d=96), _lib.PA_ERR_NOT_IMPLEMENTED),
+    (dict(d=256), _lib.PA_ERR_NOT_IMPLEMENTED),
+    (dict(bs=8), _lib.PA_ERR_NOT_IMPLEMENTED),
+    (dict(bs=48), _lib.PA_ERR_NOT_IMPLEMENTED),
+    (dict(dtype=7), _lib.PA_ERR_NOT_IMPLEMENTED),
+    (dict(hk=3), _lib.PA_ERR_INVALID_ARGUMENT),
+    (dict(hq=256, hk=1), _lib.PA_ERR_NOT_IMPLEMENTED),
+    (dict(scale=float("nan")), _lib.PA_ERR_INVALID_ARGUMENT),
+    (dict(scale=float("inf")), _lib.PA_ERR_INVALID_ARGUMENT),
+    (dict(B=0), _lib.PA_ERR_INVALID_ARGUMENT),
+    (dict(T=-1), _lib.PA_ERR_INVALID_ARGUMENT),
+    (dict(q=None), _lib.PA_ERR_INVALID_ARGUMENT),
+    (dict(table=None), _lib.PA_ERR_INVALID_ARGUMENT),
+    (dict(ws=None, wsb=1 << 30), _lib.PA_ERR_INVALID_ARGUMENT),
+    (dict(ws=ctypes.c_void_p(0x1010), wsb=1 << 30), _lib.PA_ERR_INVALID_ARGUMENT),  # unaligned
+    (dict(wsb=16), _lib.PA_ERR_WORKSPACE_TOO_SMALL),
+    (dict(NB=1 << 28, bs=16), _lib.PA_ERR_NOT_IMPLEMENTED),   # slots beyond int32
+])
+def test_attention_rejects_on_host(L, kw, status):
+    assert _attn(L, **kw) == status
+    assert L.pa_last_error() != b""
+
+
+def test_attention_empty_call_is_ok(L):
+    assert _attn(L, T=0, q=None, out=None, ws=None) == _lib.PA_OK
+
+
+def _scatter(L, **kw):
+    a = dict(k=FAKE, v=FAKE, slots=FAKE, kc=FAKE, vc=FAKE, T=5, NB=8, hk=2, d=64, bs=16, dtype=0)
+    a.update(kw)
+    return L.pa_scatter_kv(a["k"], a["v"], a["slots"], a["kc"], a["vc"], a["T"], a["NB"],
+                           a["hk"], a["d"], a["bs"], a["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(d=60), _lib.PA_ERR_NOT_IMPLEMENTED),
+    (dict(dtype=3), _lib.PA_ERR_NOT_IMPLEMENTED),
+    (dict(T=-2), _lib.PA_ERR_INVALID_ARGUMENT),
+    (dict(hk=0), _lib.PA_ERR_INVALID_ARGUMENT),
+    (dict(slots=None), _lib.PA_ERR_INVALID_ARGUMENT),
+    (dict(NB=1 << 30, bs=16), _lib.PA_ERR_NOT_IMPLEMENTED),
+])
+def test_scatter_rejects_on_host(L, kw, status):
+    assert _scatter(L, **kw) == status
+
+
+def test_scatter_empty_call_is_ok(L):
+    assert _scatter(L, T=0, k=None, v=None, slots=None) == _lib.PA_OK
