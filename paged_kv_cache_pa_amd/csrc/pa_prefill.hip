@@ -13,42 +13,77 @@
 // that share kh share every K/V tile.  Items come from 8 per-XCD queues
 // (work-group w serves queue w % 8 first, then steals from the others).
 // Each of the 4 waves owns 32 rows (two 16-row groups).  Per 64-key tile:
-//   K, V rows resolved through the block table, 128-bit loads -> LDS
+//   K, V rows resolved through the block table (one block id per wave per
+//   tile), copied HBM -> LDS by 128-bit direct-to-LDS loads, double buffered
 //   S^T = K . Q^T          16x16x32 MFMA (fp16/bf16 in, fp32 acc)
 //   causal mask key <= past + i, online softmax in fp32 (exp2)
 //   O^T += V^T . P^T       16x16x32 MFMA, P rounded to the input dtype
 // Key tiles beyond the tile's last visible key are never loaded, and a wave
 // skips the matrix work of key tiles that lie wholly above its rows'
-// diagonal.  Key rows past the visible range are zero-filled in LDS, so NaN
-// in unused cache slots cannot reach the P.V product.
+// diagonal; the causal mask is applied only on tiles that cross a row's
+// diagonal, and the output accumulators are rescaled only when a row's
+// running max moves.  Key rows past the visible range are replaced by the
+// last visible row, so NaN in unused cache slots never enters LDS.
 #include "pa_common.hpp"
 #include "pa_internal.hpp"
 
 namespace pa {
 
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// xor-16 / xor-32 lane exchanges as VALU permutes (no LDS round trip).
+__device__ inline float max_xor16_32(float v) {
+  auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ inline float sum_xor16_32(float v) {
+  auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// K/V tiles live in LDS as unpadded rows of D halfs whose 16-byte chunks are
+// XOR-swizzled by the row index (chunk c of row r sits in slot
+// c ^ (r % (D/8))), which keeps both the row-wise K reads and the
+// column-wise V reads free of bank conflicts.  The tiles are filled by
+// global_load_lds_dwordx4 (HBM/L2 -> LDS without registers), double
+// buffered: the loads of tile i+1 are in flight while tile i is computed.
 template <typename T, int D>
-__global__ __launch_bounds__(256) void prefill_kernel(AttnArgs a) {
+__global__ __launch_bounds__(256, 2) void prefill_kernel(AttnArgs a) {
   constexpr int NS = D / 32;            // QK^T steps
   constexpr int NT = D / 16;            // O^T tiles (halfs per lane per V row)
   constexpr int BN = kPrefillKeys;      // keys per K/V tile
-  constexpr int PITCH = D + 8;          // LDS row pitch (halfs): +16 B vs bank conflicts
+  constexpr int ROWB = D * 2;           // bytes per K/V row
   constexpr int CPR = D / 8;            // 16-byte chunks per row
-  constexpr int RPP = 256 / CPR;        // rows per cooperative pass
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[BN * PITCH];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[BN * PITCH];
+  constexpr int RPI = 1024 / ROWB;      // rows per wave-wide 1 KiB LDS load
+  constexpr int LPW = 16 / RPI;         // loads per wave per operand (16 rows)
+  constexpr int TB = BN * ROWB;         // bytes per operand tile
+  // Two separate LDS objects (not one array indexed by buffer) so the
+  // compiler can tell the prefetch target from the tile being read and does
+  // not wait for the prefetch before reading.
+  __shared__ __attribute__((aligned(1024))) unsigned char lds0[2 * TB];   // [K, V]
+  __shared__ __attribute__((aligned(1024))) unsigned char lds1[2 * TB];
   __shared__ int item_sh;
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
   const int r16 = lane & 15, kq = lane >> 4;
   const int hk = a.num_kv_heads, G = a.group, hq = a.num_heads;
   const int TQ = a.tokens_per_tile;
+  const int bsz = a.block_size, shift = a.block_shift;
   const int64_t row_stride = (int64_t)hk * D;
+  const float c = a.scale_log2;
   const uint16_t* __restrict__ qp = (const uint16_t*)a.q;
   const uint16_t* __restrict__ kc = (const uint16_t*)a.k_cache;
   const uint16_t* __restrict__ vc = (const uint16_t*)a.v_cache;
   uint16_t* __restrict__ op = (uint16_t*)a.out;
   const int home = blockIdx.x % kQueues;
+
+  auto slot = [](int row, int chunk) { return row * ROWB + ((chunk ^ (row & (CPR - 1))) << 4); };
 
   for (int qi = 0; qi < kQueues; ++qi) {
     const int x = (home + qi) % kQueues;
@@ -57,7 +92,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(AttnArgs a) {
     for (;;) {
       if (tid == 0) item_sh = atomicAdd(a.counters_rw + kCtrPrefill + x, 1);
       __syncthreads();
-      const int k = item_sh;
+      const int k = __builtin_amdgcn_readfirstlane(item_sh);   // uniform: scalar loads below
       __syncthreads();
       if (k >= qlen) break;
       const int4 itm = a.pf_items[qstart + k];
@@ -68,6 +103,28 @@ __global__ __launch_bounds__(256) void prefill_kernel(AttnArgs a) {
       const int i0 = tile * TQ;
       const int last_tok = min(i0 + TQ, ql) - 1;
       const int kend = past + last_tok + 1;   // keys visible to the tile's last row
+      const int32_t* trow = a.block_table + (int64_t)b * a.max_blocks_per_seq;
+
+      // Rows [16*wave, 16*wave+16) of the K and V tiles starting at key kt;
+      // keys at or past kend are clamped onto key kend-1 (finite data, masked).
+      // Block id of this wave's 16-row group of the tile at key kt (one
+      // scalar load; rows of a group never straddle a block).
+      auto block_of = [&](int kt) { return trow[min(kt + 16 * wave, kend - 1) >> shift]; };
+      auto issue = [&](int kt, unsigned char* dst, int blk) {
+        const int64_t blk_row = (int64_t)blk * bsz;
+        unsigned char* kdst = dst + 16 * wave * ROWB;
+#pragma unroll
+        for (int p = 0; p < LPW; ++p) {
+          const int row = 16 * wave + p * RPI + lane / CPR;
+          const int j = min(kt + row, kend - 1);
+          const int gch = (lane % CPR) ^ (row & (CPR - 1));
+          const int64_t off = (blk_row + (j & (bsz - 1))) * row_stride + (int64_t)kh * D + gch * 8;
+          __builtin_amdgcn_global_load_lds(kc + off, (lds_ptr_t)(kdst + p * 1024), 16, 0, 0);
+          __builtin_amdgcn_global_load_lds(vc + off, (lds_ptr_t)(kdst + TB + p * 1024), 16, 0, 0);
+        }
+      };
+      issue(0, lds0, block_of(0));
+      int blk_next = BN < kend ? block_of(BN) : 0;   // fetched one tile ahead
 
       // Q^T operands and causal limits of this lane's two row groups.
       u32x4_t qreg[2][NS];
@@ -86,8 +143,12 @@ __global__ __launch_bounds__(256) void prefill_kernel(AttnArgs a) {
           qreg[rho][s] = valid ? ld16(qrow + (4 * s + kq) * 8) : u32x4_t{0, 0, 0, 0};
       }
       int wave_kmax = max(limit[0], limit[1]);
+      int wave_kmin = min(limit[0], limit[1]);
 #pragma unroll
-      for (int o = 1; o < 64; o <<= 1) wave_kmax = max(wave_kmax, __shfl_xor(wave_kmax, o));
+      for (int o = 1; o < 64; o <<= 1) {
+        wave_kmax = max(wave_kmax, __shfl_xor(wave_kmax, o));
+        wave_kmin = min(wave_kmin, __shfl_xor(wave_kmin, o));
+      }
 
       float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f};
       float4_t acc[2][NT];
@@ -96,114 +157,132 @@ __global__ __launch_bounds__(256) void prefill_kernel(AttnArgs a) {
 #pragma unroll
         for (int t = 0; t < NT; ++t) acc[rho][t] = float4_t{0.f, 0.f, 0.f, 0.f};
 
-      const int32_t* trow = a.block_table + (int64_t)b * a.max_blocks_per_seq;
-      for (int kt = 0; kt < kend; kt += BN) {
-        __syncthreads();   // all waves are done reading the previous tile
-#pragma unroll
-        for (int p = 0; p < BN / RPP; ++p) {
-          const int jj = p * RPP + tid / CPR;
-          const int c = tid % CPR;
-          const int j = kt + jj;
-          u32x4_t kv = {0, 0, 0, 0}, vv = {0, 0, 0, 0};
-          if (j < kend) {
-            const int blk = trow[j >> a.block_shift];
-            const int64_t src = ((int64_t)blk * a.block_size + (j & (a.block_size - 1))) * row_stride +
-                                (int64_t)kh * D + c * 8;
-            kv = ld16(kc + src);
-            vv = ld16(vc + src);
-          }
-          *reinterpret_cast<u32x4_t*>(&Ks[jj * PITCH + c * 8]) = kv;
-          *reinterpret_cast<u32x4_t*>(&Vs[jj * PITCH + c * 8]) = vv;
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      auto step = [&](int kt, const unsigned char* cur, unsigned char* nxt) {
+        if (kt + BN < kend) {
+          issue(kt + BN, nxt, blk_next);
+          blk_next = kt + 2 * BN < kend ? block_of(kt + 2 * BN) : 0;
         }
-        __syncthreads();
-        if (kt > wave_kmax) continue;   // tile wholly above this wave's diagonal
+        const unsigned char* kb = cur;
+        const unsigned char* vb = cur + TB;
 
-        float4_t sacc[4][2];
+        if (kt <= wave_kmax) {   // else: tile wholly above this wave's diagonal
+          float4_t sacc[4][2];
 #pragma unroll
-        for (int kap = 0; kap < 4; ++kap) {
-          sacc[kap][0] = float4_t{0.f, 0.f, 0.f, 0.f};
-          sacc[kap][1] = float4_t{0.f, 0.f, 0.f, 0.f};
+          for (int kap = 0; kap < 4; ++kap) {
+            sacc[kap][0] = float4_t{0.f, 0.f, 0.f, 0.f};
+            sacc[kap][1] = float4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int s = 0; s < NS; ++s) {
-            const u32x4_t ka = ld16(&Ks[(16 * kap + r16) * PITCH + (4 * s + kq) * 8]);
-            sacc[kap][0] = Elt<T>::mfma32(ka, qreg[0][s], sacc[kap][0]);
-            sacc[kap][1] = Elt<T>::mfma32(ka, qreg[1][s], sacc[kap][1]);
-          }
-        }
-
-        u32x4_t pb[2][2];
-#pragma unroll
-        for (int rho = 0; rho < 2; ++rho) {
-          float sv[4][4];
-          float cmax = -INFINITY;
-#pragma unroll
-          for (int kap = 0; kap < 4; ++kap)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int key = kt + 16 * kap + 4 * kq + i;
-              sv[kap][i] = key <= limit[rho] ? sacc[kap][rho][i] * a.scale_log2 : -INFINITY;
-              cmax = fmaxf(cmax, sv[kap][i]);
+            for (int s = 0; s < NS; ++s) {
+              const u32x4_t ka = *reinterpret_cast<const u32x4_t*>(kb + slot(16 * kap + r16, 4 * s + kq));
+              sacc[kap][0] = Elt<T>::mfma32(ka, qreg[0][s], sacc[kap][0]);
+              sacc[kap][1] = Elt<T>::mfma32(ka, qreg[1][s], sacc[kap][1]);
             }
-          cmax = wave_max_xor16_32(cmax);
-          const float m_new = fmaxf(m[rho], cmax);
-          const float base_m = m_new == -INFINITY ? 0.f : m_new;
-          const float alpha = exp2f(m[rho] - base_m);
+          }
+
+          const bool diag = kt + BN - 1 > wave_kmin;   // some row needs the causal mask here
+          u32x4_t pb[2][2];
 #pragma unroll
-          for (int kap = 0; kap < 4; ++kap)
+          for (int rho = 0; rho < 2; ++rho) {
+            float sv[4][4];
+            float mt = -INFINITY;
+            if (diag) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) sv[kap][i] = exp2f(sv[kap][i] - base_m);
+              for (int kap = 0; kap < 4; ++kap)
 #pragma unroll
-          for (int t = 0; t < NT; ++t) acc[rho][t] *= alpha;
-          // P rounded to the input dtype feeds P.V; the denominator sums
-          // the same rounded values.
-          float psum = 0.f;
+                for (int i = 0; i < 4; ++i) {
+                  const int key = kt + 16 * kap + 4 * kq + i;
+                  sv[kap][i] = key <= limit[rho] ? sacc[kap][rho][i] * c : -INFINITY;
+                  mt = fmaxf(mt, sv[kap][i]);
+                }
+            } else {
+              float hi = -INFINITY, lo = INFINITY;
+#pragma unroll
+              for (int kap = 0; kap < 4; ++kap)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                  hi = fmaxf(hi, sacc[kap][rho][i]);
+                  lo = fminf(lo, sacc[kap][rho][i]);
+                }
+              mt = c >= 0.f ? hi * c : lo * c;
+            }
+            mt = max_xor16_32(mt);
+            const float m_new = fmaxf(m[rho], mt);
+            const float base_m = m_new == -INFINITY ? 0.f : m_new;
+            const float alpha = exp2f(m[rho] - base_m);
+            if (diag) {
+#pragma unroll
+              for (int kap = 0; kap < 4; ++kap)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) sv[kap][i] = exp2f(sv[kap][i] - base_m);
+            } else {
+#pragma unroll
+              for (int kap = 0; kap < 4; ++kap)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) sv[kap][i] = exp2f(fmaf(sacc[kap][rho][i], c, -base_m));
+            }
+            if (__any(alpha != 1.f)) {   // rescale only when some row's max moved
+#pragma unroll
+              for (int t = 0; t < NT; ++t) acc[rho][t] *= alpha;
+            }
+            // P rounded to the input dtype feeds P.V; the denominator sums
+            // the same rounded values.
+            float psum = 0.f;
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+              pb[rho][u] = u32x4_t{Elt<T>::pack2(sv[2 * u][0], sv[2 * u][1]),
+                                   Elt<T>::pack2(sv[2 * u][2], sv[2 * u][3]),
+                                   Elt<T>::pack2(sv[2 * u + 1][0], sv[2 * u + 1][1]),
+                                   Elt<T>::pack2(sv[2 * u + 1][2], sv[2 * u + 1][3])};
+#pragma unroll
+              for (int w = 0; w < 4; ++w) psum = Elt<T>::sum2(pb[rho][u][w], psum);
+            }
+            l[rho] = l[rho] * alpha + psum;
+            m[rho] = m_new;
+          }
+
 #pragma unroll
           for (int u = 0; u < 2; ++u) {
-            pb[rho][u] = u32x4_t{Elt<T>::pack2(sv[2 * u][0], sv[2 * u][1]),
-                                 Elt<T>::pack2(sv[2 * u][2], sv[2 * u][3]),
-                                 Elt<T>::pack2(sv[2 * u + 1][0], sv[2 * u + 1][1]),
-                                 Elt<T>::pack2(sv[2 * u + 1][2], sv[2 * u + 1][3])};
+            // Contraction element e of lane group kq <-> key 32u + 4kq + e
+            // (e < 4) or 32u + 16 + 4kq + (e - 4): the same keys pb holds.
+            uint32_t vr[8][NT / 2];
 #pragma unroll
-            for (int w = 0; w < 4; ++w) psum = Elt<T>::sum2(pb[rho][u][w], psum);
-          }
-          l[rho] = l[rho] * alpha + psum;
-          m[rho] = m_new;
-        }
-
+            for (int e = 0; e < 8; ++e) {
+              const int rowv = 32 * u + (e < 4 ? 4 * kq + e : 16 + 4 * kq + (e - 4));
+              if constexpr (NT == 8) {
+                const u32x4_t xv = *reinterpret_cast<const u32x4_t*>(vb + slot(rowv, r16));
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          // Contraction element e of lane group kq <-> key 32u + 4kq + e
-          // (e < 4) or 32u + 16 + 4kq + (e - 4): the same keys pb holds.
-          uint32_t vr[8][NT / 2];
+                for (int w = 0; w < 4; ++w) vr[e][w] = xv[w];
+              } else {
+                const u32x2_t xv = *reinterpret_cast<const u32x2_t*>(vb + slot(rowv, r16 >> 1) +
+                                                                     ((r16 & 1) << 3));
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int rowv = 32 * u + (e < 4 ? 4 * kq + e : 16 + 4 * kq + (e - 4));
-            const uint16_t* src = &Vs[rowv * PITCH + r16 * NT];
-            if constexpr (NT == 8) {
-              const u32x4_t x = ld16(src);
+                for (int w = 0; w < 2; ++w) vr[e][w] = xv[w];
+              }
+            }
 #pragma unroll
-              for (int w = 0; w < 4; ++w) vr[e][w] = x[w];
-            } else {
-              const u32x2_t x = ld8(src);
-#pragma unroll
-              for (int w = 0; w < 2; ++w) vr[e][w] = x[w];
+            for (int t = 0; t < NT; ++t) {
+              const u32x4_t va = {pair_elem(vr[0][t >> 1], vr[1][t >> 1], t & 1),
+                                  pair_elem(vr[2][t >> 1], vr[3][t >> 1], t & 1),
+                                  pair_elem(vr[4][t >> 1], vr[5][t >> 1], t & 1),
+                                  pair_elem(vr[6][t >> 1], vr[7][t >> 1], t & 1)};
+              acc[0][t] = Elt<T>::mfma32(va, pb[0][u], acc[0][t]);
+              acc[1][t] = Elt<T>::mfma32(va, pb[1][u], acc[1][t]);
             }
           }
-#pragma unroll
-          for (int t = 0; t < NT; ++t) {
-            const u32x4_t va = {pair_elem(vr[0][t >> 1], vr[1][t >> 1], t & 1),
-                                pair_elem(vr[2][t >> 1], vr[3][t >> 1], t & 1),
-                                pair_elem(vr[4][t >> 1], vr[5][t >> 1], t & 1),
-                                pair_elem(vr[6][t >> 1], vr[7][t >> 1], t & 1)};
-            acc[0][t] = Elt<T>::mfma32(va, pb[0][u], acc[0][t]);
-            acc[1][t] = Elt<T>::mfma32(va, pb[1][u], acc[1][t]);
-          }
         }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();   // next tile landed; everyone is done with this one
+      };
+      for (int kt = 0; kt < kend; kt += 2 * BN) {
+        step(kt, lds0, lds1);
+        if (kt + BN < kend) step(kt + BN, lds1, lds0);
       }
 
 #pragma unroll
       for (int rho = 0; rho < 2; ++rho) {
-        const float l_tot = wave_sum_xor16_32(l[rho]);
+        const float l_tot = sum_xor16_32(l[rho]);
         if (tok[rho] < 0) continue;
         const float inv = 1.f / l_tot;
         uint16_t* orow = op + ((int64_t)tok[rho] * hq + head[rho]) * D;
