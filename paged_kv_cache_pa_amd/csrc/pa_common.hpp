@@ -42,11 +42,11 @@ template <> struct Elt<F16> {
     return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(half4_t, a),
                                                  __builtin_bit_cast(half4_t, b), c, 0, 0, 0);
   }
-  // fp32 -> storage bits, round to nearest even.
-  __device__ static inline uint32_t bits(float x) {
-    return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)x);
+  // Two fp32 -> two packed fp16, round to nearest even (v_cvt_pk_f16_f32).
+  __device__ static inline uint32_t pack2(float lo, float hi) {
+    typedef float f2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f2{lo, hi}, half2_t));
   }
-  __device__ static inline uint32_t pack2(float lo, float hi) { return bits(lo) | (bits(hi) << 16); }
   // acc + the two packed values (exact products by 1, fp32 accumulate).
   __device__ static inline float sum2(uint32_t packed, float acc) {
     return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, packed), half2_t{1, 1}, acc, false);
@@ -62,15 +62,20 @@ template <> struct Elt<BF16> {
     return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(short4_t, a),
                                                      __builtin_bit_cast(short4_t, b), c, 0, 0, 0);
   }
-  __device__ static inline uint32_t bits(float x) {
-    return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)x);
+  // Two fp32 -> two packed bf16, round to nearest even (v_cvt_pk_bf16_f32).
+  __device__ static inline uint32_t pack2(float lo, float hi) {
+    typedef float f2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f2{lo, hi}, bf16x2_t));
   }
-  __device__ static inline uint32_t pack2(float lo, float hi) { return bits(lo) | (bits(hi) << 16); }
   __device__ static inline float sum2(uint32_t packed, float acc) {
     return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, packed),
                                            bf16x2_t{1, 1}, acc, false);
   }
 };
+
+// 2^x on the transcendental unit (v_exp_f32); softmax weights below 2^-126
+// flush to zero, which the result cannot resolve anyway.
+__device__ inline float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Element e (0..7) of 8 packed 16-bit values held in 4 dwords.
 __device__ inline uint32_t half_of(u32x4_t v, int e) {

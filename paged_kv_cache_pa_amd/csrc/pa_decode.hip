@@ -136,10 +136,10 @@ __global__ __launch_bounds__(256) void decode_kernel(AttnArgs a) {
       cmax = wave_max_xor16_32(cmax);
       const float m_new = fmaxf(m, cmax);
       const float base_m = m_new == -INFINITY ? 0.f : m_new;
-      const float alpha = exp2f(m - base_m);
+      const float alpha = exp2_fast(m - base_m);
       float p[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) p[i] = exp2f(sv[i] - base_m);
+      for (int i = 0; i < 4; ++i) p[i] = exp2_fast(sv[i] - base_m);
       // P enters P.V rounded to the input dtype; the denominator sums the
       // same rounded values so the weights of each column sum to one.
       const u32x2_t pb = {Elt<T>::pack2(p[0], p[1]), Elt<T>::pack2(p[2], p[3])};
@@ -215,7 +215,7 @@ __global__ __launch_bounds__(256) void combine_kernel(AttnArgs a) {
     for (int s = 0; s < nsplit; ++s) {
       const int64_t row = row0 + (int64_t)s * ncols;
       const float2 ml = a.part_ml[row];
-      const float f = ml.x == -INFINITY ? 0.f : exp2f(ml.x - M);
+      const float f = ml.x == -INFINITY ? 0.f : exp2_fast(ml.x - M);
       const float2 v = *reinterpret_cast<const float2*>(a.part_acc + row * D + d);
       num0 += f * v.x;
       num1 += f * v.y;

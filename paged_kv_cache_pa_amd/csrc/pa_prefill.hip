@@ -30,6 +30,7 @@
 namespace pa {
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
+typedef __attribute__((address_space(3))) short4_t* lds_s4_t;
 
 // xor-16 / xor-32 lane exchanges as VALU permutes (no LDS round trip).
 __device__ inline float max_xor16_32(float v) {
@@ -83,7 +84,13 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(AttnArgs a) {
   uint16_t* __restrict__ op = (uint16_t*)a.out;
   const int home = blockIdx.x % kQueues;
 
-  auto slot = [](int row, int chunk) { return row * ROWB + ((chunk ^ (row & (CPR - 1))) << 4); };
+  // Slot of 16-byte chunk `chunk` of tile row `row`: XOR with the row's low
+  // log2(CPR) bits rotated left by one.  Row-wise K reads (16 rows, one
+  // chunk) and transposed V reads (4 rows, two adjacent chunks) then touch
+  // distinct slots.
+  constexpr int CB = CPR == 16 ? 4 : 3;
+  auto swz = [](int row) { return ((row << 1) | ((row >> (CB - 1)) & 1)) & (CPR - 1); };
+  auto slot = [&](int row, int chunk) { return row * ROWB + ((chunk ^ swz(row)) << 4); };
 
   for (int qi = 0; qi < kQueues; ++qi) {
     const int x = (home + qi) % kQueues;
@@ -117,7 +124,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(AttnArgs a) {
         for (int p = 0; p < LPW; ++p) {
           const int row = 16 * wave + p * RPI + lane / CPR;
           const int j = min(kt + row, kend - 1);
-          const int gch = (lane % CPR) ^ (row & (CPR - 1));
+          const int gch = (lane % CPR) ^ swz(row);
           const int64_t off = (blk_row + (j & (bsz - 1))) * row_stride + (int64_t)kh * D + gch * 8;
           __builtin_amdgcn_global_load_lds(kc + off, (lds_ptr_t)(kdst + p * 1024), 16, 0, 0);
           __builtin_amdgcn_global_load_lds(vc + off, (lds_ptr_t)(kdst + TB + p * 1024), 16, 0, 0);
@@ -210,17 +217,17 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(AttnArgs a) {
             mt = max_xor16_32(mt);
             const float m_new = fmaxf(m[rho], mt);
             const float base_m = m_new == -INFINITY ? 0.f : m_new;
-            const float alpha = exp2f(m[rho] - base_m);
+            const float alpha = exp2_fast(m[rho] - base_m);
             if (diag) {
 #pragma unroll
               for (int kap = 0; kap < 4; ++kap)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) sv[kap][i] = exp2f(sv[kap][i] - base_m);
+                for (int i = 0; i < 4; ++i) sv[kap][i] = exp2_fast(sv[kap][i] - base_m);
             } else {
 #pragma unroll
               for (int kap = 0; kap < 4; ++kap)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) sv[kap][i] = exp2f(fmaf(sacc[kap][rho][i], c, -base_m));
+                for (int i = 0; i < 4; ++i) sv[kap][i] = exp2_fast(fmaf(sacc[kap][rho][i], c, -base_m));
             }
             if (__any(alpha != 1.f)) {   // rescale only when some row's max moved
 #pragma unroll
@@ -242,31 +249,28 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(AttnArgs a) {
             m[rho] = m_new;
           }
 
+          // O^T tile t covers d = 16t .. 16t+15.  ds_read_b64_tr_b16: within
+          // each 16-lane group, result lane i gets element i % 4 of the
+          // 8 bytes read by source lanes 4r + i / 4 (r = 0..3).  Source lane
+          // (kq, r, q) reads key row 4kq + r at d = 16t + 4q .. +3, so lane i
+          // receives d = 16t + i of keys 4kq .. 4kq+3: the V^T operand, with
+          // contraction element e <-> key 32u + 4kq + e (e < 4) or
+          // 32u + 16 + 4kq + (e - 4), the same keys pb holds.
+          const int r4 = (lane & 15) >> 2, q4 = lane & 3;
 #pragma unroll
           for (int u = 0; u < 2; ++u) {
-            // Contraction element e of lane group kq <-> key 32u + 4kq + e
-            // (e < 4) or 32u + 16 + 4kq + (e - 4): the same keys pb holds.
-            uint32_t vr[8][NT / 2];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              const int rowv = 32 * u + (e < 4 ? 4 * kq + e : 16 + 4 * kq + (e - 4));
-              if constexpr (NT == 8) {
-                const u32x4_t xv = *reinterpret_cast<const u32x4_t*>(vb + slot(rowv, r16));
-#pragma unroll
-                for (int w = 0; w < 4; ++w) vr[e][w] = xv[w];
-              } else {
-                const u32x2_t xv = *reinterpret_cast<const u32x2_t*>(vb + slot(rowv, r16 >> 1) +
-                                                                     ((r16 & 1) << 3));
-#pragma unroll
-                for (int w = 0; w < 2; ++w) vr[e][w] = xv[w];
-              }
-            }
+            const int R0 = 32 * u + 4 * kq + r4;
 #pragma unroll
             for (int t = 0; t < NT; ++t) {
-              const u32x4_t va = {pair_elem(vr[0][t >> 1], vr[1][t >> 1], t & 1),
-                                  pair_elem(vr[2][t >> 1], vr[3][t >> 1], t & 1),
-                                  pair_elem(vr[4][t >> 1], vr[5][t >> 1], t & 1),
-                                  pair_elem(vr[6][t >> 1], vr[7][t >> 1], t & 1)};
+              const int chunk = 2 * t + (q4 >> 1);
+              const int boff = (q4 & 1) << 3;
+              const short4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                  (lds_s4_t)(vb + slot(R0, chunk) + boff));
+              const short4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                  (lds_s4_t)(vb + slot(R0 + 16, chunk) + boff));
+              const u32x2_t l2 = __builtin_bit_cast(u32x2_t, lo);
+              const u32x2_t h2 = __builtin_bit_cast(u32x2_t, hi);
+              const u32x4_t va = {l2[0], l2[1], h2[0], h2[1]};
               acc[0][t] = Elt<T>::mfma32(va, pb[0][u], acc[0][t]);
               acc[1][t] = Elt<T>::mfma32(va, pb[1][u], acc[1][t]);
             }
@@ -287,17 +291,10 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(AttnArgs a) {
         const float inv = 1.f / l_tot;
         uint16_t* orow = op + ((int64_t)tok[rho] * hq + head[rho]) * D;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          uint32_t w[NT / 2];
-#pragma unroll
-          for (int t = 0; t < NT; t += 2)
-            w[t / 2] = Elt<T>::pack2(acc[rho][t][r] * inv, acc[rho][t + 1][r] * inv);
-          uint16_t* dst = orow + (4 * kq + r) * NT;
-          if constexpr (NT == 8) {
-            *reinterpret_cast<u32x4_t*>(dst) = u32x4_t{w[0], w[1], w[2], w[3]};
-          } else {
-            *reinterpret_cast<u32x2_t*>(dst) = u32x2_t{w[0], w[1]};
-          }
+        for (int t = 0; t < NT; ++t) {   // lane holds d = 16t + 4kq + r, r = 0..3
+          *reinterpret_cast<u32x2_t*>(orow + 16 * t + 4 * kq) =
+              u32x2_t{Elt<T>::pack2(acc[rho][t][0] * inv, acc[rho][t][1] * inv),
+                      Elt<T>::pack2(acc[rho][t][2] * inv, acc[rho][t][3] * inv)};
         }
       }
     }
