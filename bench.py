@@ -163,6 +163,27 @@ def measured_traffic(kernel, workload):
     return ent.get("bytes_per_launch")
 
 
+def copy_bandwidth(torch, nbytes=2 << 30, reps=10):
+    """Device-to-device copy of a 2 GiB buffer (read + write counted), the
+    measured reference for the HBM peak on this machine."""
+    src = torch.empty(nbytes // 2, dtype=torch.float16, device="cuda")
+    src.fill_(1.0)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) / reps * 1e-3
+    del src, dst
+    torch.cuda.empty_cache()
+    return 2 * nbytes / t / 1e9
+
+
 # ------------------------------------------------------------- CPU baseline
 def cpu_baseline(wl, W, torch, budget_s=20.0):
     """The fp64 oracle (as it stands) on a bounded sample of the workload:
@@ -224,6 +245,8 @@ def main():
     ap.add_argument("--workload", default="mixed", choices=sorted(WORKLOADS))
     ap.add_argument("--no-extra", action="store_true", help="skip the decode/prefill figures")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-only", action="store_true",
+                    help="only the 2 GiB copy (reference for counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path "
@@ -237,6 +260,10 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     pa._lib.lib()           # fail loudly when the HIP library is missing
+    if args.copy_only:
+        print(json.dumps({"copy_GBps": copy_bandwidth(torch), "bytes": 2 * (2 << 30)}))
+        return
+    copy_gbps = copy_bandwidth(torch)
 
     wl = W.by_index(WORKLOADS[args.workload])
     ms, wall_ms, per_kernel = time_workload(wl, args.steps, args.warmup, torch, pa, W)
@@ -279,6 +306,7 @@ def main():
         "decode_TBps": head.get("decode_TBps"),
         "prefill_TFLOPs": head.get("prefill_TFLOPs"),
         "kernel_ms": head["kernel_ms"],
+        "copy_GBps": copy_gbps,
         "roofline": roof,
         "extra": extra,
     }

@@ -109,9 +109,9 @@ pa_status_t check_shape(const pa::Shape& s) {
   if (s.num_heads % s.num_kv_heads != 0)
     return fail(PA_ERR_INVALID_ARGUMENT, "num_heads=%d is not a multiple of num_kv_heads=%d",
                 s.num_heads, s.num_kv_heads);
-  if (s.num_heads / s.num_kv_heads > pa::kPrefillRows)
+  if (s.num_heads / s.num_kv_heads > pa::kMaxGroup)
     return fail(PA_ERR_NOT_IMPLEMENTED, "group size %d > %d", s.num_heads / s.num_kv_heads,
-                pa::kPrefillRows);
+                pa::kMaxGroup);
   if (s.head_size != 64 && s.head_size != 128)
     return fail(PA_ERR_NOT_IMPLEMENTED, "head_size=%d (supported: 64, 128)", s.head_size);
   if (!is_pow2(s.block_size) || s.block_size < 16 || s.block_size > 1024)
@@ -126,9 +126,9 @@ pa_status_t check_shape(const pa::Shape& s) {
 
 namespace pa {
 
-int resident_blocks(const void* kernel, int num_cus) {
+int resident_blocks(const void* kernel, int num_cus, int threads) {
   int per_cu = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 256, 0) != hipSuccess ||
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess ||
       per_cu < 1)
     per_cu = 1;
   return per_cu * num_cus;

@@ -16,11 +16,12 @@ constexpr int kSplitKeys = 512;
 // A sequence takes the decode path when q_len * G columns fit one 16-wide
 // matrix-core tile.
 constexpr int kDecodeCols = 16;
-// Prefill tile: 128 (token, head-in-group) rows per work-group, 64 keys per
-// K/V tile.
-constexpr int kPrefillRows = 128;
+// Prefill tile: 256 (token, head-in-group) rows per work-group (8 waves of
+// 32 rows), 64 keys per K/V tile.
+constexpr int kPrefillRows = 256;
 constexpr int kPrefillKeys = 64;
 constexpr int kQueues = 8;  // one prefill work queue per XCD
+constexpr int kMaxGroup = 128;  // largest supported num_heads / num_kv_heads
 constexpr float kLog2e = 1.4426950408889634f;
 
 // Counter block at the start of the workspace (int32 slots).
@@ -96,7 +97,7 @@ hipError_t launch_combine(const AttnArgs& a, int dtype, int head_size, hipStream
 hipError_t launch_prefill(const AttnArgs& a, int dtype, int head_size, int64_t max_blocks,
                           int num_cus, hipStream_t st);
 
-// Work-groups of `kernel` (256 threads) resident at once on the device.
-int resident_blocks(const void* kernel, int num_cus);
+// Work-groups of `kernel` (`threads` per group) resident at once.
+int resident_blocks(const void* kernel, int num_cus, int threads = 256);
 
 }  // namespace pa

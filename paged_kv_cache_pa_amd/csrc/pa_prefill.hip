@@ -31,6 +31,15 @@ namespace pa {
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 typedef __attribute__((address_space(3))) short4_t* lds_s4_t;
+typedef __attribute__((address_space(4))) int32_t const_i32_t;
+
+// Instruction classes for __builtin_amdgcn_sched_group_barrier.
+constexpr int kSchedMfma = 0x008;
+constexpr int kSchedDsRead = 0x100;
+
+// A row's running max is raised only when a tile's max exceeds it by more
+// than this many powers of two (bounds P by 2^8: safe in fp16 and bf16).
+constexpr float kMaxSlack = 8.f;
 
 // xor-16 / xor-32 lane exchanges as VALU permutes (no LDS round trip).
 __device__ inline float max_xor16_32(float v) {
@@ -46,31 +55,61 @@ __device__ inline float sum_xor16_32(float v) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
+// 16-byte-per-lane copy global -> LDS (global_load_lds_dwordx4): lane l's
+// 16 bytes land at LDS byte lds_base + 16 * l.  Issued from inline asm so
+// that the compiler does not treat later LDS reads of *other* ring buffers
+// as dependent on it; the kernel orders these copies itself with explicit
+// vmcnt waits and barriers.  The instruction has no register results.
+__device__ inline void lds_dma16(const void* gptr, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+               :
+               : "s"(lds_base), "v"(gptr)
+               : "memory", "m0");
+}
+
+// Wait until at most N vector-memory operations of this wave are in flight.
+template <int N>
+__device__ inline void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"i"(N) : "memory");
+}
+
 // K/V tiles live in LDS as unpadded rows of D halfs whose 16-byte chunks are
-// XOR-swizzled by the row index (chunk c of row r sits in slot
-// c ^ (r % (D/8))), which keeps both the row-wise K reads and the
-// column-wise V reads free of bank conflicts.  The tiles are filled by
-// global_load_lds_dwordx4 (HBM/L2 -> LDS without registers), double
-// buffered: the loads of tile i+1 are in flight while tile i is computed.
+// XOR-swizzled by the row index (see slot()), which keeps both the row-wise
+// K reads and the transposed V reads free of bank conflicts.  Tiles are
+// filled by global_load_lds_dwordx4 (HBM/L2 -> LDS without registers) into a
+// ring of four buffers; tile i+2 is requested four barrier ticks before it
+// is first read.
+//
+// Eight waves, 32 query rows each, in two groups of four (one wave of each
+// group per SIMD).  The groups run the same per-tile program offset by one
+// phase ("ping-pong"): while group A issues the matrix-core work of a tile
+// (QK^T of tile i and P.V of tile i-1), group B runs the softmax of the
+// previous tile on the vector ALUs, and at the next barrier they swap, so
+// the two halves of every SIMD keep the MFMA and VALU pipes busy together.
 template <typename T, int D>
-__global__ __launch_bounds__(256, 2) void prefill_kernel(AttnArgs a) {
+__global__ __launch_bounds__(512, 1) void prefill_kernel(AttnArgs a) {
   constexpr int NS = D / 32;            // QK^T steps
-  constexpr int NT = D / 16;            // O^T tiles (halfs per lane per V row)
-  constexpr int BN = kPrefillKeys;      // keys per K/V tile
+  constexpr int NT = D / 16;            // O^T tiles
+  constexpr int NR = 2;                 // 16-row groups per wave (32 rows)
+  constexpr int NW = 8;                 // waves per work-group
+  static_assert(kPrefillRows == 32 * NW, "tile rows");
+  constexpr int BN = kPrefillKeys;      // keys per K/V tile (64)
+  constexpr int NK = BN / 16;           // 16-key groups per tile
   constexpr int ROWB = D * 2;           // bytes per K/V row
   constexpr int CPR = D / 8;            // 16-byte chunks per row
   constexpr int RPI = 1024 / ROWB;      // rows per wave-wide 1 KiB LDS load
-  constexpr int LPW = 16 / RPI;         // loads per wave per operand (16 rows)
+  constexpr int RPW = BN / NW;          // tile rows loaded by each wave
+  constexpr int LPW = RPW / RPI;        // loads per wave per operand
   constexpr int TB = BN * ROWB;         // bytes per operand tile
-  // Two separate LDS objects (not one array indexed by buffer) so the
-  // compiler can tell the prefetch target from the tile being read and does
-  // not wait for the prefetch before reading.
-  __shared__ __attribute__((aligned(1024))) unsigned char lds0[2 * TB];   // [K, V]
-  __shared__ __attribute__((aligned(1024))) unsigned char lds1[2 * TB];
+  static_assert(LPW >= 1 && NK % 2 == 0, "tile shape");
+  constexpr int NB = 4;                 // ring buffers of [K tile, V tile]
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[NB * 2 * TB];
   __shared__ int item_sh;
+  const uint32_t lds_addr = (uint32_t)(uintptr_t)(lds_ptr_t)lds;
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave >> 2;            // 0: group A, 1: group B
   const int lane = tid & 63;
   const int r16 = lane & 15, kq = lane >> 4;
   const int hk = a.num_kv_heads, G = a.group, hq = a.num_heads;
@@ -110,34 +149,37 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(AttnArgs a) {
       const int i0 = tile * TQ;
       const int last_tok = min(i0 + TQ, ql) - 1;
       const int kend = past + last_tok + 1;   // keys visible to the tile's last row
-      const int32_t* trow = a.block_table + (int64_t)b * a.max_blocks_per_seq;
+      const int n = (kend + BN - 1) / BN;      // key tiles of this item
+      // The block table is read-only here: read it through the constant
+      // address space so uniform reads become scalar loads (tracked apart
+      // from the vector-memory counter the tile copies use).
+      const const_i32_t* trow =
+          (const const_i32_t*)(a.block_table + (int64_t)b * a.max_blocks_per_seq);
 
-      // Rows [16*wave, 16*wave+16) of the K and V tiles starting at key kt;
-      // keys at or past kend are clamped onto key kend-1 (finite data, masked).
-      // Block id of this wave's 16-row group of the tile at key kt (one
-      // scalar load; rows of a group never straddle a block).
-      auto block_of = [&](int kt) { return trow[min(kt + 16 * wave, kend - 1) >> shift]; };
-      auto issue = [&](int kt, unsigned char* dst, int blk) {
+      // Block id of this wave's RPW-row group of key tile t (rows of a
+      // group never straddle a block: RPW divides the block size).
+      auto block_of = [&](int t) { return trow[min(t * BN + RPW * wave, kend - 1) >> shift]; };
+      // Rows [RPW*wave, RPW*wave+RPW) of the K and V tiles of key tile t;
+      // keys at or past kend are clamped onto key kend-1 (finite, masked).
+      auto issue = [&](int t, int blk) {
         const int64_t blk_row = (int64_t)blk * bsz;
-        unsigned char* kdst = dst + 16 * wave * ROWB;
+        const uint32_t kdst = lds_addr + (uint32_t)((t % NB) * 2 * TB + RPW * wave * ROWB);
 #pragma unroll
         for (int p = 0; p < LPW; ++p) {
-          const int row = 16 * wave + p * RPI + lane / CPR;
-          const int j = min(kt + row, kend - 1);
+          const int row = RPW * wave + p * RPI + lane / CPR;
+          const int j = min(t * BN + row, kend - 1);
           const int gch = (lane % CPR) ^ swz(row);
           const int64_t off = (blk_row + (j & (bsz - 1))) * row_stride + (int64_t)kh * D + gch * 8;
-          __builtin_amdgcn_global_load_lds(kc + off, (lds_ptr_t)(kdst + p * 1024), 16, 0, 0);
-          __builtin_amdgcn_global_load_lds(vc + off, (lds_ptr_t)(kdst + TB + p * 1024), 16, 0, 0);
+          lds_dma16(kc + off, kdst + p * 1024);
+          lds_dma16(vc + off, kdst + TB + p * 1024);
         }
       };
-      issue(0, lds0, block_of(0));
-      int blk_next = BN < kend ? block_of(BN) : 0;   // fetched one tile ahead
 
-      // Q^T operands and causal limits of this lane's two row groups.
-      u32x4_t qreg[2][NS];
-      int limit[2], tok[2], head[2];
+      // Q^T operands and causal limits of this lane's row groups.
+      u32x4_t qreg[NR][NS];
+      int limit[NR], tok[NR], head[NR];
 #pragma unroll
-      for (int rho = 0; rho < 2; ++rho) {
+      for (int rho = 0; rho < NR; ++rho) {
         const int row = 32 * wave + 16 * rho + r16;
         const int ti = i0 + row / G;
         const bool valid = row < TQ * G && ti < ql;
@@ -156,136 +198,232 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(AttnArgs a) {
         wave_kmax = max(wave_kmax, __shfl_xor(wave_kmax, o));
         wave_kmin = min(wave_kmin, __shfl_xor(wave_kmin, o));
       }
+      // Wave-uniform (scalar) so the per-tile branches below are uniform.
+      wave_kmax = __builtin_amdgcn_readfirstlane(wave_kmax);
+      wave_kmin = __builtin_amdgcn_readfirstlane(wave_kmin);
 
-      float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f};
-      float4_t acc[2][NT];
+      float m[NR], l[NR];
+      float4_t acc[NR][NT];
 #pragma unroll
-      for (int rho = 0; rho < 2; ++rho)
+      for (int rho = 0; rho < NR; ++rho) {
+        m[rho] = -INFINITY;
+        l[rho] = 0.f;
 #pragma unroll
         for (int t = 0; t < NT; ++t) acc[rho][t] = float4_t{0.f, 0.f, 0.f, 0.f};
+      }
+      float4_t sacc[NK][NR];   // scores of the tile between its M and V phases
+      u32x4_t pb[NR][NK / 2];  // rounded P of the tile between its V and next M phases
 
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      // Prologue: tiles 0 and 1 resident, block id of tile 2 fetched.
+      issue(0, block_of(0));
+      if (n > 1) issue(1, block_of(1));
+      int blk_next = n > 2 ? block_of(2) : 0;
+      wait_vmcnt<0>();
       __syncthreads();
-      auto step = [&](int kt, const unsigned char* cur, unsigned char* nxt) {
-        if (kt + BN < kend) {
-          issue(kt + BN, nxt, blk_next);
-          blk_next = kt + 2 * BN < kend ? block_of(kt + 2 * BN) : 0;
-        }
-        const unsigned char* kb = cur;
-        const unsigned char* vb = cur + TB;
 
-        if (kt <= wave_kmax) {   // else: tile wholly above this wave's diagonal
-          float4_t sacc[4][2];
-#pragma unroll
-          for (int kap = 0; kap < 4; ++kap) {
-            sacc[kap][0] = float4_t{0.f, 0.f, 0.f, 0.f};
-            sacc[kap][1] = float4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int s = 0; s < NS; ++s) {
-              const u32x4_t ka = *reinterpret_cast<const u32x4_t*>(kb + slot(16 * kap + r16, 4 * s + kq));
-              sacc[kap][0] = Elt<T>::mfma32(ka, qreg[0][s], sacc[kap][0]);
-              sacc[kap][1] = Elt<T>::mfma32(ka, qreg[1][s], sacc[kap][1]);
-            }
-          }
-
-          const bool diag = kt + BN - 1 > wave_kmin;   // some row needs the causal mask here
-          u32x4_t pb[2][2];
-#pragma unroll
-          for (int rho = 0; rho < 2; ++rho) {
-            float sv[4][4];
-            float mt = -INFINITY;
-            if (diag) {
-#pragma unroll
-              for (int kap = 0; kap < 4; ++kap)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                  const int key = kt + 16 * kap + 4 * kq + i;
-                  sv[kap][i] = key <= limit[rho] ? sacc[kap][rho][i] * c : -INFINITY;
-                  mt = fmaxf(mt, sv[kap][i]);
-                }
-            } else {
-              float hi = -INFINITY, lo = INFINITY;
-#pragma unroll
-              for (int kap = 0; kap < 4; ++kap)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                  hi = fmaxf(hi, sacc[kap][rho][i]);
-                  lo = fminf(lo, sacc[kap][rho][i]);
-                }
-              mt = c >= 0.f ? hi * c : lo * c;
-            }
-            mt = max_xor16_32(mt);
-            const float m_new = fmaxf(m[rho], mt);
-            const float base_m = m_new == -INFINITY ? 0.f : m_new;
-            const float alpha = exp2_fast(m[rho] - base_m);
-            if (diag) {
-#pragma unroll
-              for (int kap = 0; kap < 4; ++kap)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) sv[kap][i] = exp2_fast(sv[kap][i] - base_m);
-            } else {
-#pragma unroll
-              for (int kap = 0; kap < 4; ++kap)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) sv[kap][i] = exp2_fast(fmaf(sacc[kap][rho][i], c, -base_m));
-            }
-            if (__any(alpha != 1.f)) {   // rescale only when some row's max moved
-#pragma unroll
-              for (int t = 0; t < NT; ++t) acc[rho][t] *= alpha;
-            }
-            // P rounded to the input dtype feeds P.V; the denominator sums
-            // the same rounded values.
-            float psum = 0.f;
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-              pb[rho][u] = u32x4_t{Elt<T>::pack2(sv[2 * u][0], sv[2 * u][1]),
-                                   Elt<T>::pack2(sv[2 * u][2], sv[2 * u][3]),
-                                   Elt<T>::pack2(sv[2 * u + 1][0], sv[2 * u + 1][1]),
-                                   Elt<T>::pack2(sv[2 * u + 1][2], sv[2 * u + 1][3])};
-#pragma unroll
-              for (int w = 0; w < 4; ++w) psum = Elt<T>::sum2(pb[rho][u][w], psum);
-            }
-            l[rho] = l[rho] * alpha + psum;
-            m[rho] = m_new;
-          }
-
+      // Matrix phase of step i: acc += P_{i-1} V_{i-1}, then S = K_i Q^T
+      // (P dies before S is born: fewer live registers).
+      auto mphase = [&](int i) {
+        const unsigned char* kb = lds + (i % NB) * 2 * TB;            // K of tile i
+        const unsigned char* vb = lds + ((i + NB - 1) % NB) * 2 * TB; // V of tile i-1
+        if (i >= 1 && (i - 1) * BN <= wave_kmax) {
           // O^T tile t covers d = 16t .. 16t+15.  ds_read_b64_tr_b16: within
           // each 16-lane group, result lane i gets element i % 4 of the
           // 8 bytes read by source lanes 4r + i / 4 (r = 0..3).  Source lane
-          // (kq, r, q) reads key row 4kq + r at d = 16t + 4q .. +3, so lane i
-          // receives d = 16t + i of keys 4kq .. 4kq+3: the V^T operand, with
-          // contraction element e <-> key 32u + 4kq + e (e < 4) or
+          // (kq, r, q) reads key row 4kq + r at d = 16t + 4q .. +3, so lane
+          // i receives d = 16t + i of keys 4kq .. 4kq+3: the V^T operand,
+          // with contraction element e <-> key 32u + 4kq + e (e < 4) or
           // 32u + 16 + 4kq + (e - 4), the same keys pb holds.
           const int r4 = (lane & 15) >> 2, q4 = lane & 3;
 #pragma unroll
-          for (int u = 0; u < 2; ++u) {
+          for (int u = 0; u < NK / 2; ++u) {
             const int R0 = 32 * u + 4 * kq + r4;
 #pragma unroll
             for (int t = 0; t < NT; ++t) {
               const int chunk = 2 * t + (q4 >> 1);
               const int boff = (q4 & 1) << 3;
               const short4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                  (lds_s4_t)(vb + slot(R0, chunk) + boff));
+                  (lds_s4_t)(vb + TB + slot(R0, chunk) + boff));
               const short4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                  (lds_s4_t)(vb + slot(R0 + 16, chunk) + boff));
+                  (lds_s4_t)(vb + TB + slot(R0 + 16, chunk) + boff));
               const u32x2_t l2 = __builtin_bit_cast(u32x2_t, lo);
               const u32x2_t h2 = __builtin_bit_cast(u32x2_t, hi);
               const u32x4_t va = {l2[0], l2[1], h2[0], h2[1]};
-              acc[0][t] = Elt<T>::mfma32(va, pb[0][u], acc[0][t]);
-              acc[1][t] = Elt<T>::mfma32(va, pb[1][u], acc[1][t]);
+#pragma unroll
+              for (int rho = 0; rho < NR; ++rho)
+                acc[rho][t] = Elt<T>::mfma32(va, pb[rho][u], acc[rho][t]);
             }
           }
+          // Two V^T operands (4 transposed reads) ahead of the MFMAs.
+          __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 4, 0);
+#pragma unroll
+          for (int r = 0; r < NT * (NK / 2) - 2; ++r) {
+            __builtin_amdgcn_sched_group_barrier(kSchedMfma, NR, 0);
+            __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+          }
+          __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2 * NR, 0);
         }
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();   // next tile landed; everyone is done with this one
+        __builtin_amdgcn_sched_barrier(0);
+        if (i < n && i * BN <= wave_kmax) {
+#pragma unroll
+          for (int kap = 0; kap < NK; ++kap) {
+#pragma unroll
+            for (int rho = 0; rho < NR; ++rho) sacc[kap][rho] = float4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < NS; ++s) {
+              const u32x4_t ka = *reinterpret_cast<const u32x4_t*>(kb + slot(16 * kap + r16, 4 * s + kq));
+#pragma unroll
+              for (int rho = 0; rho < NR; ++rho)
+                sacc[kap][rho] = Elt<T>::mfma32(ka, qreg[rho][s], sacc[kap][rho]);
+            }
+          }
+          // Keep one 16-key group of K operands in flight ahead of the MFMAs
+          // instead of hoisting every read (register pressure).
+          __builtin_amdgcn_sched_group_barrier(kSchedDsRead, NS, 0);
+#pragma unroll
+          for (int r = 0; r < NK - 1; ++r) {
+            __builtin_amdgcn_sched_group_barrier(kSchedMfma, NS * NR, 0);
+            __builtin_amdgcn_sched_group_barrier(kSchedDsRead, NS, 0);
+          }
+          __builtin_amdgcn_sched_group_barrier(kSchedMfma, NS * NR, 0);
+        } else {
+#pragma unroll
+          for (int kap = 0; kap < NK; ++kap)
+#pragma unroll
+            for (int rho = 0; rho < NR; ++rho) sacc[kap][rho] = float4_t{0.f, 0.f, 0.f, 0.f};
+        }
       };
-      for (int kt = 0; kt < kend; kt += 2 * BN) {
-        step(kt, lds0, lds1);
-        if (kt + BN < kend) step(kt + BN, lds1, lds0);
+
+      // Softmax phase of tile j: P_j from S_j, running max / sum, rescale.
+      auto vphase = [&](int j) {
+        if (j < 0 || j >= n || j * BN > wave_kmax) {   // tile above this wave's diagonal
+#pragma unroll
+          for (int rho = 0; rho < NR; ++rho)
+#pragma unroll
+            for (int u = 0; u < NK / 2; ++u) pb[rho][u] = u32x4_t{0, 0, 0, 0};
+          return;
+        }
+        const int kt = j * BN;
+        const bool diag = kt + BN - 1 > wave_kmin;   // some row needs the causal mask here
+#pragma unroll
+        for (int rho = 0; rho < NR; ++rho) {
+          // x = s * c (log2 units); masked keys get -inf.  The running max
+          // m is raised only when a tile max exceeds it by more than
+          // kMaxSlack, so P stays <= 2^kMaxSlack and rescales are rare; the
+          // result is unchanged since numerator and denominator share the
+          // offset.
+          float sv[NK][4];
+          float mt = -INFINITY;
+          if (diag) {
+#pragma unroll
+            for (int kap = 0; kap < NK; ++kap)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                const int key = kt + 16 * kap + 4 * kq + i;
+                sv[kap][i] = key <= limit[rho] ? sacc[kap][rho][i] * c : -INFINITY;
+                mt = fmaxf(mt, sv[kap][i]);
+              }
+          } else if (c >= 0.f) {
+            float hi = -INFINITY;
+#pragma unroll
+            for (int kap = 0; kap < NK; ++kap)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) hi = fmaxf(hi, sacc[kap][rho][i]);
+            mt = hi * c;
+          } else {
+            float lo = INFINITY;
+#pragma unroll
+            for (int kap = 0; kap < NK; ++kap)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) lo = fminf(lo, sacc[kap][rho][i]);
+            mt = lo * c;
+          }
+          mt = max_xor16_32(mt);
+          const bool raise = mt > m[rho] + kMaxSlack || m[rho] == -INFINITY;
+          float alpha = 1.f;
+          if (__any(raise)) {   // rare after the first tile
+            const float m_new = raise ? fmaxf(m[rho], mt) : m[rho];
+            const float base_old = m[rho] == -INFINITY ? 0.f : m[rho];
+            const float base_new = m_new == -INFINITY ? 0.f : m_new;
+            alpha = m[rho] == -INFINITY ? 0.f : exp2_fast(base_old - base_new);
+            m[rho] = m_new;
+#pragma unroll
+            for (int t = 0; t < NT; ++t) acc[rho][t] *= alpha;
+          }
+          const float base_m = m[rho] == -INFINITY ? 0.f : m[rho];
+          if (diag) {
+#pragma unroll
+            for (int kap = 0; kap < NK; ++kap)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) sv[kap][i] = exp2_fast(sv[kap][i] - base_m);
+          } else {
+#pragma unroll
+            for (int kap = 0; kap < NK; ++kap)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) sv[kap][i] = exp2_fast(fmaf(sacc[kap][rho][i], c, -base_m));
+          }
+          // P rounded to the input dtype feeds P.V; the denominator sums
+          // the same rounded values.
+          float psum = 0.f;
+#pragma unroll
+          for (int u = 0; u < NK / 2; ++u) {
+            pb[rho][u] = u32x4_t{Elt<T>::pack2(sv[2 * u][0], sv[2 * u][1]),
+                                 Elt<T>::pack2(sv[2 * u][2], sv[2 * u][3]),
+                                 Elt<T>::pack2(sv[2 * u + 1][0], sv[2 * u + 1][1]),
+                                 Elt<T>::pack2(sv[2 * u + 1][2], sv[2 * u + 1][3])};
+#pragma unroll
+            for (int w = 0; w < 4; ++w) psum = Elt<T>::sum2(pb[rho][u][w], psum);
+          }
+          l[rho] = l[rho] * alpha + psum;
+          __builtin_amdgcn_sched_barrier(0);   // one row group at a time (registers)
+        }
+      };
+
+      // Tick pair i (ticks 2i and 2i+1).  Tick 2i: request tile i+2 (its
+      // block id fetched first so the copies are the newest vector-memory
+      // ops); group A runs M_i, group B runs V_{i-1}.  Tick 2i+1: group A
+      // runs V_i, group B runs M_i; then everything but tile i+2's copies
+      // has landed (so tile i+1 is complete) before the barrier.  Tile t
+      // lives in ring buffer t % 4: tile i+2 overwrites tile i-2, whose V
+      // was last read at tick 2i-1.
+      // Issued at the start of tick 2i by every wave: request tile i+2 and
+      // fetch the block id of tile i+3 (a scalar load, used next tick pair).
+      auto even_service = [&](int i) {
+        if (i + 2 < n) {
+          issue(i + 2, blk_next);
+          blk_next = i + 3 < n ? block_of(i + 3) : 0;
+        }
+      };
+      // Run at the end of tick 2i+1 by every wave, before its barrier: all
+      // copies but tile i+2's have landed, so tile i+1 is complete.
+      auto odd_service = [&](int i) {
+        if (i + 2 < n) wait_vmcnt<2 * LPW>(); else wait_vmcnt<0>();
+      };
+      // Both groups pass the same 2(n+1) barriers; group B runs every phase
+      // one tick after group A.  (Separate loops keep only one of S and P
+      // live across a tick boundary.)
+      if (grp == 0) {
+        for (int i = 0; i <= n; ++i) {
+          even_service(i);
+          mphase(i);
+          __syncthreads();
+          vphase(i);
+          odd_service(i);
+          __syncthreads();
+        }
+      } else {
+        for (int i = 0; i <= n; ++i) {
+          even_service(i);
+          vphase(i - 1);
+          __syncthreads();
+          mphase(i);
+          odd_service(i);
+          __syncthreads();
+        }
       }
 
 #pragma unroll
-      for (int rho = 0; rho < 2; ++rho) {
+      for (int rho = 0; rho < NR; ++rho) {
         const float l_tot = sum_xor16_32(l[rho]);
         if (tok[rho] < 0) continue;
         const float inv = 1.f / l_tot;
@@ -305,13 +443,13 @@ template <typename T>
 static hipError_t prefill_dispatch(const AttnArgs& a, int head_size, int64_t max_blocks, int num_cus,
                                   hipStream_t st) {
   const void* fn = head_size == 128 ? (const void*)&prefill_kernel<T, 128> : (const void*)&prefill_kernel<T, 64>;
-  int64_t grid = resident_blocks(fn, num_cus);
+  int64_t grid = resident_blocks(fn, num_cus, 512);
   if (grid > max_blocks) grid = max_blocks;
   if (grid < 1) grid = 1;
   if (head_size == 128)
-    hipLaunchKernelGGL((prefill_kernel<T, 128>), dim3((unsigned)grid), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((prefill_kernel<T, 128>), dim3((unsigned)grid), dim3(512), 0, st, a);
   else
-    hipLaunchKernelGGL((prefill_kernel<T, 64>), dim3((unsigned)grid), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((prefill_kernel<T, 64>), dim3((unsigned)grid), dim3(512), 0, st, a);
   return hipGetLastError();
 }
 
