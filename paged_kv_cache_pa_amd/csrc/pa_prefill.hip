@@ -24,6 +24,8 @@
 // diagonal, and the output accumulators are rescaled only when a row's
 // running max moves.  Key rows past the visible range are replaced by the
 // last visible row, so NaN in unused cache slots never enters LDS.
+#include <type_traits>
+
 #include "pa_common.hpp"
 #include "pa_internal.hpp"
 
@@ -65,6 +67,16 @@ __device__ inline void lds_dma16(const void* gptr, uint32_t lds_base) {
                :
                : "s"(lds_base), "v"(gptr)
                : "memory", "m0");
+}
+
+// acc *= alpha, updating the same registers, so that the (rare) rescale
+// branch and the fall-through share the accumulator registers instead of
+// the compiler copying all of them on every tile.
+__device__ inline void scale_in_place(float4_t& acc, float alpha) {
+  asm volatile("v_mul_f32 %0, %4, %0\n\tv_mul_f32 %1, %4, %1\n\t"
+               "v_mul_f32 %2, %4, %2\n\tv_mul_f32 %3, %4, %3"
+               : "+v"(acc[0]), "+v"(acc[1]), "+v"(acc[2]), "+v"(acc[3])
+               : "v"(alpha));
 }
 
 // Wait until at most N vector-memory operations of this wave are in flight.
@@ -221,12 +233,9 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(AttnArgs a) {
       wait_vmcnt<0>();
       __syncthreads();
 
-      // Matrix phase of step i: acc += P_{i-1} V_{i-1}, then S = K_i Q^T
-      // (P dies before S is born: fewer live registers).
-      auto mphase = [&](int i) {
-        const unsigned char* kb = lds + (i % NB) * 2 * TB;            // K of tile i
-        const unsigned char* vb = lds + ((i + NB - 1) % NB) * 2 * TB; // V of tile i-1
-        if (i >= 1 && (i - 1) * BN <= wave_kmax) {
+      // acc += P_t V_t with V of tile t (buffer t % 4).
+      auto pv = [&](int t) {
+        const unsigned char* vb = lds + (t % NB) * 2 * TB;
           // O^T tile t covers d = 16t .. 16t+15.  ds_read_b64_tr_b16: within
           // each 16-lane group, result lane i gets element i % 4 of the
           // 8 bytes read by source lanes 4r + i / 4 (r = 0..3).  Source lane
@@ -262,9 +271,10 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(AttnArgs a) {
             __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
           }
           __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2 * NR, 0);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-        if (i < n && i * BN <= wave_kmax) {
+      };
+      // S = K_t Q^T with K of tile t.
+      auto qk = [&](int t) {
+        const unsigned char* kb = lds + (t % NB) * 2 * TB;
 #pragma unroll
           for (int kap = 0; kap < NK; ++kap) {
 #pragma unroll
@@ -286,57 +296,37 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(AttnArgs a) {
             __builtin_amdgcn_sched_group_barrier(kSchedDsRead, NS, 0);
           }
           __builtin_amdgcn_sched_group_barrier(kSchedMfma, NS * NR, 0);
-        } else {
-#pragma unroll
-          for (int kap = 0; kap < NK; ++kap)
-#pragma unroll
-            for (int rho = 0; rho < NR; ++rho) sacc[kap][rho] = float4_t{0.f, 0.f, 0.f, 0.f};
-        }
       };
 
-      // Softmax phase of tile j: P_j from S_j, running max / sum, rescale.
-      auto vphase = [&](int j) {
-        if (j < 0 || j >= n || j * BN > wave_kmax) {   // tile above this wave's diagonal
-#pragma unroll
-          for (int rho = 0; rho < NR; ++rho)
-#pragma unroll
-            for (int u = 0; u < NK / 2; ++u) pb[rho][u] = u32x4_t{0, 0, 0, 0};
-          return;
-        }
+      // Softmax of tile j into P (pb), running max / sum and rescale.
+      // kMasked: apply the causal mask (tiles crossing a row's diagonal, and
+      // every tile when scale <= 0); otherwise all 64 keys are visible to
+      // every row of the wave and scale > 0.
+      auto softmax = [&](int j, auto masked_tag) {
+        constexpr bool kMasked = decltype(masked_tag)::value;
         const int kt = j * BN;
-        const bool diag = kt + BN - 1 > wave_kmin;   // some row needs the causal mask here
 #pragma unroll
         for (int rho = 0; rho < NR; ++rho) {
-          // x = s * c (log2 units); masked keys get -inf.  The running max
-          // m is raised only when a tile max exceeds it by more than
-          // kMaxSlack, so P stays <= 2^kMaxSlack and rescales are rare; the
-          // result is unchanged since numerator and denominator share the
-          // offset.
-          float sv[NK][4];
+          // The running max m is raised only when a tile max exceeds it by
+          // more than kMaxSlack, so P stays <= 2^kMaxSlack and rescales are
+          // rare; the result is unchanged since numerator and denominator
+          // share the offset.
           float mt = -INFINITY;
-          if (diag) {
+          if constexpr (kMasked) {
 #pragma unroll
             for (int kap = 0; kap < NK; ++kap)
 #pragma unroll
               for (int i = 0; i < 4; ++i) {
                 const int key = kt + 16 * kap + 4 * kq + i;
-                sv[kap][i] = key <= limit[rho] ? sacc[kap][rho][i] * c : -INFINITY;
-                mt = fmaxf(mt, sv[kap][i]);
+                sacc[kap][rho][i] = key <= limit[rho] ? sacc[kap][rho][i] * c : -INFINITY;
+                mt = fmaxf(mt, sacc[kap][rho][i]);
               }
-          } else if (c >= 0.f) {
-            float hi = -INFINITY;
-#pragma unroll
-            for (int kap = 0; kap < NK; ++kap)
-#pragma unroll
-              for (int i = 0; i < 4; ++i) hi = fmaxf(hi, sacc[kap][rho][i]);
-            mt = hi * c;
           } else {
-            float lo = INFINITY;
 #pragma unroll
             for (int kap = 0; kap < NK; ++kap)
 #pragma unroll
-              for (int i = 0; i < 4; ++i) lo = fminf(lo, sacc[kap][rho][i]);
-            mt = lo * c;
+              for (int i = 0; i < 4; ++i) mt = fmaxf(mt, sacc[kap][rho][i]);
+            mt *= c;
           }
           mt = max_xor16_32(mt);
           const bool raise = mt > m[rho] + kMaxSlack || m[rho] == -INFINITY;
@@ -348,20 +338,16 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(AttnArgs a) {
             alpha = m[rho] == -INFINITY ? 0.f : exp2_fast(base_old - base_new);
             m[rho] = m_new;
 #pragma unroll
-            for (int t = 0; t < NT; ++t) acc[rho][t] *= alpha;
+            for (int t = 0; t < NT; ++t) scale_in_place(acc[rho][t], alpha);
           }
           const float base_m = m[rho] == -INFINITY ? 0.f : m[rho];
-          if (diag) {
+          float sv[NK][4];
 #pragma unroll
-            for (int kap = 0; kap < NK; ++kap)
+          for (int kap = 0; kap < NK; ++kap)
 #pragma unroll
-              for (int i = 0; i < 4; ++i) sv[kap][i] = exp2_fast(sv[kap][i] - base_m);
-          } else {
-#pragma unroll
-            for (int kap = 0; kap < NK; ++kap)
-#pragma unroll
-              for (int i = 0; i < 4; ++i) sv[kap][i] = exp2_fast(fmaf(sacc[kap][rho][i], c, -base_m));
-          }
+            for (int i = 0; i < 4; ++i)
+              sv[kap][i] = kMasked ? exp2_fast(sacc[kap][rho][i] - base_m)
+                                   : exp2_fast(fmaf(sacc[kap][rho][i], c, -base_m));
           // P rounded to the input dtype feeds P.V; the denominator sums
           // the same rounded values.
           float psum = 0.f;
@@ -378,14 +364,14 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(AttnArgs a) {
           __builtin_amdgcn_sched_barrier(0);   // one row group at a time (registers)
         }
       };
+      using Plain = std::integral_constant<bool, false>;
+      using Masked = std::integral_constant<bool, true>;
 
-      // Tick pair i (ticks 2i and 2i+1).  Tick 2i: request tile i+2 (its
-      // block id fetched first so the copies are the newest vector-memory
-      // ops); group A runs M_i, group B runs V_{i-1}.  Tick 2i+1: group A
-      // runs V_i, group B runs M_i; then everything but tile i+2's copies
-      // has landed (so tile i+1 is complete) before the barrier.  Tile t
-      // lives in ring buffer t % 4: tile i+2 overwrites tile i-2, whose V
-      // was last read at tick 2i-1.
+      // Tiles this wave computes: 0 .. nw-1 (later ones lie wholly above
+      // all its rows' diagonals); of those, tiles 0 .. nd-1 need no mask.
+      const int nw = wave_kmax < 0 ? 0 : min(n, wave_kmax / BN + 1);
+      const int nd = c > 0.f ? min(nw, (wave_kmin + 1) / BN) : 0;
+
       // Issued at the start of tick 2i by every wave: request tile i+2 and
       // fetch the block id of tile i+3 (a scalar load, used next tick pair).
       auto even_service = [&](int i) {
@@ -399,24 +385,68 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(AttnArgs a) {
       auto odd_service = [&](int i) {
         if (i + 2 < n) wait_vmcnt<2 * LPW>(); else wait_vmcnt<0>();
       };
-      // Both groups pass the same 2(n+1) barriers; group B runs every phase
-      // one tick after group A.  (Separate loops keep only one of S and P
-      // live across a tick boundary.)
+
+      // Tick pair i (ticks 2i and 2i+1): tick 2i requests tile i+2; tick
+      // 2i+1 ends with tile i+1 complete.  Tile t lives in ring buffer t % 4:
+      // tile i+2 overwrites tile i-2, whose V was last read at tick 2i-1.
+      // Group A runs M_i = {P.V of tile i-1, QK^T of tile i} at tick 2i and
+      // the softmax V_i at tick 2i+1; group B runs V_{i-1} at tick 2i and
+      // M_i at tick 2i+1.  Both pass the same 2(n+1) barriers; the loops are
+      // split where a wave's tiles change kind so each body is straight-line.
       if (grp == 0) {
-        for (int i = 0; i <= n; ++i) {
+        int i = 0;
+        for (; i < nd; ++i) {
           even_service(i);
-          mphase(i);
+          if (i > 0) pv(i - 1);
+          __builtin_amdgcn_sched_barrier(0);
+          qk(i);
           __syncthreads();
-          vphase(i);
+          softmax(i, Plain{});
+          odd_service(i);
+          __syncthreads();
+        }
+        for (; i < nw; ++i) {
+          even_service(i);
+          if (i > 0) pv(i - 1);
+          __builtin_amdgcn_sched_barrier(0);
+          qk(i);
+          __syncthreads();
+          softmax(i, Masked{});
+          odd_service(i);
+          __syncthreads();
+        }
+        for (; i <= n; ++i) {
+          even_service(i);
+          if (i == nw && i > 0) pv(i - 1);
+          __syncthreads();
           odd_service(i);
           __syncthreads();
         }
       } else {
-        for (int i = 0; i <= n; ++i) {
+        int i = 0;
+        for (; i <= nd; ++i) {   // V_{i-1} plain (if any), then M_i
           even_service(i);
-          vphase(i - 1);
+          if (i > 0) softmax(i - 1, Plain{});
           __syncthreads();
-          mphase(i);
+          if (i > 0) pv(i - 1);
+          __builtin_amdgcn_sched_barrier(0);
+          if (i < nw) qk(i);
+          odd_service(i);
+          __syncthreads();
+        }
+        for (; i <= nw; ++i) {   // V_{i-1} masked, then M_i
+          even_service(i);
+          softmax(i - 1, Masked{});
+          __syncthreads();
+          pv(i - 1);
+          __builtin_amdgcn_sched_barrier(0);
+          if (i < nw) qk(i);
+          odd_service(i);
+          __syncthreads();
+        }
+        for (; i <= n; ++i) {
+          even_service(i);
+          __syncthreads();
           odd_service(i);
           __syncthreads();
         }
