@@ -91,17 +91,34 @@ __device__ inline uint32_t pair_elem(uint32_t xw, uint32_t yw, bool hi) {
   return hi ? __builtin_amdgcn_perm(yw, xw, 0x07060302u) : __builtin_amdgcn_perm(yw, xw, 0x05040100u);
 }
 
-__device__ inline float wave_max_xor16_32(float v) {
-  v = fmaxf(v, __shfl_xor(v, 16));
-  v = fmaxf(v, __shfl_xor(v, 32));
-  return v;
+// A row's running max is raised only when a tile's (chunk's) max exceeds it by more
+// than this many powers of two (bounds P by 2^8: safe in fp16 and bf16).
+constexpr float kMaxSlack = 8.f;
+
+// xor-16 / xor-32 lane exchanges as VALU permutes (no LDS round trip).
+__device__ inline float max_xor16_32(float v) {
+  auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ inline float sum_xor16_32(float v) {
+  auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
-__device__ inline float wave_sum_xor16_32(float v) {
-  v += __shfl_xor(v, 16);
-  v += __shfl_xor(v, 32);
-  return v;
+// acc *= alpha, updating the same registers, so that the (rare) rescale
+// branch and the fall-through share the accumulator registers instead of
+// the compiler copying all of them on every tile.
+__device__ inline void scale_in_place(float4_t& acc, float alpha) {
+  asm volatile("v_mul_f32 %0, %4, %0\n\tv_mul_f32 %1, %4, %1\n\t"
+               "v_mul_f32 %2, %4, %2\n\tv_mul_f32 %3, %4, %3"
+               : "+v"(acc[0]), "+v"(acc[1]), "+v"(acc[2]), "+v"(acc[3])
+               : "v"(alpha));
 }
+
 
 __device__ inline u32x4_t ld16(const void* p) { return *reinterpret_cast<const u32x4_t*>(p); }
 __device__ inline u32x2_t ld8(const void* p) { return *reinterpret_cast<const u32x2_t*>(p); }

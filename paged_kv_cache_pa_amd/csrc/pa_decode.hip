@@ -96,34 +96,36 @@ __global__ __launch_bounds__(256) void decode_kernel(AttnArgs a) {
 #pragma unroll
     for (int t = 0; t < NT; ++t) acc[t] = float4_t{0.f, 0.f, 0.f, 0.f};
 
-    for (int c0 = k0; c0 < k1; c0 += 16) {
+    // K/V registers of one 16-key chunk.
+    struct Chunk {
+      u32x4_t k[NS];
+      uint32_t v[4][NT / 2];
+    };
+    auto load = [&](int c0, Chunk& ch) {
       const int blk = __builtin_amdgcn_readlane(my_blk, (c0 >> a.block_shift) - blk0);
       const int64_t base =
           ((int64_t)blk * a.block_size + (c0 & (a.block_size - 1))) * row_stride + (int64_t)kh * D;
-      u32x4_t kreg[NS];
       const uint16_t* krow = kc + base + r16 * row_stride;
 #pragma unroll
-      for (int s = 0; s < NS; ++s) kreg[s] = ld16(krow + (4 * s + kq) * 8);
-      uint32_t vreg[4][NT / 2];
+      for (int s = 0; s < NS; ++s) ch.k[s] = ld16(krow + (4 * s + kq) * 8);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const uint16_t* vrow = vc + base + (4 * kq + e) * row_stride + r16 * NT;
-        const bool live = c0 + 4 * kq + e < k1;   // rows past L may hold NaN
         if constexpr (NT == 8) {
-          u32x4_t x = ld16(vrow);
+          const u32x4_t x = ld16(vrow);
 #pragma unroll
-          for (int w = 0; w < 4; ++w) vreg[e][w] = live ? x[w] : 0u;
+          for (int w = 0; w < 4; ++w) ch.v[e][w] = x[w];
         } else {
-          u32x2_t x = ld8(vrow);
+          const u32x2_t x = ld8(vrow);
 #pragma unroll
-          for (int w = 0; w < 2; ++w) vreg[e][w] = live ? x[w] : 0u;
+          for (int w = 0; w < 2; ++w) ch.v[e][w] = x[w];
         }
       }
-
+    };
+    auto compute = [&](int c0, const Chunk& ch) {
       float4_t sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int s = 0; s < NS; ++s) sc = Elt<T>::mfma32(kreg[s], qreg[s], sc);
-
+      for (int s = 0; s < NS; ++s) sc = Elt<T>::mfma32(ch.k[s], qreg[s], sc);
       float sv[4];
       float cmax = -INFINITY;
 #pragma unroll
@@ -133,27 +135,60 @@ __global__ __launch_bounds__(256) void decode_kernel(AttnArgs a) {
         sv[i] = vis ? sc[i] * a.scale_log2 : -INFINITY;
         cmax = fmaxf(cmax, sv[i]);
       }
-      cmax = wave_max_xor16_32(cmax);
-      const float m_new = fmaxf(m, cmax);
-      const float base_m = m_new == -INFINITY ? 0.f : m_new;
-      const float alpha = exp2_fast(m - base_m);
+      cmax = max_xor16_32(cmax);
+      // Raise the running max only when this chunk exceeds it by more than
+      // kMaxSlack (P stays <= 2^kMaxSlack), so the accumulators are rescaled
+      // rarely; numerator and denominator share the offset.
+      const bool raise = cmax > m + kMaxSlack || m == -INFINITY;
+      if (__any(raise)) {
+        const float m_new = raise ? fmaxf(m, cmax) : m;
+        const float base_new = m_new == -INFINITY ? 0.f : m_new;
+        const float alpha = m == -INFINITY ? 0.f : exp2_fast(m - base_new);
+        m = m_new;
+        l *= alpha;
+#pragma unroll
+        for (int t = 0; t < NT; ++t) scale_in_place(acc[t], alpha);
+      }
+      const float base_m = m == -INFINITY ? 0.f : m;
       float p[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) p[i] = exp2_fast(sv[i] - base_m);
       // P enters P.V rounded to the input dtype; the denominator sums the
       // same rounded values so the weights of each column sum to one.
       const u32x2_t pb = {Elt<T>::pack2(p[0], p[1]), Elt<T>::pack2(p[2], p[3])};
-      l = l * alpha + Elt<T>::sum2(pb[1], Elt<T>::sum2(pb[0], 0.f));
-      m = m_new;
+      l += Elt<T>::sum2(pb[1], Elt<T>::sum2(pb[0], 0.f));
+      // Value rows at or past the split end may be unused slots (NaN).
+      uint32_t vz[4][NT / 2];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const bool live = c0 + 4 * kq + e < k1;
+#pragma unroll
+        for (int w = 0; w < NT / 2; ++w) vz[e][w] = live ? ch.v[e][w] : 0u;
+      }
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
-        const uint32_t w0 = pair_elem(vreg[0][t >> 1], vreg[1][t >> 1], t & 1);
-        const uint32_t w1 = pair_elem(vreg[2][t >> 1], vreg[3][t >> 1], t & 1);
-        acc[t] = Elt<T>::mfma16(u32x2_t{w0, w1}, pb, acc[t] * alpha);
+        const uint32_t w0 = pair_elem(vz[0][t >> 1], vz[1][t >> 1], t & 1);
+        const uint32_t w1 = pair_elem(vz[2][t >> 1], vz[3][t >> 1], t & 1);
+        acc[t] = Elt<T>::mfma16(u32x2_t{w0, w1}, pb, acc[t]);
       }
+    };
+
+    // Software pipeline: the loads of chunk c+1 are in flight while chunk c
+    // is computed (two register sets, unrolled by two).
+    Chunk ca, cb;
+    load(k0, ca);
+    for (int c0 = k0;;) {
+      if (c0 + 16 < k1) load(c0 + 16, cb);
+      compute(c0, ca);
+      c0 += 16;
+      if (c0 >= k1) break;
+      if (c0 + 16 < k1) load(c0 + 16, ca);
+      compute(c0, cb);
+      c0 += 16;
+      if (c0 >= k1) break;
     }
 
-    const float l_tot = wave_sum_xor16_32(l);
+    const float l_tot = sum_xor16_32(l);
     const int n = r16;
     if (n >= ncols) {
       // padding column: nothing to store

@@ -39,24 +39,6 @@ typedef __attribute__((address_space(4))) int32_t const_i32_t;
 constexpr int kSchedMfma = 0x008;
 constexpr int kSchedDsRead = 0x100;
 
-// A row's running max is raised only when a tile's max exceeds it by more
-// than this many powers of two (bounds P by 2^8: safe in fp16 and bf16).
-constexpr float kMaxSlack = 8.f;
-
-// xor-16 / xor-32 lane exchanges as VALU permutes (no LDS round trip).
-__device__ inline float max_xor16_32(float v) {
-  auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
-  auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
-}
-__device__ inline float sum_xor16_32(float v) {
-  auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-  auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
-}
-
 // 16-byte-per-lane copy global -> LDS (global_load_lds_dwordx4): lane l's
 // 16 bytes land at LDS byte lds_base + 16 * l.  Issued from inline asm so
 // that the compiler does not treat later LDS reads of *other* ring buffers
@@ -67,16 +49,6 @@ __device__ inline void lds_dma16(const void* gptr, uint32_t lds_base) {
                :
                : "s"(lds_base), "v"(gptr)
                : "memory", "m0");
-}
-
-// acc *= alpha, updating the same registers, so that the (rare) rescale
-// branch and the fall-through share the accumulator registers instead of
-// the compiler copying all of them on every tile.
-__device__ inline void scale_in_place(float4_t& acc, float alpha) {
-  asm volatile("v_mul_f32 %0, %4, %0\n\tv_mul_f32 %1, %4, %1\n\t"
-               "v_mul_f32 %2, %4, %2\n\tv_mul_f32 %3, %4, %3"
-               : "+v"(acc[0]), "+v"(acc[1]), "+v"(acc[2]), "+v"(acc[3])
-               : "v"(alpha));
 }
 
 // Wait until at most N vector-memory operations of this wave are in flight.
@@ -147,6 +119,7 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(AttnArgs a) {
     const int x = (home + qi) % kQueues;
     const int qlen = a.counters[kQueueLen + x];
     const int qstart = a.counters[kQueueStart + x];
+    if (qlen == 0) continue;   // no atomics or barriers on empty queues
     for (;;) {
       if (tid == 0) item_sh = atomicAdd(a.counters_rw + kCtrPrefill + x, 1);
       __syncthreads();
