@@ -117,8 +117,9 @@ pa_status_t check_shape(const pa::Shape& s) {
   if (!is_pow2(s.block_size) || s.block_size < 16 || s.block_size > 1024)
     return fail(PA_ERR_NOT_IMPLEMENTED, "block_size=%d (supported: powers of two in [16, 1024])",
                 s.block_size);
-  if ((int64_t)s.max_blocks_per_seq * s.block_size > INT32_MAX)
-    return fail(PA_ERR_NOT_IMPLEMENTED, "max_blocks_per_seq * block_size exceeds INT32_MAX");
+  if ((int64_t)s.max_blocks_per_seq * s.block_size > (int64_t)pa::kSplitKeys * pa::kMaxSplitsCombine)
+    return fail(PA_ERR_NOT_IMPLEMENTED, "max_blocks_per_seq * block_size exceeds %d tokens",
+                pa::kSplitKeys * pa::kMaxSplitsCombine);
   return PA_OK;
 }
 

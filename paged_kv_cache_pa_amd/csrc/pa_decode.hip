@@ -229,9 +229,16 @@ __global__ __launch_bounds__(256) void decode_kernel(AttnArgs a) {
 }
 
 // One work-group per (sequence, KV head); a no-op unless the sequence took
-// the decode path with more than one split.
+// the decode path with more than one split.  The per-split weights
+// w_s = 2^(m_s - M) of each column are computed once into LDS together with
+// 1 / sum_s w_s l_s; then each thread produces 4 consecutive outputs of one
+// column from 16-byte partial loads, with the splits unrolled so several
+// loads are in flight.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void combine_kernel(AttnArgs a) {
+  constexpr int MAXS = kMaxSplitsCombine;
+  __shared__ float wts[kDecodeCols][MAXS];
+  __shared__ float inv_den[kDecodeCols];
   const int b = blockIdx.x, kh = blockIdx.y;
   const SeqInfo si = a.seqinfo[b];
   const int G = a.group;
@@ -239,28 +246,46 @@ __global__ __launch_bounds__(256) void combine_kernel(AttnArgs a) {
   if (si.q_len <= 0 || ncols > kDecodeCols) return;
   const int nsplit = (si.kv_len + kSplitKeys - 1) / kSplitKeys;
   if (nsplit <= 1) return;
-  uint16_t* __restrict__ op = (uint16_t*)a.out;
-  for (int idx = threadIdx.x; idx < ncols * (D / 2); idx += blockDim.x) {
-    const int n = idx / (D / 2);
-    const int d = (idx - n * (D / 2)) * 2;
-    const int64_t row0 = (int64_t)si.pbase + (int64_t)kh * nsplit * ncols + n;
+  const int64_t row0 = (int64_t)si.pbase + (int64_t)kh * nsplit * ncols;
+  // Column n's weights: one 16-lane group of a wave per column.
+  for (int n = threadIdx.x >> 4; n < ncols; n += blockDim.x >> 4) {
+    const int lane16 = threadIdx.x & 15;
     float M = -INFINITY;
-    for (int s = 0; s < nsplit; ++s) M = fmaxf(M, a.part_ml[row0 + (int64_t)s * ncols].x);
-    float num0 = 0.f, num1 = 0.f, den = 0.f;
-    for (int s = 0; s < nsplit; ++s) {
-      const int64_t row = row0 + (int64_t)s * ncols;
-      const float2 ml = a.part_ml[row];
-      const float f = ml.x == -INFINITY ? 0.f : exp2_fast(ml.x - M);
-      const float2 v = *reinterpret_cast<const float2*>(a.part_acc + row * D + d);
-      num0 += f * v.x;
-      num1 += f * v.y;
-      den += f * ml.y;
+    for (int s = lane16; s < nsplit; s += 16) M = fmaxf(M, a.part_ml[row0 + (int64_t)s * ncols + n].x);
+#pragma unroll
+    for (int o = 8; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 16));
+    float den = 0.f;
+    for (int s = lane16; s < nsplit; s += 16) {
+      const float2 ml = a.part_ml[row0 + (int64_t)s * ncols + n];
+      const float w = ml.x == -INFINITY ? 0.f : exp2_fast(ml.x - M);
+      if (s < MAXS) wts[n][s] = w;
+      den += w * ml.y;
     }
-    const float inv = 1.f / den;
+#pragma unroll
+    for (int o = 8; o >= 1; o >>= 1) den += __shfl_xor(den, o, 16);
+    if (lane16 == 0) inv_den[n] = 1.f / den;
+  }
+  __syncthreads();
+  uint16_t* __restrict__ op = (uint16_t*)a.out;
+  for (int idx = threadIdx.x; idx < ncols * (D / 4); idx += blockDim.x) {
+    const int n = idx / (D / 4);
+    const int d = (idx - n * (D / 4)) * 4;
+    const float* src = a.part_acc + (row0 + n) * D + d;
+    const int64_t step = (int64_t)ncols * D;
+    float4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+    int s = 0;
+    for (; s + 1 < nsplit; s += 2) {
+      const float4_t v0 = *reinterpret_cast<const float4_t*>(src + s * step);
+      const float4_t v1 = *reinterpret_cast<const float4_t*>(src + (s + 1) * step);
+      acc0 += wts[n][s] * v0;
+      acc1 += wts[n][s + 1] * v1;
+    }
+    if (s < nsplit) acc0 += wts[n][s] * *reinterpret_cast<const float4_t*>(src + s * step);
+    const float4_t o = (acc0 + acc1) * inv_den[n];
     const int tok = si.cu + n / G;
     const int h = kh * G + n % G;
-    *reinterpret_cast<uint32_t*>(op + ((int64_t)tok * a.num_heads + h) * D + d) =
-        Elt<T>::pack2(num0 * inv, num1 * inv);
+    *reinterpret_cast<u32x2_t*>(op + ((int64_t)tok * a.num_heads + h) * D + d) =
+        u32x2_t{Elt<T>::pack2(o[0], o[1]), Elt<T>::pack2(o[2], o[3])};
   }
 }
 

@@ -13,6 +13,9 @@ namespace pa {
 // nothing but this constant, so a sequence's output never depends on its
 // batch-mates.
 constexpr int kSplitKeys = 512;
+// Largest split count per sequence (the block table row bounds the context:
+// max_blocks_per_seq * block_size <= kSplitKeys * kMaxSplitsCombine).
+constexpr int kMaxSplitsCombine = 256;
 // A sequence takes the decode path when q_len * G columns fit one 16-wide
 // matrix-core tile.
 constexpr int kDecodeCols = 16;
