@@ -114,13 +114,13 @@ def time_workload(wl, steps, warmup, torch, pa, W):
 
 
 def summarize(wl, ms, per_kernel):
-    """Throughputs of one step and of its decode / prefill kernels."""
+    """Throughputs of one step and of its attention kernel (the one launch
+    that runs both the prefill tiles and the split-KV decode items)."""
     att_bytes, att_flops = attention_work(wl)
     nbytes = att_bytes + scatter_work(wl)
     t = ms * 1e-3
-    dec_sel = wl.q_lens * (wl.num_heads // wl.num_kv_heads) <= 16
-    dec_bytes, dec_flops = attention_work(wl, dec_sel & (wl.q_lens > 0))
-    pf_bytes, pf_flops = attention_work(wl, ~dec_sel)
+    dec_sel = (wl.q_lens * (wl.num_heads // wl.num_kv_heads) <= 16) & (wl.q_lens > 0)
+    pf_sel = wl.q_lens * (wl.num_heads // wl.num_kv_heads) > 16
     r = {
         "ms_per_step": ms,
         "roofline_pct": 100.0 * roofline_time(nbytes, att_flops) / t,
@@ -129,14 +129,20 @@ def summarize(wl, ms, per_kernel):
         "alg_flops": att_flops,
         "kernel_ms": {k: round(v, 5) for k, v in per_kernel.items()},
     }
-    if dec_bytes and per_kernel.get("decode"):
-        r["decode_TBps"] = dec_bytes / (per_kernel["decode"] * 1e-3) / 1e12
-        r["decode_hbm_frac"] = r["decode_TBps"] * 1e12 / HBM_PEAK
-        r["decode_alg_bytes"] = dec_bytes
-    if pf_flops and per_kernel.get("prefill"):
-        r["prefill_TFLOPs"] = pf_flops / (per_kernel["prefill"] * 1e-3) / 1e12
-        r["prefill_mfma_frac"] = r["prefill_TFLOPs"] * 1e12 / MFMA_PEAK
-        r["prefill_alg_flops"] = pf_flops
+    ta = per_kernel.get("attention", 0.0) * 1e-3
+    if ta > 0:
+        r["attention_alg_bytes"] = att_bytes
+        r["attention_alg_flops"] = att_flops
+        r["attention_TBps"] = att_bytes / ta / 1e12
+        r["attention_TFLOPs"] = att_flops / ta / 1e12
+        r["attention_roofline_frac"] = roofline_time(att_bytes, att_flops) / ta
+        r["attention_bound"] = "hbm" if att_bytes / HBM_PEAK >= att_flops / MFMA_PEAK else "mfma"
+        if not pf_sel.any():       # decode only: the kernel's bytes are the decode bytes
+            r["decode_TBps"] = r["attention_TBps"]
+            r["decode_hbm_frac"] = r["decode_TBps"] * 1e12 / HBM_PEAK
+        if not dec_sel.any():      # prefill only
+            r["prefill_TFLOPs"] = r["attention_TFLOPs"]
+            r["prefill_mfma_frac"] = r["prefill_TFLOPs"] * 1e12 / MFMA_PEAK
     return r
 
 
@@ -268,19 +274,17 @@ def main():
     wl = W.by_index(WORKLOADS[args.workload])
     ms, wall_ms, per_kernel = time_workload(wl, args.steps, args.warmup, torch, pa, W)
     head = summarize(wl, ms, per_kernel)
-    dominant = max(("decode", "prefill"), key=lambda k: per_kernel.get(k, 0.0))
-    if dominant == "decode":
-        ach = head.get("decode_TBps", 0.0) * 1e3
-        roof = {"bound": "hbm", "kernel": "decode_kernel", "achieved": ach, "peak": 8000.0,
-                "unit": "GB/s", "frac": ach / 8000.0,
-                "avg_launch_ms": per_kernel.get("decode", 0.0),
-                "alg_bytes_per_launch": head.get("decode_alg_bytes")}
-    else:
-        ach = head.get("prefill_TFLOPs", 0.0)
-        roof = {"bound": "mfma", "kernel": "prefill_kernel", "achieved": ach, "peak": 2500.0,
+    if head.get("attention_bound") == "mfma":
+        ach = head["attention_TFLOPs"]
+        roof = {"bound": "mfma", "kernel": "attention_kernel", "achieved": ach, "peak": 2500.0,
                 "unit": "TFLOP/s", "frac": ach / 2500.0,
-                "avg_launch_ms": per_kernel.get("prefill", 0.0),
-                "alg_flops_per_launch": head.get("prefill_alg_flops")}
+                "alg_flops_per_launch": head["attention_alg_flops"]}
+    else:
+        ach = head.get("attention_TBps", 0.0) * 1e3
+        roof = {"bound": "hbm", "kernel": "attention_kernel", "achieved": ach, "peak": 8000.0,
+                "unit": "GB/s", "frac": ach / 8000.0,
+                "alg_bytes_per_launch": head.get("attention_alg_bytes")}
+    roof["avg_launch_ms"] = per_kernel.get("attention", 0.0)
     roof["traffic"] = measured_traffic(roof["kernel"], args.workload)
 
     extra = {}
@@ -303,8 +307,11 @@ def main():
                    "step": "pa_scatter_kv(new tokens) + pa_attention(whole batch)",
                    "parallelism": "single GPU"},
         "tokens_per_s": head["tokens_per_s"],
-        "decode_TBps": head.get("decode_TBps"),
-        "prefill_TFLOPs": head.get("prefill_TFLOPs"),
+        "attention_TBps": head.get("attention_TBps"),
+        "attention_TFLOPs": head.get("attention_TFLOPs"),
+        "decode_TBps": head.get("decode_TBps") or extra.get("decode", {}).get("decode_TBps"),
+        "prefill_TFLOPs": (head.get("prefill_TFLOPs")
+                           or extra.get("prefill", {}).get("prefill_TFLOPs")),
         "kernel_ms": head["kernel_ms"],
         "copy_GBps": copy_gbps,
         "roofline": roof,

@@ -191,10 +191,11 @@ const char* pa_last_error(void);
  * pa_attention bracket each kernel launch with a pair of HIP events on the
  * caller's stream.  pa_profile_read waits for the recorded events and
  * returns, per kernel kind, the summed milliseconds and launch counts
- * (host arrays of n entries; kinds: 0 scatter, 1 plan, 2 prefill,
- * 3 decode, 4 combine), then forgets them.  Not for concurrent use.
+ * (host arrays of n entries; kinds: 0 scatter, 1 plan, 2 attention (the
+ * one launch that runs prefill tiles and split-KV decode items), 3 split-KV
+ * combine), then forgets them.  Not for concurrent use.
  */
-#define PA_PROFILE_KINDS 5
+#define PA_PROFILE_KINDS 4
 pa_status_t pa_profile_enable(int32_t enable);
 pa_status_t pa_profile_read(double* ms, int64_t* launches, int32_t n);
 

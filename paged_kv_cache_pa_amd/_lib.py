@@ -19,7 +19,7 @@ PA_ERR_WORKSPACE_TOO_SMALL = 3
 PA_ERR_HIP = 4
 PA_F16 = 0
 PA_BF16 = 1
-PROFILE_KINDS = ("scatter", "plan", "prefill", "decode", "combine")
+PROFILE_KINDS = ("scatter", "plan", "attention", "combine")
 
 EXPORTS = ("pa_scatter_kv", "pa_attention_workspace_size", "pa_attention",
            "pa_validate_metadata", "pa_status_string", "pa_last_error",

@@ -265,6 +265,12 @@ pa_status_t pa_attention(const void* q, const int32_t* cu_seqlens_q, const int32
   pl.group = G;
   pl.num_kv_heads = num_kv_heads;
   pl.tokens_per_tile = tq;
+  // Persistent grid: what the device holds at once, but no more groups than
+  // there are prefill items plus groups of 8 decode waves.
+  const int64_t max_groups = L.max_pf_items + (L.max_dec_pairs * num_kv_heads + 7) / 8;
+  const int workers = (int)std::max<int64_t>(
+      1, std::min<int64_t>(pa::attention_workers(dtype, head_size, cus), max_groups));
+  pl.num_workers = workers;
   hipError_t e = timed(1, st, [&] { return pa::launch_plan(pl, st); });
   if (e != hipSuccess) return hip_fail(e, "plan launch");
 
@@ -290,22 +296,12 @@ pa_status_t pa_attention(const void* q, const int32_t* cu_seqlens_q, const int32
   a.block_shift = log2i(block_size);
   a.tokens_per_tile = tq;
   a.scale_log2 = scale * pa::kLog2e;
+  a.inv_group = 1.0f / (float)G;
 
-  // Prefill first: its tiles are the long poles; decode streams behind it.
-  const bool any_prefill = (int64_t)num_tokens * G > pa::kDecodeCols;
-  if (any_prefill) {
-    e = timed(2, st, [&] {
-      return pa::launch_prefill(a, dtype, head_size, L.max_pf_items, cus, st);
-    });
-    if (e != hipSuccess) return hip_fail(e, "prefill launch");
-  }
-  const int64_t dec_waves = L.max_dec_pairs * num_kv_heads;
-  e = timed(3, st, [&] {
-    return pa::launch_decode(a, dtype, head_size, (dec_waves + 3) / 4, cus, st);
-  });
-  if (e != hipSuccess) return hip_fail(e, "decode launch");
+  e = timed(2, st, [&] { return pa::launch_attention(a, dtype, head_size, workers, st); });
+  if (e != hipSuccess) return hip_fail(e, "attention launch");
   if (L.max_part_rows > 0) {
-    e = timed(4, st, [&] { return pa::launch_combine(a, dtype, head_size, st); });
+    e = timed(3, st, [&] { return pa::launch_combine(a, dtype, head_size, st); });
     if (e != hipSuccess) return hip_fail(e, "combine launch");
   }
   return PA_OK;

@@ -1,0 +1,80 @@
+// The attention kernel: one persistent launch that runs both kinds of work
+// item the plan produced, prefill tiles (matrix-core bound) and split-KV
+// decode items (HBM bound), plus the split-KV combine.
+//
+// Sources: "[WebGPU] Initial PagedAttention implementation (1/n)" -
+// "Description" (one attention pass over a continuous batch that mixes
+// prefill chunks and decode tokens) and "Roadmap" (phase 2: page-aware
+// prefill and decode kernels reading K/V through the block table).
+//
+// Run back to back, the two kinds of work leave one MI355X resource idle in
+// turn: prefill keeps the matrix cores busy while HBM idles, decode streams
+// HBM while the matrix cores idle, and one CU streams only ~40 GB/s, so
+// decode needs many CUs for full bandwidth.  Here each work-group (8 waves,
+// one per CU) takes a role at start: the first counters[kPrefillFirst]
+// groups (spread over the XCDs by the round-robin dispatch) run prefill
+// items and the rest run decode items, both at once; a group whose queue
+// runs dry moves to the other kind, so the tail balances itself.  The plan
+// kernel sizes the split so that both halves finish together under the cost
+// model kPrefillStepCost.
+#include "pa_decode.hpp"
+#include "pa_prefill.hpp"
+
+namespace pa {
+
+template <typename T, int D>
+__global__ __launch_bounds__(512, 1) void attention_kernel(AttnArgs a) {
+  const bool prefill_first = (int)blockIdx.x < a.counters[kPrefillFirst];
+  // Straight-line phases (no loop around them, so nothing of one body is
+  // hoisted to stay live across the other); the small decode body appears
+  // twice, the large prefill body once.
+  if (!prefill_first) decode_items<T, D>(a);
+  prefill_items<T, D>(a);
+  if (prefill_first) decode_items<T, D>(a);
+}
+
+template <typename T, int D>
+static const void* attention_fn() {
+  return (const void*)&attention_kernel<T, D>;
+}
+
+static const void* attention_fn(int dtype, int head_size) {
+  if (dtype == 0) return head_size == 128 ? attention_fn<F16, 128>() : attention_fn<F16, 64>();
+  return head_size == 128 ? attention_fn<BF16, 128>() : attention_fn<BF16, 64>();
+}
+
+int attention_workers(int dtype, int head_size, int num_cus) {
+  return resident_blocks(attention_fn(dtype, head_size), num_cus, 512);
+}
+
+template <typename T>
+static hipError_t attention_dispatch(const AttnArgs& a, int head_size, int grid, hipStream_t st) {
+  if (head_size == 128)
+    hipLaunchKernelGGL((attention_kernel<T, 128>), dim3((unsigned)grid), dim3(512), 0, st, a);
+  else
+    hipLaunchKernelGGL((attention_kernel<T, 64>), dim3((unsigned)grid), dim3(512), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_attention(const AttnArgs& a, int dtype, int head_size, int grid,
+                            hipStream_t st) {
+  return dtype == 0 ? attention_dispatch<F16>(a, head_size, grid, st)
+                    : attention_dispatch<BF16>(a, head_size, grid, st);
+}
+
+template <typename T>
+static hipError_t combine_dispatch(const AttnArgs& a, int head_size, hipStream_t st) {
+  dim3 grid(a.num_seqs, a.num_kv_heads);
+  if (head_size == 128)
+    hipLaunchKernelGGL((combine_kernel<T, 128>), grid, dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL((combine_kernel<T, 64>), grid, dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_combine(const AttnArgs& a, int dtype, int head_size, hipStream_t st) {
+  return dtype == 0 ? combine_dispatch<F16>(a, head_size, st)
+                    : combine_dispatch<BF16>(a, head_size, st);
+}
+
+}  // namespace pa

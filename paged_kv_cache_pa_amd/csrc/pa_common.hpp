@@ -120,6 +120,22 @@ __device__ inline void scale_in_place(float4_t& acc, float alpha) {
 }
 
 
+// Lane index 0..63, recomputed at each use: the asm is volatile, so values
+// derived from it are not hoisted out of a loop and held (or spilled) across
+// it.  For per-lane address offsets that are cheaper to recompute than to
+// keep in registers.
+__device__ inline int lane_here() {
+  int l;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+  return l;
+}
+
+// floor(x / g) for 0 <= x < 65536 and 1 <= g <= 128, from inv_g = 1/g (a
+// uniform kernel argument, so no per-lane reciprocal is built and kept).
+// (x + 0.5) / g lies at least 0.5/g from an integer, far more than the
+// float rounding error of the product, so the floor is exact.
+__device__ inline int div_small(int x, float inv_g) { return (int)(((float)x + 0.5f) * inv_g); }
+
 __device__ inline u32x4_t ld16(const void* p) { return *reinterpret_cast<const u32x4_t*>(p); }
 __device__ inline u32x2_t ld8(const void* p) { return *reinterpret_cast<const u32x2_t*>(p); }
 

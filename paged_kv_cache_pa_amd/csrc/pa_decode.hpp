@@ -32,16 +32,24 @@
 // A sequence with one split writes its normalised output directly; longer
 // sequences write (m, l, unnormalised acc) per split and column, merged by
 // combine_kernel:  O = sum_s 2^(m_s - M) acc_s / sum_s 2^(m_s - M) l_s.
+#pragma once
+
 #include "pa_common.hpp"
 #include "pa_internal.hpp"
 
 namespace pa {
 
+// Runs decode work items on the calling wave until the decode counter is
+// exhausted.  Every wave is independent (no barriers, no LDS).
 template <typename T, int D>
-__global__ __launch_bounds__(256) void decode_kernel(AttnArgs a) {
+__device__ __forceinline__ void decode_items(const AttnArgs& a) {
   constexpr int NS = D / 32;    // QK^T contraction steps (8 halfs per lane)
   constexpr int NT = D / 16;    // O^T tiles; also halfs per lane per V row
-  const int lane = threadIdx.x & 63;
+  // Lane from lane_here() rather than threadIdx: each inlined copy of this
+  // body then derives its own per-lane values, instead of sharing values
+  // computed once at kernel entry that would stay live (spilled) across the
+  // other work the kernel does in between.
+  const int lane = lane_here();
   const int r16 = lane & 15, kq = lane >> 4;
   const int hk = a.num_kv_heads, G = a.group, hq = a.num_heads;
   const int64_t row_stride = (int64_t)hk * D;   // elements between token rows
@@ -55,7 +63,7 @@ __global__ __launch_bounds__(256) void decode_kernel(AttnArgs a) {
     int it = 0;
     if (lane == 0) it = atomicAdd(a.counters_rw + kCtrDecode, 1);
     it = __builtin_amdgcn_readfirstlane(__shfl(it, 0));
-    if (it >= n_items) break;
+    if (it >= n_items) return;
     const int pair = it / hk;
     const int kh = it - pair * hk;
     const int2 bsplit = a.dec_items[pair];
@@ -73,8 +81,9 @@ __global__ __launch_bounds__(256) void decode_kernel(AttnArgs a) {
     {
       const int n = r16;
       const bool valid = n < ncols;
-      const int tok = si.cu + (valid ? n / G : 0);
-      const int h = kh * G + (valid ? n % G : 0);
+      const int ng = div_small(n, a.inv_group);
+      const int tok = si.cu + (valid ? ng : 0);
+      const int h = kh * G + (valid ? n - ng * G : 0);
       const uint16_t* qrow = qp + ((int64_t)tok * hq + h) * D;
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
@@ -83,7 +92,7 @@ __global__ __launch_bounds__(256) void decode_kernel(AttnArgs a) {
     }
     // Causal limit of column n: token n / G sees keys <= past + n / G
     // (padding columns see every key and are never stored).
-    const int col_limit = past + r16 / G;
+    const int col_limit = past + div_small(r16, a.inv_group);
 
     // Block ids of this split, one per lane.
     const int blk0 = k0 >> a.block_shift;
@@ -173,20 +182,26 @@ __global__ __launch_bounds__(256) void decode_kernel(AttnArgs a) {
       }
     };
 
-    // Software pipeline: the loads of chunk c+1 are in flight while chunk c
-    // is computed (two register sets, unrolled by two).
+    // Software pipeline over two register sets: chunk c+1 is requested
+    // before chunk c is computed.  The loop runs over chunk pairs with a
+    // uniform trip count and its only exit is the loop test, so its body is
+    // straight-line and the compiler's wait counts keep the younger chunk in
+    // flight; the pair's second request past the split end re-reads the
+    // split's last chunk (cached) instead of branching.  A deeper ring
+    // measured no faster: a CU's streaming rate is bounded by its
+    // outstanding-miss capacity, not by how far ahead each wave issues.
+    const int nch = (k1 - k0 + 15) >> 4;
+    const int last_c0 = k0 + 16 * (nch - 1);
     Chunk ca, cb;
     load(k0, ca);
-    for (int c0 = k0;;) {
-      if (c0 + 16 < k1) load(c0 + 16, cb);
+    for (int pr = 0; pr < (nch >> 1); ++pr) {
+      const int c0 = k0 + 32 * pr;
+      load(c0 + 16, cb);
       compute(c0, ca);
-      c0 += 16;
-      if (c0 >= k1) break;
-      if (c0 + 16 < k1) load(c0 + 16, ca);
-      compute(c0, cb);
-      c0 += 16;
-      if (c0 >= k1) break;
+      load(min(c0 + 32, last_c0), ca);
+      compute(c0 + 16, cb);
     }
+    if (nch & 1) compute(last_c0, ca);
 
     const float l_tot = sum_xor16_32(l);
     const int n = r16;
@@ -194,8 +209,9 @@ __global__ __launch_bounds__(256) void decode_kernel(AttnArgs a) {
       // padding column: nothing to store
     } else if (nsplit == 1) {
       const float inv = 1.f / l_tot;
-      const int tok = si.cu + n / G;
-      const int h = kh * G + n % G;
+      const int ng = div_small(n, a.inv_group);
+      const int tok = si.cu + ng;
+      const int h = kh * G + n - ng * G;
       uint16_t* orow = op + ((int64_t)tok * hq + h) * D;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -287,41 +303,6 @@ __global__ __launch_bounds__(256) void combine_kernel(AttnArgs a) {
     *reinterpret_cast<u32x2_t*>(op + ((int64_t)tok * a.num_heads + h) * D + d) =
         u32x2_t{Elt<T>::pack2(o[0], o[1]), Elt<T>::pack2(o[2], o[3])};
   }
-}
-
-template <typename T>
-static hipError_t decode_dispatch(const AttnArgs& a, int head_size, int64_t max_blocks, int num_cus,
-                                  hipStream_t st) {
-  const void* fn = head_size == 128 ? (const void*)&decode_kernel<T, 128> : (const void*)&decode_kernel<T, 64>;
-  int64_t grid = resident_blocks(fn, num_cus);
-  if (grid > max_blocks) grid = max_blocks;
-  if (grid < 1) grid = 1;
-  if (head_size == 128)
-    hipLaunchKernelGGL((decode_kernel<T, 128>), dim3((unsigned)grid), dim3(256), 0, st, a);
-  else
-    hipLaunchKernelGGL((decode_kernel<T, 64>), dim3((unsigned)grid), dim3(256), 0, st, a);
-  return hipGetLastError();
-}
-
-hipError_t launch_decode(const AttnArgs& a, int dtype, int head_size, int64_t max_blocks,
-                         int num_cus, hipStream_t st) {
-  return dtype == 0 ? decode_dispatch<F16>(a, head_size, max_blocks, num_cus, st)
-                    : decode_dispatch<BF16>(a, head_size, max_blocks, num_cus, st);
-}
-
-template <typename T>
-static hipError_t combine_dispatch(const AttnArgs& a, int head_size, hipStream_t st) {
-  dim3 grid(a.num_seqs, a.num_kv_heads);
-  if (head_size == 128)
-    hipLaunchKernelGGL((combine_kernel<T, 128>), grid, dim3(256), 0, st, a);
-  else
-    hipLaunchKernelGGL((combine_kernel<T, 64>), grid, dim3(256), 0, st, a);
-  return hipGetLastError();
-}
-
-hipError_t launch_combine(const AttnArgs& a, int dtype, int head_size, hipStream_t st) {
-  return dtype == 0 ? combine_dispatch<F16>(a, head_size, st)
-                    : combine_dispatch<BF16>(a, head_size, st);
 }
 
 }  // namespace pa

@@ -24,18 +24,32 @@ constexpr int kDecodeCols = 16;
 constexpr int kPrefillRows = 256;
 constexpr int kPrefillKeys = 64;
 constexpr int kQueues = 8;  // one prefill work queue per XCD
+// Cost model of the attention kernel's role split: one CU spends about as
+// long on one prefill tile step (256 query rows x 64 keys) as on streaming
+// this many decode key rows (K and V of one KV head); both scale with
+// head_size.  Measured on MI355X: 2.8 us per bf16/fp16 tile step at
+// head_size 128, 13.5 ns per 512-byte key row with ~96 CUs streaming.
+constexpr float kPrefillStepCost = 200.f;
 constexpr int kMaxGroup = 128;  // largest supported num_heads / num_kv_heads
 constexpr float kLog2e = 1.4426950408889634f;
 
-// Counter block at the start of the workspace (int32 slots).
+// Counter block at the start of the workspace (int32 slots).  Every fetch
+// counter (a device-scope atomic) has a 128-byte cache line of its own, and
+// the read-only plan results share another: atomics on a line serialize at
+// the L2, so reads or atomics that shared a line with the decode counter
+// would queue behind its traffic and hold up the decode item fetches.
+constexpr int kLine = 32;   // int32 slots per 128-byte line
 enum Counter : int {
-  kCtrDecode = 0,            // decode work fetch counter
-  kCtrPrefill = 1,           // 1..8: per-queue prefill fetch counters
-  kNumDecPairs = 9,          // number of (sequence, split) decode pairs
-  kQueueLen = 10,            // 10..17
-  kQueueStart = 18,          // 18..25
-  kNumCounters = 64
+  kCtrDecode = 0,                          // decode work fetch counter
+  kCtrPrefill = kLine,                     // + kLine * x: fetch counter of prefill queue x
+  kPlanResults = kLine * (1 + kQueues),    // read-only plan results from here:
+  kNumDecPairs = kPlanResults,             //   number of (sequence, split) decode pairs
+  kQueueLen = kPlanResults + 1,            //   + x: items in prefill queue x
+  kQueueStart = kPlanResults + 1 + kQueues,  // + x: first item of queue x
+  kPrefillFirst = kPlanResults + 1 + 2 * kQueues,  // attention groups [0, this) start on prefill
+  kNumCounters = kPlanResults + kLine
 };
+static_assert(kPrefillFirst < kNumCounters, "counter block layout");
 
 struct SeqInfo {  // one per sequence, written by the plan kernel
   int32_t cu;     // first packed token
@@ -69,6 +83,7 @@ struct PlanArgs {
   int2* dec_items;
   int4* pf_items;
   int32_t num_seqs, group, num_kv_heads, tokens_per_tile;
+  int32_t num_workers;  // grid size of the attention kernel
 };
 
 struct AttnArgs {
@@ -87,18 +102,20 @@ struct AttnArgs {
   int32_t num_seqs, num_heads, num_kv_heads, group, max_blocks_per_seq;
   int32_t block_size, block_shift, tokens_per_tile;
   float scale_log2;  // scale * log2(e)
+  float inv_group;   // 1 / group (exact small-integer division, see div_small)
 };
 
 hipError_t launch_scatter(const void* k_new, const void* v_new, const int32_t* slots, void* kc,
                           void* vc, int64_t num_tokens, int32_t row_bytes, hipStream_t st);
 hipError_t launch_plan(const PlanArgs& a, hipStream_t st);
-// Persistent kernels: the launchers size the grid as min(what the device
-// holds at once, max_blocks) so no work-group is launched only to exit.
-hipError_t launch_decode(const AttnArgs& a, int dtype, int head_size, int64_t max_blocks,
-                         int num_cus, hipStream_t st);
+// The attention kernel is persistent: one 512-thread work-group per slot the
+// device holds at once.  Work-groups [0, counters[kPrefillFirst]) run prefill
+// items first and then decode items; the others run decode items first, so
+// compute-bound prefill and bandwidth-bound decode overlap across CUs.
+int attention_workers(int dtype, int head_size, int num_cus);
+hipError_t launch_attention(const AttnArgs& a, int dtype, int head_size, int grid,
+                            hipStream_t st);
 hipError_t launch_combine(const AttnArgs& a, int dtype, int head_size, hipStream_t st);
-hipError_t launch_prefill(const AttnArgs& a, int dtype, int head_size, int64_t max_blocks,
-                          int num_cus, hipStream_t st);
 
 // Work-groups of `kernel` (`threads` per group) resident at once.
 int resident_blocks(const void* kernel, int num_cus, int threads = 256);

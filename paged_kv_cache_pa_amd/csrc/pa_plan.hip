@@ -13,7 +13,10 @@
 // takes the prefill path in tiles of tokens_per_tile tokens per KV head.
 // Prefill (sequence, KV head) pairs are dealt to 8 queues, one per XCD, so
 // all tiles that reuse one K/V stream share an L2; inside a queue the
-// heaviest (last) tile of each pair comes first.
+// heaviest (last) tile of each pair comes first.  The plan also splits the
+// attention kernel's work-groups between the two kinds of work in proportion
+// to their estimated CU time (prefill: 64-key tile steps x kPrefillStepCost;
+// decode: key rows streamed).
 #include "pa_common.hpp"
 #include "pa_internal.hpp"
 
@@ -94,14 +97,26 @@ __device__ inline int heads_in_queue(int b, int hk, int x) {
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
   __shared__ int lds[(kPlanWaves + 1) * 12];
   __shared__ int qstart[kQueues];
+  __shared__ float cost_sh[2];
   const int tid = threadIdx.x;
-  if (tid <= kQueues) a.counters[kCtrDecode + tid] = 0;   // fetch counters 0..8
+  if (tid <= kQueues) a.counters[kLine * tid] = 0;   // fetch counters: decode, then queues 0..7
+  if (tid < 2) cost_sh[tid] = 0.f;
+  __syncthreads();
 
-  // Pass 1: sequence info, decode pairs, partial-row bases, queue sizes.
+  // Pass 1: sequence info, decode pairs, partial-row bases, queue sizes,
+  // estimated prefill and decode costs.
   int carry[3 + kQueues] = {0};
+  float cost_p = 0.f, cost_d = 0.f;
   for (int base = 0; base < a.num_seqs; base += kPlanThreads) {
     const int b = base + tid;
     const SeqCounts c = seq_counts(a, b);
+    if (c.ntiles > 0) {   // key tiles per item ~ (past + mid-tile row) / 64, rounded up
+      const float past = (float)(c.L - c.q_len);
+      cost_p += (float)c.ntiles * a.num_kv_heads *
+                ((past + 0.5f * (c.q_len + a.tokens_per_tile)) / kPrefillKeys + 0.5f);
+    } else if (c.q_len > 0) {
+      cost_d += (float)c.L * a.num_kv_heads;
+    }
     int v[3 + kQueues], tot[3 + kQueues];
     v[0] = c.nsplit;
     v[1] = c.prows;
@@ -117,7 +132,22 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
 #pragma unroll
     for (int k = 0; k < 3 + kQueues; ++k) carry[k] += tot[k];
   }
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    cost_p += __shfl_xor(cost_p, o);
+    cost_d += __shfl_xor(cost_d, o);
+  }
+  if ((tid & 63) == 0) {
+    atomicAdd(&cost_sh[0], cost_p);
+    atomicAdd(&cost_sh[1], cost_d);
+  }
+  __syncthreads();
   if (tid == 0) {
+    const float wp = cost_sh[0] * kPrefillStepCost, wd = cost_sh[1];
+    int first = a.num_workers;
+    if (wd > 0.f) first = (int)(a.num_workers * (wp / (wp + wd)) + 0.5f);
+    if (wp > 0.f && first < 1) first = 1;
+    a.counters[kPrefillFirst] = min(first, a.num_workers);
     a.counters[kNumDecPairs] = carry[0];
     int run = 0;
     for (int x = 0; x < kQueues; ++x) {

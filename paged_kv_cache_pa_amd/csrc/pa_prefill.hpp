@@ -8,13 +8,14 @@
 // K/V straight from the paged cache); FlexAttention operator page -
 // "FlexAttention Computation" and "Grouped Query Attention (GQA)".
 //
-// Work item = (sequence b, KV head kh, tile): 128 query rows, row r being
+// Work item = (sequence b, KV head kh, tile): 256 query rows, row r being
 // token i0 + r / G of the tile and query head kh*G + r % G, so the G heads
 // that share kh share every K/V tile.  Items come from 8 per-XCD queues
 // (work-group w serves queue w % 8 first, then steals from the others).
-// Each of the 4 waves owns 32 rows (two 16-row groups).  Per 64-key tile:
+// Each of the 8 waves owns 32 rows (two 16-row groups).  Per 64-key tile:
 //   K, V rows resolved through the block table (one block id per wave per
-//   tile), copied HBM -> LDS by 128-bit direct-to-LDS loads, double buffered
+//   tile), copied HBM -> LDS by 128-bit direct-to-LDS loads into a ring of
+//   four tile buffers
 //   S^T = K . Q^T          16x16x32 MFMA (fp16/bf16 in, fp32 acc)
 //   causal mask key <= past + i, online softmax in fp32 (exp2)
 //   O^T += V^T . P^T       16x16x32 MFMA, P rounded to the input dtype
@@ -24,6 +25,8 @@
 // diagonal, and the output accumulators are rescaled only when a row's
 // running max moves.  Key rows past the visible range are replaced by the
 // last visible row, so NaN in unused cache slots never enters LDS.
+#pragma once
+
 #include <type_traits>
 
 #include "pa_common.hpp"
@@ -39,15 +42,17 @@ typedef __attribute__((address_space(4))) int32_t const_i32_t;
 constexpr int kSchedMfma = 0x008;
 constexpr int kSchedDsRead = 0x100;
 
-// 16-byte-per-lane copy global -> LDS (global_load_lds_dwordx4): lane l's
-// 16 bytes land at LDS byte lds_base + 16 * l.  Issued from inline asm so
-// that the compiler does not treat later LDS reads of *other* ring buffers
-// as dependent on it; the kernel orders these copies itself with explicit
-// vmcnt waits and barriers.  The instruction has no register results.
-__device__ inline void lds_dma16(const void* gptr, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+// 16-byte-per-lane copy global -> LDS (global_load_lds_dwordx4): lane l
+// copies the 16 bytes at base + voff (base wave-uniform in SGPRs, voff a
+// 32-bit per-lane byte offset) to LDS byte lds_base + 16 * l.  Issued from
+// inline asm so that the compiler does not treat later LDS reads of *other*
+// ring buffers as dependent on it; the kernel orders these copies itself
+// with explicit vmcnt waits and barriers.  The instruction has no register
+// results.
+__device__ inline void lds_dma16(const void* base, uint32_t voff, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
                :
-               : "s"(lds_base), "v"(gptr)
+               : "s"(lds_base), "v"(voff), "s"(base)
                : "memory", "m0");
 }
 
@@ -70,8 +75,10 @@ __device__ inline void wait_vmcnt() {
 // (QK^T of tile i and P.V of tile i-1), group B runs the softmax of the
 // previous tile on the vector ALUs, and at the next barrier they swap, so
 // the two halves of every SIMD keep the MFMA and VALU pipes busy together.
+// Runs prefill work items on the calling work-group (512 threads, all of
+// which must call it) until every queue is exhausted.
 template <typename T, int D>
-__global__ __launch_bounds__(512, 1) void prefill_kernel(AttnArgs a) {
+__device__ __forceinline__ void prefill_items(const AttnArgs& a) {
   constexpr int NS = D / 32;            // QK^T steps
   constexpr int NT = D / 16;            // O^T tiles
   constexpr int NR = 2;                 // 16-row groups per wave (32 rows)
@@ -94,8 +101,6 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(AttnArgs a) {
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int grp = wave >> 2;            // 0: group A, 1: group B
-  const int lane = tid & 63;
-  const int r16 = lane & 15, kq = lane >> 4;
   const int hk = a.num_kv_heads, G = a.group, hq = a.num_heads;
   const int TQ = a.tokens_per_tile;
   const int bsz = a.block_size, shift = a.block_shift;
@@ -121,7 +126,7 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(AttnArgs a) {
     const int qstart = a.counters[kQueueStart + x];
     if (qlen == 0) continue;   // no atomics or barriers on empty queues
     for (;;) {
-      if (tid == 0) item_sh = atomicAdd(a.counters_rw + kCtrPrefill + x, 1);
+      if (tid == 0) item_sh = atomicAdd(a.counters_rw + kCtrPrefill + kLine * x, 1);
       __syncthreads();
       const int k = __builtin_amdgcn_readfirstlane(item_sh);   // uniform: scalar loads below
       __syncthreads();
@@ -147,45 +152,58 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(AttnArgs a) {
       // Rows [RPW*wave, RPW*wave+RPW) of the K and V tiles of key tile t;
       // keys at or past kend are clamped onto key kend-1 (finite, masked).
       auto issue = [&](int t, int blk) {
-        const int64_t blk_row = (int64_t)blk * bsz;
+        // Block start (wave-uniform, scalar) + 32-bit lane offset in bytes.
+        const int64_t bstart = (int64_t)blk * bsz * row_stride + (int64_t)kh * D;
+        const uint16_t* kbase = kc + bstart;
+        const uint16_t* vbase = vc + bstart;
         const uint32_t kdst = lds_addr + (uint32_t)((t % NB) * 2 * TB + RPW * wave * ROWB);
+        const int ln = lane_here();   // recomputed, not held across the tile loop
 #pragma unroll
         for (int p = 0; p < LPW; ++p) {
-          const int row = RPW * wave + p * RPI + lane / CPR;
+          const int row = RPW * wave + p * RPI + ln / CPR;
           const int j = min(t * BN + row, kend - 1);
-          const int gch = (lane % CPR) ^ swz(row);
-          const int64_t off = (blk_row + (j & (bsz - 1))) * row_stride + (int64_t)kh * D + gch * 8;
-          lds_dma16(kc + off, kdst + p * 1024);
-          lds_dma16(vc + off, kdst + TB + p * 1024);
+          const int gch = (ln % CPR) ^ swz(row);
+          const uint32_t voff = (uint32_t)(((j & (bsz - 1)) * (int)row_stride + gch * 8) * 2);
+          lds_dma16(kbase, voff, kdst + p * 1024);
+          lds_dma16(vbase, voff, kdst + TB + p * 1024);
         }
       };
 
+      // Per-lane indices taken per item (lane_here), so values derived from
+      // them are not hoisted out of the item loop and held across it.
+      const int lane = lane_here();
+      const int r16 = lane & 15, kq = lane >> 4;
+
       // Q^T operands and causal limits of this lane's row groups.
       u32x4_t qreg[NR][NS];
-      int limit[NR], tok[NR], head[NR];
+      int limit[NR];
 #pragma unroll
       for (int rho = 0; rho < NR; ++rho) {
         const int row = 32 * wave + 16 * rho + r16;
-        const int ti = i0 + row / G;
+        const int rg = div_small(row, a.inv_group);
+        const int ti = i0 + rg;
         const bool valid = row < TQ * G && ti < ql;
-        tok[rho] = valid ? si.cu + ti : -1;
-        head[rho] = kh * G + row % G;
+        const int head = kh * G + row - rg * G;
         limit[rho] = valid ? past + ti : -1;
-        const uint16_t* qrow = qp + ((int64_t)(valid ? tok[rho] : 0) * hq + head[rho]) * D;
+        const uint16_t* qrow = qp + ((int64_t)(valid ? si.cu + ti : 0) * hq + head) * D;
 #pragma unroll
         for (int s = 0; s < NS; ++s)
           qreg[rho][s] = valid ? ld16(qrow + (4 * s + kq) * 8) : u32x4_t{0, 0, 0, 0};
       }
-      int wave_kmax = max(limit[0], limit[1]);
-      int wave_kmin = min(limit[0], limit[1]);
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        wave_kmax = max(wave_kmax, __shfl_xor(wave_kmax, o));
-        wave_kmin = min(wave_kmin, __shfl_xor(wave_kmin, o));
+      // Largest and smallest causal limit over this wave's rows
+      // 32*wave .. 32*wave+31 (a padding row counts as -1), in closed form
+      // from wave-uniform values so the per-tile branches below are
+      // uniform: limits grow with the row, and rows below rows_valid are
+      // the real ones.
+      int wave_kmax = -1, wave_kmin = -1;
+      {
+        const int r0 = 32 * wave;
+        const int rows_valid = min(TQ, ql - i0) * G;
+        if (r0 < rows_valid) {
+          wave_kmax = past + i0 + min(r0 + 31, rows_valid - 1) / G;
+          if (r0 + 31 < rows_valid) wave_kmin = past + i0 + r0 / G;
+        }
       }
-      // Wave-uniform (scalar) so the per-tile branches below are uniform.
-      wave_kmax = __builtin_amdgcn_readfirstlane(wave_kmax);
-      wave_kmin = __builtin_amdgcn_readfirstlane(wave_kmin);
 
       float m[NR], l[NR];
       float4_t acc[NR][NT];
@@ -216,10 +234,10 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(AttnArgs a) {
           // i receives d = 16t + i of keys 4kq .. 4kq+3: the V^T operand,
           // with contraction element e <-> key 32u + 4kq + e (e < 4) or
           // 32u + 16 + 4kq + (e - 4), the same keys pb holds.
-          const int r4 = (lane & 15) >> 2, q4 = lane & 3;
+          const int r4 = (lane & 15) >> 2, q4 = lane & 3, vk = kq;
 #pragma unroll
           for (int u = 0; u < NK / 2; ++u) {
-            const int R0 = 32 * u + 4 * kq + r4;
+            const int R0 = 32 * u + 4 * vk + r4;
 #pragma unroll
             for (int t = 0; t < NT; ++t) {
               const int chunk = 2 * t + (q4 >> 1);
@@ -248,13 +266,17 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(AttnArgs a) {
       // S = K_t Q^T with K of tile t.
       auto qk = [&](int t) {
         const unsigned char* kb = lds + (t % NB) * 2 * TB;
+        // Per-lane K read offsets recomputed here (a few VALU ops per tile)
+        // rather than held across the tile loop.
+        const int ln = lane_here();
+        const int kr = ln & 15, kk = ln >> 4;
 #pragma unroll
           for (int kap = 0; kap < NK; ++kap) {
 #pragma unroll
             for (int rho = 0; rho < NR; ++rho) sacc[kap][rho] = float4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int s = 0; s < NS; ++s) {
-              const u32x4_t ka = *reinterpret_cast<const u32x4_t*>(kb + slot(16 * kap + r16, 4 * s + kq));
+              const u32x4_t ka = *reinterpret_cast<const u32x4_t*>(kb + slot(16 * kap + kr, 4 * s + kk));
 #pragma unroll
               for (int rho = 0; rho < NR; ++rho)
                 sacc[kap][rho] = Elt<T>::mfma32(ka, qreg[rho][s], sacc[kap][rho]);
@@ -425,41 +447,27 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(AttnArgs a) {
         }
       }
 
+      // Output rows: token and head recomputed here (not held in registers
+      // through the tile loops).
+      const int eln = lane_here();
 #pragma unroll
       for (int rho = 0; rho < NR; ++rho) {
         const float l_tot = sum_xor16_32(l[rho]);
-        if (tok[rho] < 0) continue;
+        if (limit[rho] < 0) continue;   // padding row
         const float inv = 1.f / l_tot;
-        uint16_t* orow = op + ((int64_t)tok[rho] * hq + head[rho]) * D;
+        const int row = 32 * wave + 16 * rho + (eln & 15);
+        const int rg = div_small(row, a.inv_group);
+        const int64_t orow_el = ((int64_t)(si.cu + i0 + rg) * hq + kh * G + row - rg * G) * D;
+        uint16_t* orow = op + orow_el + 4 * (eln >> 4);
 #pragma unroll
         for (int t = 0; t < NT; ++t) {   // lane holds d = 16t + 4kq + r, r = 0..3
-          *reinterpret_cast<u32x2_t*>(orow + 16 * t + 4 * kq) =
+          *reinterpret_cast<u32x2_t*>(orow + 16 * t) =
               u32x2_t{Elt<T>::pack2(acc[rho][t][0] * inv, acc[rho][t][1] * inv),
                       Elt<T>::pack2(acc[rho][t][2] * inv, acc[rho][t][3] * inv)};
         }
       }
     }
   }
-}
-
-template <typename T>
-static hipError_t prefill_dispatch(const AttnArgs& a, int head_size, int64_t max_blocks, int num_cus,
-                                  hipStream_t st) {
-  const void* fn = head_size == 128 ? (const void*)&prefill_kernel<T, 128> : (const void*)&prefill_kernel<T, 64>;
-  int64_t grid = resident_blocks(fn, num_cus, 512);
-  if (grid > max_blocks) grid = max_blocks;
-  if (grid < 1) grid = 1;
-  if (head_size == 128)
-    hipLaunchKernelGGL((prefill_kernel<T, 128>), dim3((unsigned)grid), dim3(512), 0, st, a);
-  else
-    hipLaunchKernelGGL((prefill_kernel<T, 64>), dim3((unsigned)grid), dim3(512), 0, st, a);
-  return hipGetLastError();
-}
-
-hipError_t launch_prefill(const AttnArgs& a, int dtype, int head_size, int64_t max_blocks,
-                         int num_cus, hipStream_t st) {
-  return dtype == 0 ? prefill_dispatch<F16>(a, head_size, max_blocks, num_cus, st)
-                    : prefill_dispatch<BF16>(a, head_size, max_blocks, num_cus, st);
 }
 
 }  // namespace pa
