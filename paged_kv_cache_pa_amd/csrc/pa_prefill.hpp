@@ -122,8 +122,9 @@ __device__ __forceinline__ void prefill_items(const AttnArgs& a) {
 
   for (int qi = 0; qi < kQueues; ++qi) {
     const int x = (home + qi) % kQueues;
-    const int qlen = a.counters[kQueueLen + x];
-    const int qstart = a.counters[kQueueStart + x];
+    // Uniform plan results: keep them in scalar registers.
+    const int qlen = __builtin_amdgcn_readfirstlane(a.counters[kQueueLen + x]);
+    const int qstart = __builtin_amdgcn_readfirstlane(a.counters[kQueueStart + x]);
     if (qlen == 0) continue;   // no atomics or barriers on empty queues
     for (;;) {
       if (tid == 0) item_sh = atomicAdd(a.counters_rw + kCtrPrefill + kLine * x, 1);
@@ -235,62 +236,77 @@ __device__ __forceinline__ void prefill_items(const AttnArgs& a) {
           // with contraction element e <-> key 32u + 4kq + e (e < 4) or
           // 32u + 16 + 4kq + (e - 4), the same keys pb holds.
           const int r4 = (lane & 15) >> 2, q4 = lane & 3, vk = kq;
-#pragma unroll
-          for (int u = 0; u < NK / 2; ++u) {
+          // Operands in groups of VG (u, t .. t+VG-1); group g+1 is read while
+          // group g feeds its MFMAs (two register sets, fenced as in qk).
+          constexpr int VG = 2;
+          constexpr int NG = (NK / 2) * NT / VG;
+          auto vread = [&](int u, int t) {
             const int R0 = 32 * u + 4 * vk + r4;
+            const int chunk = 2 * t + (q4 >> 1);
+            const int boff = (q4 & 1) << 3;
+            const short4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_s4_t)(vb + TB + slot(R0, chunk) + boff));
+            const short4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_s4_t)(vb + TB + slot(R0 + 16, chunk) + boff));
+            const u32x2_t l2 = __builtin_bit_cast(u32x2_t, lo);
+            const u32x2_t h2 = __builtin_bit_cast(u32x2_t, hi);
+            return u32x4_t{l2[0], l2[1], h2[0], h2[1]};
+          };
+          u32x4_t va[2][VG];
 #pragma unroll
-            for (int t = 0; t < NT; ++t) {
-              const int chunk = 2 * t + (q4 >> 1);
-              const int boff = (q4 & 1) << 3;
-              const short4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                  (lds_s4_t)(vb + TB + slot(R0, chunk) + boff));
-              const short4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                  (lds_s4_t)(vb + TB + slot(R0 + 16, chunk) + boff));
-              const u32x2_t l2 = __builtin_bit_cast(u32x2_t, lo);
-              const u32x2_t h2 = __builtin_bit_cast(u32x2_t, hi);
-              const u32x4_t va = {l2[0], l2[1], h2[0], h2[1]};
+          for (int e = 0; e < VG; ++e) va[0][e] = vread(0, e);
+#pragma unroll
+          for (int g = 0; g < NG; ++g) {
+            if (g + 1 < NG) {
+#pragma unroll
+              for (int e = 0; e < VG; ++e) {
+                const int k = (g + 1) * VG + e;
+                va[(g + 1) & 1][e] = vread(k / NT, k % NT);
+              }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int e = 0; e < VG; ++e) {
+              const int k = g * VG + e, u = k / NT, t = k % NT;
 #pragma unroll
               for (int rho = 0; rho < NR; ++rho)
-                acc[rho][t] = Elt<T>::mfma32(va, pb[rho][u], acc[rho][t]);
+                acc[rho][t] = Elt<T>::mfma32(va[g & 1][e], pb[rho][u], acc[rho][t]);
             }
+            __builtin_amdgcn_sched_barrier(0);
           }
-          // Two V^T operands (4 transposed reads) ahead of the MFMAs.
-          __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 4, 0);
-#pragma unroll
-          for (int r = 0; r < NT * (NK / 2) - 2; ++r) {
-            __builtin_amdgcn_sched_group_barrier(kSchedMfma, NR, 0);
-            __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
-          }
-          __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2 * NR, 0);
       };
-      // S = K_t Q^T with K of tile t.
+      // S = K_t Q^T with K of tile t.  The K operands of 16-key group kap+1
+      // are read while group kap feeds its MFMAs (two register sets; the
+      // fences keep each group's reads a group ahead of their use, so the
+      // LDS latency hides under the previous group's 8 MFMAs).
       auto qk = [&](int t) {
         const unsigned char* kb = lds + (t % NB) * 2 * TB;
         // Per-lane K read offsets recomputed here (a few VALU ops per tile)
         // rather than held across the tile loop.
         const int ln = lane_here();
         const int kr = ln & 15, kk = ln >> 4;
+        u32x4_t ka[2][NS];
 #pragma unroll
-          for (int kap = 0; kap < NK; ++kap) {
+        for (int s = 0; s < NS; ++s)
+          ka[0][s] = *reinterpret_cast<const u32x4_t*>(kb + slot(kr, 4 * s + kk));
 #pragma unroll
-            for (int rho = 0; rho < NR; ++rho) sacc[kap][rho] = float4_t{0.f, 0.f, 0.f, 0.f};
+        for (int kap = 0; kap < NK; ++kap) {
+          if (kap + 1 < NK) {
 #pragma unroll
-            for (int s = 0; s < NS; ++s) {
-              const u32x4_t ka = *reinterpret_cast<const u32x4_t*>(kb + slot(16 * kap + kr, 4 * s + kk));
-#pragma unroll
-              for (int rho = 0; rho < NR; ++rho)
-                sacc[kap][rho] = Elt<T>::mfma32(ka, qreg[rho][s], sacc[kap][rho]);
-            }
+            for (int s = 0; s < NS; ++s)
+              ka[(kap + 1) & 1][s] =
+                  *reinterpret_cast<const u32x4_t*>(kb + slot(16 * (kap + 1) + kr, 4 * s + kk));
           }
-          // Keep one 16-key group of K operands in flight ahead of the MFMAs
-          // instead of hoisting every read (register pressure).
-          __builtin_amdgcn_sched_group_barrier(kSchedDsRead, NS, 0);
+          __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-          for (int r = 0; r < NK - 1; ++r) {
-            __builtin_amdgcn_sched_group_barrier(kSchedMfma, NS * NR, 0);
-            __builtin_amdgcn_sched_group_barrier(kSchedDsRead, NS, 0);
+          for (int s = 0; s < NS; ++s) {
+#pragma unroll
+            for (int rho = 0; rho < NR; ++rho)
+              sacc[kap][rho] = Elt<T>::mfma32(ka[kap & 1][s], qreg[rho][s],
+                                              s == 0 ? float4_t{0.f, 0.f, 0.f, 0.f} : sacc[kap][rho]);
           }
-          __builtin_amdgcn_sched_group_barrier(kSchedMfma, NS * NR, 0);
+          __builtin_amdgcn_sched_barrier(0);
+        }
       };
 
       // Softmax of tile j into P (pb), running max / sum and rescale.
