@@ -97,6 +97,7 @@ __device__ inline int heads_in_queue(int b, int hk, int x) {
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
   __shared__ int lds[(kPlanWaves + 1) * 12];
   __shared__ int qstart[kQueues];
+  __shared__ int nfull_total;
   __shared__ float cost_sh[2];
   const int tid = threadIdx.x;
   if (tid <= kQueues) a.counters[kLine * tid] = 0;   // fetch counters: decode, then queues 0..7
@@ -117,17 +118,22 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
     } else if (c.q_len > 0) {
       cost_d += (float)c.L * a.num_kv_heads;
     }
+    // Decode pairs: every full kSplitKeys split first (pass 1), then the
+    // shorter last splits (pass 2), so the tail of the decode work is made
+    // of short items.
+    const int has_part = (c.L % kSplitKeys) != 0 && c.nsplit > 0;
+    const int nfull = c.nsplit - has_part;
     int v[3 + kQueues], tot[3 + kQueues];
-    v[0] = c.nsplit;
+    v[0] = nfull;
     v[1] = c.prows;
-    v[2] = c.ntiles > 0;
+    v[2] = has_part;
 #pragma unroll
     for (int x = 0; x < kQueues; ++x) v[3 + x] = c.ntiles * heads_in_queue(b, a.num_kv_heads, x);
     block_scan<3 + kQueues>(v, tot, lds);
     if (b < a.num_seqs) {
       a.seqinfo[b] = SeqInfo{c.cu0, c.q_len, c.L, carry[1] + v[1]};
       const int off = carry[0] + v[0];
-      for (int s = 0; s < c.nsplit; ++s) a.dec_items[off + s] = make_int2(b, s);
+      for (int s = 0; s < nfull; ++s) a.dec_items[off + s] = make_int2(b, s);
     }
 #pragma unroll
     for (int k = 0; k < 3 + kQueues; ++k) carry[k] += tot[k];
@@ -148,7 +154,8 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
     if (wd > 0.f) first = (int)(a.num_workers * (wp / (wp + wd)) + 0.5f);
     if (wp > 0.f && first < 1) first = 1;
     a.counters[kPrefillFirst] = min(first, a.num_workers);
-    a.counters[kNumDecPairs] = carry[0];
+    a.counters[kNumDecPairs] = carry[0] + carry[2];
+    nfull_total = carry[0];
     int run = 0;
     for (int x = 0; x < kQueues; ++x) {
       a.counters[kQueueLen + x] = carry[3 + x];
@@ -159,15 +166,19 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
   }
   __syncthreads();
 
-  // Pass 2: prefill items, heaviest tile of each (sequence, head) first.
-  int qcarry[kQueues] = {0};
+  // Pass 2: the partial last decode splits after all full ones; prefill
+  // items, heaviest tile of each (sequence, head) first.
+  int qcarry[kQueues + 1] = {0};
   for (int base = 0; base < a.num_seqs; base += kPlanThreads) {
     const int b = base + tid;
     const SeqCounts c = seq_counts(a, b);
-    int v[kQueues], tot[kQueues];
+    const int has_part = (c.L % kSplitKeys) != 0 && c.nsplit > 0;
+    int v[kQueues + 1], tot[kQueues + 1];
 #pragma unroll
     for (int x = 0; x < kQueues; ++x) v[x] = c.ntiles * heads_in_queue(b, a.num_kv_heads, x);
-    block_scan<kQueues>(v, tot, lds);
+    v[kQueues] = has_part;
+    block_scan<kQueues + 1>(v, tot, lds);
+    if (has_part) a.dec_items[nfull_total + qcarry[kQueues] + v[kQueues]] = make_int2(b, c.nsplit - 1);
     if (c.ntiles > 0) {
       for (int kh = 0; kh < a.num_kv_heads; ++kh) {
         const int x = (int)(((int64_t)b * a.num_kv_heads + kh) & 7);
@@ -176,7 +187,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
       }
     }
 #pragma unroll
-    for (int x = 0; x < kQueues; ++x) qcarry[x] += tot[x];
+    for (int x = 0; x <= kQueues; ++x) qcarry[x] += tot[x];
   }
 }
 
