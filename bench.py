@@ -87,7 +87,49 @@ def step(wl, st, pa):
                     wl.num_heads, wl.num_kv_heads, out=st["out"], workspace=st["ws"])
 
 
-def time_workload(wl, steps, warmup, torch, pa, W):
+SCRUB_BYTES = 512 << 20     # written between separately timed reps (larger than the 256 MB MALL)
+
+
+def per_rep_times(fn, reps, torch, scrub):
+    """Each rep timed on its own with HIP events, after writing `scrub`
+    (outside the events) so that no cache level still holds the previous
+    rep's data.  Median, min and p90 over the reps."""
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(reps)]
+    for i, (a, b) in enumerate(ev):
+        scrub.fill_(i & 255)
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    t = sorted(a.elapsed_time(b) for a, b in ev)
+    return {"reps": reps, "scrub_MiB": scrub.numel() >> 20, "median_ms": float(np.median(t)),
+            "min_ms": float(t[0]), "p90_ms": float(np.percentile(t, 90))}
+
+
+def sub_batch(wl, st, sel, torch, pa):
+    """Device inputs of pa_attention over the sequences in `sel` only; their
+    K/V already sit in the shared, filled cache."""
+    idx = np.flatnonzero(sel)
+    cu = wl.cu_seqlens_q
+    rows = np.concatenate([np.arange(cu[b], cu[b + 1]) for b in idx]).astype(np.int64)
+    ql = wl.q_lens[idx]
+    q = st["q"][torch.from_numpy(rows).cuda()].contiguous()
+    sub = {"q": q, "kc": st["kc"], "vc": st["vc"], "out": torch.empty_like(q),
+           "cu": torch.from_numpy(np.concatenate([[0], np.cumsum(ql)]).astype(np.int32)).cuda(),
+           "lens": torch.from_numpy(wl.seqlens_kv[idx].astype(np.int32)).cuda(),
+           "table": torch.from_numpy(np.ascontiguousarray(wl.block_table[idx]).astype(np.int32)).cuda()}
+    n = pa.pa_attention_workspace_size(len(idx), int(ql.sum()), wl.max_blocks_per_seq, wl.num_heads,
+                                       wl.num_kv_heads, wl.head_size, wl.block_size)
+    sub["ws"] = torch.empty(max(n, 256), dtype=torch.uint8, device="cuda")
+    return sub
+
+
+def time_workload(wl, steps, warmup, torch, pa, W, extras=False):
+    """Back-to-back timing of `steps` steps (the headline figure) and the
+    per-kernel averages; with `extras`, also per-rep scrubbed timing of the
+    step and, for a batch that mixes both kinds, its decode-only and
+    prefill-only sub-batches timed as separate pa_attention calls."""
     st = setup(wl, torch, pa, W)
     for _ in range(warmup):
         step(wl, st, pa)
@@ -108,9 +150,39 @@ def time_workload(wl, steps, warmup, torch, pa, W):
     kern = pa.profile_read()
     ms = e0.elapsed_time(e1) / steps
     per_kernel = {k: (v[0] / v[1] if v[1] else 0.0) for k, v in kern.items()}
+    more = {}
+    if extras:
+        scrub = torch.empty(SCRUB_BYTES, dtype=torch.uint8, device="cuda")
+        more["step_reps"] = per_rep_times(lambda: step(wl, st, pa), steps, torch, scrub)
+        G = wl.num_heads // wl.num_kv_heads
+        dec_sel = (wl.q_lens * G <= 16) & (wl.q_lens > 0)
+        pf_sel = wl.q_lens * G > 16
+        if dec_sel.any() and pf_sel.any():
+            subs = {}
+            for name, sel in (("decode_only", dec_sel), ("prefill_only", pf_sel)):
+                sb = sub_batch(wl, st, sel, torch, pa)
+                call = lambda sb=sb: pa.pa_attention(  # noqa: E731
+                    sb["q"], sb["cu"], sb["lens"], sb["table"], sb["kc"], sb["vc"], wl.scale,
+                    wl.num_heads, wl.num_kv_heads, out=sb["out"], workspace=sb["ws"])
+                for _ in range(3):
+                    call()
+                r = per_rep_times(call, steps, torch, scrub)
+                nbytes, flops = attention_work(wl, sel)
+                t = r["median_ms"] * 1e-3
+                r.update({"num_seqs": int(sel.sum()), "alg_bytes": nbytes, "alg_flops": flops,
+                          "TBps": nbytes / t / 1e12, "TFLOPs": flops / t / 1e12,
+                          "roofline_frac": roofline_time(nbytes, flops) / t})
+                subs[name] = r
+                del sb
+            subs["note"] = ("the two kinds of sequence of the same batch as separate pa_attention "
+                            "calls (same cache); their sum against the one mixed call shows what "
+                            "running both kinds in one launch gains")
+            subs["sum_of_separate_ms"] = subs["decode_only"]["median_ms"] + subs["prefill_only"]["median_ms"]
+            more["sub_batches"] = subs
+        del scrub
     del st
     torch.cuda.empty_cache()
-    return ms, wall / steps * 1e3, per_kernel
+    return ms, wall / steps * 1e3, per_kernel, more
 
 
 def summarize(wl, ms, per_kernel):
@@ -193,15 +265,15 @@ def copy_bandwidth(torch, nbytes=2 << 30, reps=10):
 # ------------------------------------------------------------- CPU baseline
 def cpu_baseline(wl, W, torch, budget_s=20.0):
     """The fp64 oracle (as it stands) on a bounded sample of the workload:
-    the first decode sequences and, if any, one prefill chunk; reported in
-    the metric's unit and as tokens/s."""
+    the first decode sequences and, if any, the first prefill chunks;
+    reported in the metric's unit and as tokens/s."""
     import oracle
     f64 = lambda t: t.float().cpu().numpy().astype(np.float64)  # noqa: E731
     vals = W.make_values(wl, device="cuda", backend="torch")
     kv_cu, cu = wl.kv_cu, wl.cu_seqlens_q
     dec = [int(b) for b in np.flatnonzero(wl.q_lens == 1)]
     pre = [int(b) for b in np.flatnonzero(wl.q_lens > 1)]
-    picks = pre[:1] + dec[:16]
+    picks = pre[:6] + dec[:96]      # ~10 s of fp64 oracle work on the host
     shape = (wl.block_size, wl.num_kv_heads, wl.head_size)
     kc, vc = {}, {}
     for b in picks:
@@ -213,6 +285,11 @@ def cpu_baseline(wl, W, torch, budget_s=20.0):
                           f64(vals["v_all"][kv_cu[b]:kv_cu[b + 1]]),
                           wl.kv_slots[kv_cu[b]:kv_cu[b + 1]], kc, vc, wl.block_size)
     q_parts = [f64(vals["q"][cu[b]:cu[b + 1]]) for b in picks]
+    # this step's new K/V rows of the sample (the last q_len positions of each)
+    new_lo = [int(kv_cu[b + 1] - wl.q_lens[b]) for b in picks]
+    new_k = [f64(vals["k_all"][lo:kv_cu[b + 1]]) for lo, b in zip(new_lo, picks)]
+    new_v = [f64(vals["v_all"][lo:kv_cu[b + 1]]) for lo, b in zip(new_lo, picks)]
+    new_slots = [wl.kv_slots[lo:kv_cu[b + 1]] for lo, b in zip(new_lo, picks)]
     del vals
     torch.cuda.empty_cache()
     q_lens = np.array([wl.q_lens[b] for b in picks], dtype=np.int32)
@@ -220,6 +297,10 @@ def cpu_baseline(wl, W, torch, budget_s=20.0):
     sub_lens = np.array([wl.seqlens_kv[b] for b in picks], dtype=np.int32)
     sub_table = wl.block_table[picks]
     q = np.concatenate(q_parts, axis=0)
+    t0 = time.perf_counter()
+    oracle.scatter_kv(np.concatenate(new_k), np.concatenate(new_v), np.concatenate(new_slots),
+                      kc, vc, wl.block_size)
+    t_scatter = time.perf_counter() - t0
     t0 = time.perf_counter()
     oracle.attention(q, sub_cu, sub_lens, sub_table, kc, vc, wl.scale, wl.num_heads,
                      wl.num_kv_heads, wl.block_size)
@@ -235,10 +316,13 @@ def cpu_baseline(wl, W, torch, budget_s=20.0):
     cores = len(os.sched_getaffinity(0))
     return {"value": 100.0 * roofline_time(nbytes, flops) / t, "unit": "% of MI355X roofline",
             "tokens_per_s": float(q_lens.sum()) / t, "seconds": t,
+            "scatter_seconds": t_scatter,
+            "scatter_tokens_per_s": float(q_lens.sum()) / max(t_scatter, 1e-9),
             "cores": int(blas or cores), "host_cpus": os.cpu_count(), "affinity_cpus": cores,
             "kind": "oracle",
-            "sample": f"fp64 NumPy oracle, pa_attention only, on {len(pre[:1])} prefill chunk(s) "
-                      f"of 512 tokens + {len(dec[:16])} decode sequences of the same workload "
+            "sample": f"fp64 NumPy oracle (attention timed apart from the scatter of the sample's "
+                      f"new tokens) on {len(pre[:6])} prefill chunk(s) "
+                      f"of 512 tokens + {len(dec[:96])} decode sequences of the same workload "
                       f"({int(q_lens.sum())} query tokens)"}
 
 
@@ -272,7 +356,8 @@ def main():
     copy_gbps = copy_bandwidth(torch)
 
     wl = W.by_index(WORKLOADS[args.workload])
-    ms, wall_ms, per_kernel = time_workload(wl, args.steps, args.warmup, torch, pa, W)
+    ms, wall_ms, per_kernel, more = time_workload(wl, args.steps, args.warmup, torch, pa, W,
+                                                  extras=not args.no_extra)
     head = summarize(wl, ms, per_kernel)
     if head.get("attention_bound") == "mfma":
         ach = head["attention_TFLOPs"]
@@ -291,9 +376,11 @@ def main():
     if not args.no_extra and args.workload == "mixed":
         for name in ("decode", "prefill"):
             w2 = W.by_index(WORKLOADS[name])
-            m2, _, k2 = time_workload(w2, max(5, args.steps // 2), 3, torch, pa, W)
+            m2, _, k2, more2 = time_workload(w2, max(5, args.steps // 2), 3, torch, pa, W,
+                                             extras=True)
             extra[name] = summarize(w2, m2, k2)
             extra[name]["workload"] = w2.name
+            extra[name]["step_reps"] = more2.get("step_reps")
 
     line = {
         "metric": "paged-attn decode HBM TB/s + prefill TFLOP/s, % of MI355X roofline",
@@ -315,6 +402,8 @@ def main():
         "kernel_ms": head["kernel_ms"],
         "copy_GBps": copy_gbps,
         "roofline": roof,
+        "step_reps": more.get("step_reps"),
+        "sub_batches": more.get("sub_batches"),
         "extra": extra,
     }
     if not args.no_cpu_baseline:
