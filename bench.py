@@ -154,6 +154,23 @@ def time_workload(wl, steps, warmup, torch, pa, W, extras=False):
     if extras:
         scrub = torch.empty(SCRUB_BYTES, dtype=torch.uint8, device="cuda")
         more["step_reps"] = per_rep_times(lambda: step(wl, st, pa), steps, torch, scrub)
+        # Both scatter entry points on this step's new tokens: slots from the
+        # host-side slot_mapping, and slots derived on the GPU from the
+        # block table (pa_scatter_kv_paged).
+        sc_bytes = scatter_work(wl)
+        scat = {}
+        for name, fn in (
+                ("slot_mapping", lambda: pa.pa_scatter_kv(st["k_new"], st["v_new"], st["slots"],
+                                                          st["kc"], st["vc"])),
+                ("paged", lambda: pa.pa_scatter_kv_paged(st["k_new"], st["v_new"], st["cu"],
+                                                         st["lens"], st["table"], st["kc"],
+                                                         st["vc"]))):
+            fn()
+            r = per_rep_times(fn, steps, torch, scrub)
+            r["GBps"] = sc_bytes / (r["median_ms"] * 1e-3) / 1e9
+            scat[name] = r
+        scat["bytes"] = sc_bytes
+        more["scatter"] = scat
         G = wl.num_heads // wl.num_kv_heads
         dec_sel = (wl.q_lens * G <= 16) & (wl.q_lens > 0)
         pf_sel = wl.q_lens * G > 16
@@ -404,6 +421,7 @@ def main():
         "roofline": roof,
         "step_reps": more.get("step_reps"),
         "sub_batches": more.get("sub_batches"),
+        "scatter": more.get("scatter"),
         "extra": extra,
     }
     if not args.no_cpu_baseline:

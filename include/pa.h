@@ -97,6 +97,60 @@ pa_status_t pa_scatter_kv(const void* k_new, const void* v_new,
                           int32_t dtype, void* stream);
 
 /*
+ * pa_scatter_kv_paged - pa_scatter_kv with each new token's slot computed on
+ * the device from the batch metadata instead of a slot_mapping array.
+ *
+ * Defines: "[WebGPU] Initial PagedAttention implementation (1/n)", section
+ * "Description" (the op derives the cache slots of the new tokens from the
+ * cumulative query lengths, the past lengths and the block table) and the
+ * review's checked items (token-to-sequence scan, scatter block
+ * addressing).  For new token t: b = the first sequence with
+ * cu_seqlens_q[b+1] > t; past_b = seqlens_kv[b] - q_len_b;
+ * pos = past_b + (t - cu_seqlens_q[b]);
+ *   s = block_table[b][pos / block_size] * block_size + pos % block_size,
+ * then the copy of pa_scatter_kv.  A negative table entry skips the token.
+ *
+ * k_new, v_new   [num_tokens, num_kv_heads, head_size] dtype, read only.
+ * cu_seqlens_q, seqlens_kv, block_table
+ *                as for pa_attention (same preconditions: past_b >= 0 and
+ *                pos / block_size < max_blocks_per_seq for every token).
+ * k_cache,
+ * v_cache        [num_blocks, block_size, num_kv_heads, head_size], updated
+ *                in place, bit-exact copies.  The slots must not repeat
+ *                (precondition; they do not when the table rows are
+ *                disjoint, as a block manager hands them out).
+ * Limits: as pa_scatter_kv, plus num_seqs >= 1, max_blocks_per_seq >= 1,
+ * max_blocks_per_seq * block_size <= INT32_MAX.  num_tokens == 0 returns
+ * PA_OK without launching.
+ */
+pa_status_t pa_scatter_kv_paged(const void* k_new, const void* v_new,
+                                const int32_t* cu_seqlens_q,
+                                const int32_t* seqlens_kv,
+                                const int32_t* block_table, void* k_cache,
+                                void* v_cache, int32_t num_seqs,
+                                int64_t num_tokens, int32_t max_blocks_per_seq,
+                                int64_t num_blocks, int32_t num_kv_heads,
+                                int32_t head_size, int32_t block_size,
+                                int32_t dtype, void* stream);
+
+/*
+ * pa_seqlens_from_past - total KV lengths from past lengths, on the device:
+ *   seqlens_kv[b] = past_seqlens[b] + (cu_seqlens_q[b+1] - cu_seqlens_q[b]).
+ *
+ * Defines: "[WebGPU] Initial PagedAttention implementation (1/n)", section
+ * "FlashAttention: optional seqlens_q input" (the op receives past lengths;
+ * past_b = total_b - q_len_b).  Lets a caller that holds past lengths feed
+ * pa_scatter_kv_paged and pa_attention, which take total lengths.
+ * cu_seqlens_q [num_seqs + 1], past_seqlens [num_seqs] int32, read only;
+ * seqlens_kv [num_seqs] int32, written (may not alias the inputs).
+ * num_seqs >= 1.
+ */
+pa_status_t pa_seqlens_from_past(const int32_t* cu_seqlens_q,
+                                 const int32_t* past_seqlens,
+                                 int32_t* seqlens_kv, int32_t num_seqs,
+                                 void* stream);
+
+/*
  * pa_attention_workspace_size - bytes of device workspace pa_attention
  * needs for these host-known sizes (an upper bound over every metadata the
  * device could hold).  Returns 0 when the sizes are invalid.
@@ -191,9 +245,10 @@ const char* pa_last_error(void);
  * pa_attention bracket each kernel launch with a pair of HIP events on the
  * caller's stream.  pa_profile_read waits for the recorded events and
  * returns, per kernel kind, the summed milliseconds and launch counts
- * (host arrays of n entries; kinds: 0 scatter, 1 plan, 2 attention (the
- * one launch that runs prefill tiles and split-KV decode items), 3 split-KV
- * combine), then forgets them.  Not for concurrent use.
+ * (host arrays of n entries; kinds: 0 scatter (both scatter entry points),
+ * 1 plan (and pa_seqlens_from_past), 2 attention (the one launch that runs
+ * prefill tiles and split-KV decode items), 3 split-KV combine), then
+ * forgets them.  Not for concurrent use.
  */
 #define PA_PROFILE_KINDS 4
 pa_status_t pa_profile_enable(int32_t enable);

@@ -11,8 +11,9 @@ import ctypes
 
 from ._lib import (PA_BF16, PA_F16, PROFILE_KINDS, PAError, check, lib)  # noqa: F401
 
-__all__ = ["pa_scatter_kv", "pa_attention", "pa_attention_workspace_size",
-           "pa_validate_metadata", "profile_enable", "profile_read", "PAError"]
+__all__ = ["pa_scatter_kv", "pa_scatter_kv_paged", "pa_seqlens_from_past", "pa_attention",
+           "pa_attention_workspace_size", "pa_validate_metadata", "profile_enable",
+           "profile_read", "PAError"]
 
 
 def _dtype_code(t):
@@ -57,6 +58,41 @@ def pa_scatter_kv(k_new, v_new, slot_mapping, k_cache, v_cache, stream=None):
         _dev(k_new, "k_new"), _dev(v_new, "v_new"), _dev(slot_mapping, "slot_mapping", torch.int32),
         _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), T, nb, hk, d, bs,
         _dtype_code(k_cache), _stream_ptr(k_cache, stream)))
+
+
+def pa_scatter_kv_paged(k_new, v_new, cu_seqlens_q, seqlens_kv, block_table, k_cache, v_cache,
+                        stream=None):
+    """pa_scatter_kv with the slots derived on the GPU: token t of sequence b
+    goes to KV position past_b + (t - cu[b]) of b's block-table row."""
+    import torch
+    T, hk, d = k_new.shape
+    nb, bs = k_cache.shape[0], k_cache.shape[1]
+    B = cu_seqlens_q.shape[0] - 1
+    if tuple(v_new.shape) != (T, hk, d) or tuple(k_cache.shape) != (nb, bs, hk, d) \
+            or tuple(v_cache.shape) != (nb, bs, hk, d) or seqlens_kv.shape != (B,) \
+            or block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError("inconsistent shapes")
+    if not (k_new.dtype == v_new.dtype == k_cache.dtype == v_cache.dtype):
+        raise ValueError("K/V and caches must share one dtype")
+    check(lib().pa_scatter_kv_paged(
+        _dev(k_new, "k_new"), _dev(v_new, "v_new"), _dev(cu_seqlens_q, "cu_seqlens_q", torch.int32),
+        _dev(seqlens_kv, "seqlens_kv", torch.int32), _dev(block_table, "block_table", torch.int32),
+        _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), B, T, block_table.shape[1], nb, hk, d,
+        bs, _dtype_code(k_cache), _stream_ptr(k_cache, stream)))
+
+
+def pa_seqlens_from_past(cu_seqlens_q, past_seqlens, out=None, stream=None):
+    """Total KV lengths (int32 [B]) from past lengths: past[b] + q_len_b."""
+    import torch
+    B = cu_seqlens_q.shape[0] - 1
+    if past_seqlens.shape != (B,):
+        raise ValueError("inconsistent shapes")
+    if out is None:
+        out = torch.empty(B, dtype=torch.int32, device=past_seqlens.device)
+    check(lib().pa_seqlens_from_past(
+        _dev(cu_seqlens_q, "cu_seqlens_q", torch.int32), _dev(past_seqlens, "past_seqlens", torch.int32),
+        _dev(out, "out", torch.int32), B, _stream_ptr(out, stream)))
+    return out
 
 
 def pa_attention_workspace_size(num_seqs, num_tokens, max_blocks_per_seq, num_heads,

@@ -21,7 +21,8 @@ PA_F16 = 0
 PA_BF16 = 1
 PROFILE_KINDS = ("scatter", "plan", "attention", "combine")
 
-EXPORTS = ("pa_scatter_kv", "pa_attention_workspace_size", "pa_attention",
+EXPORTS = ("pa_scatter_kv", "pa_scatter_kv_paged", "pa_seqlens_from_past",
+           "pa_attention_workspace_size", "pa_attention",
            "pa_validate_metadata", "pa_status_string", "pa_last_error",
            "pa_profile_enable", "pa_profile_read")
 
@@ -48,6 +49,11 @@ def lib():
                              ctypes.c_float, ctypes.c_size_t)
     L.pa_scatter_kv.argtypes = [vp, vp, vp, vp, vp, i64, i64, i32, i32, i32, i32, vp]
     L.pa_scatter_kv.restype = i32
+    L.pa_scatter_kv_paged.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i64, i32, i32,
+                                      i32, i32, vp]
+    L.pa_scatter_kv_paged.restype = i32
+    L.pa_seqlens_from_past.argtypes = [vp, vp, vp, i32, vp]
+    L.pa_seqlens_from_past.restype = i32
     L.pa_attention_workspace_size.argtypes = [i32, i64, i32, i32, i32, i32, i32]
     L.pa_attention_workspace_size.restype = sz
     L.pa_attention.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i64, f32, i32, i32,

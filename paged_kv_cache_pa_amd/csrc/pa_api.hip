@@ -208,6 +208,56 @@ pa_status_t pa_scatter_kv(const void* k_new, const void* v_new, const int32_t* s
   return PA_OK;
 }
 
+pa_status_t pa_scatter_kv_paged(const void* k_new, const void* v_new, const int32_t* cu_seqlens_q,
+                                const int32_t* seqlens_kv, const int32_t* block_table,
+                                void* k_cache, void* v_cache, int32_t num_seqs,
+                                int64_t num_tokens, int32_t max_blocks_per_seq, int64_t num_blocks,
+                                int32_t num_kv_heads, int32_t head_size, int32_t block_size,
+                                int32_t dtype, void* stream) {
+  g_err[0] = 0;
+  if (dtype != PA_F16 && dtype != PA_BF16)
+    return fail(PA_ERR_NOT_IMPLEMENTED, "dtype=%d (supported: PA_F16, PA_BF16)", dtype);
+  if (num_tokens < 0 || num_tokens > INT32_MAX)
+    return fail(PA_ERR_INVALID_ARGUMENT, "num_tokens outside [0, INT32_MAX]");
+  if (num_seqs < 1 || max_blocks_per_seq < 1)
+    return fail(PA_ERR_INVALID_ARGUMENT, "num_seqs and max_blocks_per_seq must be >= 1");
+  if (num_kv_heads < 1 || head_size < 1 || block_size < 1 || num_blocks < 1)
+    return fail(PA_ERR_INVALID_ARGUMENT, "sizes must be >= 1");
+  if (head_size % 8 != 0)
+    return fail(PA_ERR_NOT_IMPLEMENTED, "head_size=%d is not a multiple of 8", head_size);
+  if (num_blocks * (int64_t)block_size > INT32_MAX)
+    return fail(PA_ERR_NOT_IMPLEMENTED, "num_blocks * block_size exceeds INT32_MAX");
+  if ((int64_t)max_blocks_per_seq * block_size > INT32_MAX)
+    return fail(PA_ERR_NOT_IMPLEMENTED, "max_blocks_per_seq * block_size exceeds INT32_MAX");
+  const int64_t row_bytes = (int64_t)num_kv_heads * head_size * 2;
+  if (row_bytes > INT32_MAX) return fail(PA_ERR_NOT_IMPLEMENTED, "row too large");
+  if (num_tokens == 0) return PA_OK;
+  if (!k_new || !v_new || !cu_seqlens_q || !seqlens_kv || !block_table || !k_cache || !v_cache)
+    return fail(PA_ERR_INVALID_ARGUMENT, "null pointer argument");
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e = timed(0, st, [&] {
+    return pa::launch_scatter_paged(k_new, v_new, cu_seqlens_q, seqlens_kv, block_table, k_cache,
+                                    v_cache, num_seqs, num_tokens, max_blocks_per_seq, block_size,
+                                    (int32_t)row_bytes, st);
+  });
+  if (e != hipSuccess) return hip_fail(e, "scatter launch");
+  return PA_OK;
+}
+
+pa_status_t pa_seqlens_from_past(const int32_t* cu_seqlens_q, const int32_t* past_seqlens,
+                                 int32_t* seqlens_kv, int32_t num_seqs, void* stream) {
+  g_err[0] = 0;
+  if (num_seqs < 1) return fail(PA_ERR_INVALID_ARGUMENT, "num_seqs < 1");
+  if (!cu_seqlens_q || !past_seqlens || !seqlens_kv)
+    return fail(PA_ERR_INVALID_ARGUMENT, "null pointer argument");
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e = timed(1, st, [&] {
+    return pa::launch_seqlens_from_past(cu_seqlens_q, past_seqlens, seqlens_kv, num_seqs, st);
+  });
+  if (e != hipSuccess) return hip_fail(e, "lengths launch");
+  return PA_OK;
+}
+
 size_t pa_attention_workspace_size(int32_t num_seqs, int64_t num_tokens, int32_t max_blocks_per_seq,
                                    int32_t num_heads, int32_t num_kv_heads, int32_t head_size,
                                    int32_t block_size) {

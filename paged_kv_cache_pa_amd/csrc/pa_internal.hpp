@@ -107,6 +107,12 @@ struct AttnArgs {
 
 hipError_t launch_scatter(const void* k_new, const void* v_new, const int32_t* slots, void* kc,
                           void* vc, int64_t num_tokens, int32_t row_bytes, hipStream_t st);
+hipError_t launch_scatter_paged(const void* k_new, const void* v_new, const int32_t* cu,
+                                const int32_t* lens, const int32_t* table, void* kc, void* vc,
+                                int32_t num_seqs, int64_t num_tokens, int32_t max_blocks,
+                                int32_t block_size, int32_t row_bytes, hipStream_t st);
+hipError_t launch_seqlens_from_past(const int32_t* cu, const int32_t* past, int32_t* out,
+                                    int32_t num_seqs, hipStream_t st);
 hipError_t launch_plan(const PlanArgs& a, hipStream_t st);
 // The attention kernel is persistent: one 512-thread work-group per slot the
 // device holds at once.  Work-groups [0, counters[kPrefillFirst]) run prefill

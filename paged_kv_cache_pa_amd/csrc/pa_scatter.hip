@@ -43,4 +43,76 @@ hipError_t launch_scatter(const void* k_new, const void* v_new, const int32_t* s
   return hipGetLastError();
 }
 
+// Scatter with the slots computed on the device from the batch metadata
+// ("[WebGPU] Initial PagedAttention implementation (1/n)", section
+// "Description": the op derives each new token's cache slot from the
+// cumulative query lengths, the past lengths and the block table; the
+// review's checks of the token-to-sequence scan and the scatter block
+// addressing).  One wavefront per new token t: the first sequence b with
+// cu[b+1] > t (binary search, wave-uniform), KV position
+// pos = past_b + (t - cu[b]) with past_b = seqlens_kv[b] - q_len_b, slot =
+// block_table[b][pos / bs] * bs + pos % bs; then the row copy as above.  A
+// negative table entry skips the token.
+__global__ __launch_bounds__(256) void scatter_paged_kernel(
+    const u32x4_t* __restrict__ k_new, const u32x4_t* __restrict__ v_new,
+    const int32_t* __restrict__ cu, const int32_t* __restrict__ lens,
+    const int32_t* __restrict__ table, u32x4_t* __restrict__ kc, u32x4_t* __restrict__ vc,
+    int32_t num_seqs, int64_t num_tokens, int32_t max_blocks, int32_t block_size,
+    int32_t row_chunks) {
+  const int lane = threadIdx.x & 63;
+  const int64_t nwaves = (int64_t)gridDim.x * (blockDim.x >> 6);
+  for (int64_t t = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6); t < num_tokens;
+       t += nwaves) {
+    // first b in [0, num_seqs) with cu[b + 1] > t
+    int lo = 0, hi = num_seqs - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (__builtin_amdgcn_readfirstlane(cu[mid + 1]) > t) hi = mid; else lo = mid + 1;
+    }
+    const int b = lo;
+    const int c0 = __builtin_amdgcn_readfirstlane(cu[b]);
+    const int q_len = __builtin_amdgcn_readfirstlane(cu[b + 1]) - c0;
+    const int past = __builtin_amdgcn_readfirstlane(lens[b]) - q_len;
+    const int pos = past + (int)(t - c0);
+    const int blk = __builtin_amdgcn_readfirstlane(table[(int64_t)b * max_blocks + pos / block_size]);
+    if (blk < 0) continue;
+    const int64_t slot = (int64_t)blk * block_size + pos % block_size;
+    for (int c = lane; c < row_chunks; c += 64) {
+      const int64_t src = t * row_chunks + c;
+      const int64_t dst = slot * row_chunks + c;
+      kc[dst] = k_new[src];
+      vc[dst] = v_new[src];
+    }
+  }
+}
+
+hipError_t launch_scatter_paged(const void* k_new, const void* v_new, const int32_t* cu,
+                                const int32_t* lens, const int32_t* table, void* kc, void* vc,
+                                int32_t num_seqs, int64_t num_tokens, int32_t max_blocks,
+                                int32_t block_size, int32_t row_bytes, hipStream_t st) {
+  int64_t blocks = (num_tokens + 3) / 4;   // 4 waves (tokens) per work-group
+  if (blocks > 16384) blocks = 16384;
+  hipLaunchKernelGGL(scatter_paged_kernel, dim3((unsigned)blocks), dim3(256), 0, st,
+                     (const u32x4_t*)k_new, (const u32x4_t*)v_new, cu, lens, table, (u32x4_t*)kc,
+                     (u32x4_t*)vc, num_seqs, num_tokens, max_blocks, block_size, row_bytes / 16);
+  return hipGetLastError();
+}
+
+// seqlens_kv[b] = past_seqlens[b] + q_len_b: total KV lengths from the past
+// lengths the pages' op takes ("FlashAttention: optional seqlens_q input").
+__global__ __launch_bounds__(256) void seqlens_from_past_kernel(const int32_t* __restrict__ cu,
+                                                                const int32_t* __restrict__ past,
+                                                                int32_t* __restrict__ out,
+                                                                int32_t num_seqs) {
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b < num_seqs) out[b] = past[b] + (cu[b + 1] - cu[b]);
+}
+
+hipError_t launch_seqlens_from_past(const int32_t* cu, const int32_t* past, int32_t* out,
+                                    int32_t num_seqs, hipStream_t st) {
+  hipLaunchKernelGGL(seqlens_from_past_kernel, dim3((unsigned)((num_seqs + 255) / 256)), dim3(256),
+                     0, st, cu, past, out, num_seqs);
+  return hipGetLastError();
+}
+
 }  // namespace pa

@@ -107,3 +107,39 @@ def test_scatter_rejects_on_host(L, kw, status):
 
 def test_scatter_empty_call_is_ok(L):
     assert _scatter(L, T=0, k=None, v=None, slots=None) == _lib.PA_OK
+
+
+def _scatter_paged(L, **kw):
+    a = dict(k=FAKE, v=FAKE, cu=FAKE, lens=FAKE, table=FAKE, kc=FAKE, vc=FAKE, B=2, T=5, MB=2,
+             NB=8, hk=2, d=64, bs=16, dtype=0)
+    a.update(kw)
+    return L.pa_scatter_kv_paged(a["k"], a["v"], a["cu"], a["lens"], a["table"], a["kc"], a["vc"],
+                                 a["B"], a["T"], a["MB"], a["NB"], a["hk"], a["d"], a["bs"],
+                                 a["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(d=60), _lib.PA_ERR_NOT_IMPLEMENTED),
+    (dict(dtype=2), _lib.PA_ERR_NOT_IMPLEMENTED),
+    (dict(T=-1), _lib.PA_ERR_INVALID_ARGUMENT),
+    (dict(B=0), _lib.PA_ERR_INVALID_ARGUMENT),
+    (dict(MB=0), _lib.PA_ERR_INVALID_ARGUMENT),
+    (dict(hk=0), _lib.PA_ERR_INVALID_ARGUMENT),
+    (dict(cu=None), _lib.PA_ERR_INVALID_ARGUMENT),
+    (dict(table=None), _lib.PA_ERR_INVALID_ARGUMENT),
+    (dict(NB=1 << 30, bs=16), _lib.PA_ERR_NOT_IMPLEMENTED),
+    (dict(MB=1 << 28, bs=16), _lib.PA_ERR_NOT_IMPLEMENTED),
+])
+def test_scatter_paged_rejects_on_host(L, kw, status):
+    assert _scatter_paged(L, **kw) == status
+    assert L.pa_last_error() != b""
+
+
+def test_scatter_paged_empty_call_is_ok(L):
+    assert _scatter_paged(L, T=0, k=None, v=None) == _lib.PA_OK
+
+
+def test_seqlens_from_past_rejects_on_host(L):
+    assert L.pa_seqlens_from_past(FAKE, FAKE, FAKE, 0, None) == _lib.PA_ERR_INVALID_ARGUMENT
+    assert L.pa_seqlens_from_past(FAKE, None, FAKE, 3, None) == _lib.PA_ERR_INVALID_ARGUMENT
+    assert L.pa_seqlens_from_past(FAKE, FAKE, None, 3, None) == _lib.PA_ERR_INVALID_ARGUMENT

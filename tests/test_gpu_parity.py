@@ -12,7 +12,7 @@ import torch
 import oracle
 import paged_kv_cache_pa_amd as pa
 from paged_kv_cache_pa_amd import workloads as W
-from gpu_util import (NAN_BITS, TOL, device_inputs, max_err, oracle_full, oracle_rows,
+from gpu_util import (NAN_BITS, TOL, device_inputs, max_err, nan_cache, oracle_full, oracle_rows,
                       require_gpu, run_attention)
 from pa_testutil import embed_flex_example, load_golden, to_np64
 
@@ -86,6 +86,90 @@ def test_scatter_bit_exact_large(idx):
     free = np.flatnonzero(~used)
     for x in free[:: max(1, len(free) // 8)][:8]:
         assert (_bits(d["kc"][int(x)]) == NAN_BITS).all()
+
+
+def _new_token_values(wl, vals):
+    rows = torch.from_numpy(wl.new_rows).to(vals["k_all"].device)
+    return vals["k_all"][rows].contiguous(), vals["v_all"][rows].contiguous()
+
+
+@pytest.mark.parametrize("make", [W.tiny, lambda: W.small((16, 4), (64, 32), 8, 2),
+                                  lambda: W.custom([3, 0, 1, 7], [40, 5, 1, 300], 8, 2, 128, 16,
+                                                   dtype="bf16")])
+def test_scatter_paged_bit_exact_small(make):
+    """Slots derived on the GPU from (cu_seqlens_q, seqlens_kv, block_table)
+    write exactly the bytes the oracle's in-op addressing says, into
+    NaN-filled caches; a negative table entry skips its tokens."""
+    wl = make()
+    _log(f"scatter paged: {wl.name}")
+    require_gpu()
+    vals = {k: v.cuda() for k, v in W.make_values(wl).items()}
+    k_new, v_new = _new_token_values(wl, vals)
+    table = wl.block_table.astype(np.int32).copy()
+    # Drop the block of the first new token of the last non-empty sequence.
+    b_last = int(np.flatnonzero(wl.q_lens > 0)[-1])
+    pos0 = int(wl.seqlens_kv[b_last] - wl.q_lens[b_last])
+    table[b_last, pos0 // wl.block_size] = -1
+    slots = oracle.slots_from_block_table(wl.cu_seqlens_q, wl.seqlens_kv, table, wl.block_size)
+    shape = (wl.num_blocks, wl.block_size, wl.num_kv_heads, wl.head_size)
+    kref = np.full(shape, NAN_BITS, dtype=np.uint16)
+    vref = np.full(shape, NAN_BITS, dtype=np.uint16)
+    slots[slots < 0] = -1    # tokens whose table entry is negative are skipped
+    oracle.scatter_kv(_bits(k_new), _bits(v_new), slots, kref, vref, wl.block_size)
+    kc, vc = nan_cache(wl), nan_cache(wl)
+    pa.pa_scatter_kv_paged(k_new, v_new, torch.from_numpy(wl.cu_seqlens_q).cuda(),
+                           torch.from_numpy(wl.seqlens_kv.astype(np.int32)).cuda(),
+                           torch.from_numpy(table).cuda(), kc, vc)
+    torch.cuda.synchronize()
+    assert np.array_equal(_bits(kc), kref)
+    assert np.array_equal(_bits(vc), vref)
+
+
+@pytest.mark.parametrize("idx", [3, 5])
+def test_scatter_paged_large(idx):
+    """Multi-GB pools: the device-derived slots land where the slot-mapping
+    scatter puts the same tokens (sign-flipped values over the filled
+    cache), bit for bit on sampled sequences' blocks."""
+    wl = W.by_index(idx)
+    _log(f"scatter paged: {wl.name}")
+    d = device_inputs(wl, backend="torch")
+    k_new, v_new = _new_token_values(wl, d)
+    k_neg = (k_new.view(torch.int16) ^ -0x8000).view(k_new.dtype)   # sign bit flipped
+    v_neg = (v_new.view(torch.int16) ^ -0x8000).view(v_new.dtype)
+    pa.pa_scatter_kv_paged(k_neg, v_neg, d["cu"], d["lens"], d["table"], d["kc"], d["vc"])
+    torch.cuda.synchronize()
+    slots = oracle.slots_from_block_table(wl.cu_seqlens_q, wl.seqlens_kv, wl.block_table,
+                                          wl.block_size)
+    assert np.array_equal(slots, wl.slot_mapping.astype(np.int64))
+    rng = np.random.default_rng(100 + idx)
+    seqs = [int(x) for x in rng.choice(np.flatnonzero(wl.q_lens > 0), size=4, replace=False)]
+    kv_cu, cu = wl.kv_cu, wl.cu_seqlens_q
+    shape = (wl.block_size, wl.num_kv_heads, wl.head_size)
+    kb_new, vb_new = _bits(k_neg), _bits(v_neg)
+    for b in seqs:
+        nb = -(-int(wl.seqlens_kv[b]) // wl.block_size)
+        blocks = [int(x) for x in wl.block_table[b, :nb]]
+        kref = {x: np.full(shape, NAN_BITS, dtype=np.uint16) for x in blocks}
+        vref = {x: np.full(shape, NAN_BITS, dtype=np.uint16) for x in blocks}
+        oracle.scatter_kv(_bits(d["k_all"][kv_cu[b]:kv_cu[b + 1]]),
+                          _bits(d["v_all"][kv_cu[b]:kv_cu[b + 1]]),
+                          wl.kv_slots[kv_cu[b]:kv_cu[b + 1]], kref, vref, wl.block_size)
+        oracle.scatter_kv(kb_new[cu[b]:cu[b + 1]], vb_new[cu[b]:cu[b + 1]], slots[cu[b]:cu[b + 1]],
+                          kref, vref, wl.block_size)
+        for x in blocks:
+            assert np.array_equal(_bits(d["kc"][x]), kref[x]), (b, x)
+            assert np.array_equal(_bits(d["vc"][x]), vref[x]), (b, x)
+
+
+def test_seqlens_from_past():
+    require_gpu()
+    rng = np.random.default_rng(7)
+    q_lens = rng.integers(0, 40, size=3000).astype(np.int32)
+    past = rng.integers(0, 100000, size=3000).astype(np.int32)
+    cu = np.concatenate([[0], np.cumsum(q_lens)]).astype(np.int32)
+    out = pa.pa_seqlens_from_past(torch.from_numpy(cu).cuda(), torch.from_numpy(past).cuda())
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy(), past + q_lens)
 
 
 # ---------------------------------------------------------------- attention
