@@ -197,7 +197,7 @@ size_t pa_attention_workspace_size(int32_t num_seqs, int64_t num_tokens,
  *              are scratch (plan lists, split-KV partial results).
  * Limits: head_size in {64, 128}; block_size a power of two in [16, 1024];
  * num_heads % num_kv_heads == 0 with G <= 128; num_blocks * block_size
- * <= INT32_MAX; max_blocks_per_seq * block_size <= 131072 tokens;
+ * <= INT32_MAX; max_blocks_per_seq * block_size <= 262144 tokens;
  * num_seqs <= 65536.  Other shapes return PA_ERR_NOT_IMPLEMENTED.
  * num_tokens == 0 returns PA_OK without launching.
  */

@@ -12,7 +12,7 @@
 //
 // Work item = (sequence b, split s, KV head kh), one wavefront each, fetched
 // from a device counter.  The wave walks 16-key chunks of keys
-// [s*512, min(L, (s+1)*512)) through the block table (the split's block ids
+// [s*S, min(L, (s+1)*S)), S = kSplitKeys, through the block table (the split's block ids
 // are prefetched into one VGPR and broadcast per chunk with readlane).  The
 // G query heads of kh (times q_len tokens) are the 16 columns n = i*G + g of
 // the score tile, so every K/V byte is read from HBM exactly once per call.

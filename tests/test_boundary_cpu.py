@@ -75,7 +75,7 @@ def _attn(L, **kw):
     (dict(ws=ctypes.c_void_p(0x1010), wsb=1 << 30), _lib.PA_ERR_INVALID_ARGUMENT),  # unaligned
     (dict(wsb=16), _lib.PA_ERR_WORKSPACE_TOO_SMALL),
     (dict(NB=1 << 28, bs=16), _lib.PA_ERR_NOT_IMPLEMENTED),   # slots beyond int32
-    (dict(MB=8193, bs=16), _lib.PA_ERR_NOT_IMPLEMENTED),      # context beyond 131072 tokens
+    (dict(MB=16385, bs=16), _lib.PA_ERR_NOT_IMPLEMENTED),     # context beyond 262144 tokens
 ])
 def test_attention_rejects_on_host(L, kw, status):
     assert _attn(L, **kw) == status

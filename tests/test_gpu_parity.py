@@ -333,7 +333,7 @@ EDGE = [
     # (q_lens, total kv, Hq, Hk, D, block size, dtype)
     ([1], [1], 4, 4, 64, 16, "f16"),
     ([0, 3, 0, 1], [5, 3, 0, 9], 8, 2, 64, 16, "f16"),            # empty sequences
-    ([1, 1, 1], [512, 513, 1024], 32, 8, 128, 16, "f16"),         # split boundaries
+    ([1, 1, 1, 1, 1], [512, 513, 1024, 1025, 2048], 32, 8, 128, 16, "f16"),   # split boundaries
     ([1, 1], [1, 4097], 64, 8, 128, 16, "bf16"),
     ([4, 2, 16], [1500, 2, 16], 16, 4, 128, 32, "f16"),           # q_len*G = 16 decode path
     ([5, 17], [1600, 17], 16, 4, 128, 64, "bf16"),                # q_len*G > 16 prefill path
