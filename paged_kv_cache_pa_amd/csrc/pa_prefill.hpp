@@ -223,6 +223,14 @@ __device__ __forceinline__ void prefill_items(const AttnArgs& a) {
       if (n > 1) issue(1, block_of(1));
       int blk_next = n > 2 ? block_of(2) : 0;
       wait_vmcnt<0>();
+      // The wait above is opaque to the compiler, which would otherwise
+      // still count the Q loads as in flight and guard their first use in
+      // every tile with a full vmcnt(0) (waiting for the tile copies too).
+      // Passing the operands through an empty asm marks them as ready.
+#pragma unroll
+      for (int rho = 0; rho < NR; ++rho)
+#pragma unroll
+        for (int s = 0; s < NS; ++s) asm volatile("" : "+v"(qreg[rho][s]));
       __syncthreads();
 
       // acc += P_t V_t with V of tile t (buffer t % 4).
@@ -383,13 +391,16 @@ __device__ __forceinline__ void prefill_items(const AttnArgs& a) {
       const int nw = wave_kmax < 0 ? 0 : min(n, wave_kmax / BN + 1);
       const int nd = c > 0.f ? min(nw, (wave_kmin + 1) / BN) : 0;
 
-      // Issued at the start of tick 2i by every wave: request tile i+2 and
-      // fetch the block id of tile i+3 (a scalar load, used next tick pair).
+      // Issued at the start of tick 2i by every wave: request tile i+2.
       auto even_service = [&](int i) {
-        if (i + 2 < n) {
-          issue(i + 2, blk_next);
-          blk_next = i + 3 < n ? block_of(i + 3) : 0;
-        }
+        if (i + 2 < n) issue(i + 2, blk_next);
+      };
+      // Block id of tile i+3 (a scalar load, first used at tick 2i+2), read
+      // at the start of the wave's softmax phase: that phase has no LDS reads
+      // and hides the load, whereas an SMEM load in flight during the
+      // matrix-core phase would turn its LDS waits into full lgkmcnt drains.
+      auto fetch_service = [&](int i) {
+        if (i + 3 < n) blk_next = block_of(i + 3);
       };
       // Run at the end of tick 2i+1 by every wave, before its barrier: all
       // copies but tile i+2's have landed, so tile i+1 is complete.
@@ -412,6 +423,7 @@ __device__ __forceinline__ void prefill_items(const AttnArgs& a) {
           __builtin_amdgcn_sched_barrier(0);
           qk(i);
           __syncthreads();
+          fetch_service(i);
           softmax(i, Plain{});
           odd_service(i);
           __syncthreads();
@@ -422,6 +434,7 @@ __device__ __forceinline__ void prefill_items(const AttnArgs& a) {
           __builtin_amdgcn_sched_barrier(0);
           qk(i);
           __syncthreads();
+          fetch_service(i);
           softmax(i, Masked{});
           odd_service(i);
           __syncthreads();
@@ -430,33 +443,55 @@ __device__ __forceinline__ void prefill_items(const AttnArgs& a) {
           even_service(i);
           if (i == nw && i > 0) pv(i - 1);
           __syncthreads();
+          fetch_service(i);
           odd_service(i);
           __syncthreads();
         }
       } else {
-        int i = 0;
-        for (; i <= nd; ++i) {   // V_{i-1} plain (if any), then M_i
+        // Tick pair 0: M_0 = QK^T of tile 0 only.
+        even_service(0);
+        fetch_service(0);
+        __syncthreads();
+        if (nw > 0) qk(0);
+        odd_service(0);
+        __syncthreads();
+        int i = 1;
+        const int np = min(nd + 1, nw);
+        for (; i < np; ++i) {    // V_{i-1} plain, then M_i
           even_service(i);
-          if (i > 0) softmax(i - 1, Plain{});
+          fetch_service(i);
+          softmax(i - 1, Plain{});
           __syncthreads();
-          if (i > 0) pv(i - 1);
+          pv(i - 1);
           __builtin_amdgcn_sched_barrier(0);
-          if (i < nw) qk(i);
+          qk(i);
           odd_service(i);
           __syncthreads();
         }
-        for (; i <= nw; ++i) {   // V_{i-1} masked, then M_i
+        for (; i < nw; ++i) {    // V_{i-1} masked, then M_i
           even_service(i);
+          fetch_service(i);
           softmax(i - 1, Masked{});
           __syncthreads();
           pv(i - 1);
           __builtin_amdgcn_sched_barrier(0);
-          if (i < nw) qk(i);
+          qk(i);
           odd_service(i);
           __syncthreads();
         }
+        if (i == nw && nw > 0) { // V_{nw-1} (the mask is a no-op on a plain tile), P.V only
+          even_service(i);
+          fetch_service(i);
+          softmax(i - 1, Masked{});
+          __syncthreads();
+          pv(i - 1);
+          odd_service(i);
+          __syncthreads();
+          ++i;
+        }
         for (; i <= n; ++i) {
           even_service(i);
+          fetch_service(i);
           __syncthreads();
           odd_service(i);
           __syncthreads();
