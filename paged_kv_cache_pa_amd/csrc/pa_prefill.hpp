@@ -63,8 +63,9 @@ __device__ inline void wait_vmcnt() {
 }
 
 // K/V tiles live in LDS as unpadded rows of D halfs whose 16-byte chunks are
-// XOR-swizzled by the row index (see slot()), which keeps both the row-wise
-// K reads and the transposed V reads free of bank conflicts.  Tiles are
+// XOR-swizzled by the row index, with one swizzle per operand so that both
+// the row-wise K reads (kslot()) and the transposed V reads (slot()) are free
+// of bank conflicts.  Tiles are
 // filled by global_load_lds_dwordx4 (HBM/L2 -> LDS without registers) into a
 // ring of four buffers; tile i+2 is requested four barrier ticks before it
 // is first read.
@@ -112,13 +113,20 @@ __device__ __forceinline__ void prefill_items(const AttnArgs& a) {
   uint16_t* __restrict__ op = (uint16_t*)a.out;
   const int home = blockIdx.x % kQueues;
 
-  // Slot of 16-byte chunk `chunk` of tile row `row`: XOR with the row's low
-  // log2(CPR) bits rotated left by one.  Row-wise K reads (16 rows, one
-  // chunk) and transposed V reads (4 rows, two adjacent chunks) then touch
-  // distinct slots.
+  // Slot of 16-byte chunk `chunk` of V row `row`: XOR with the row's low
+  // log2(CPR) bits rotated left by one, so the transposed reads (4 rows,
+  // two adjacent chunks) touch distinct slots.
   constexpr int CB = CPR == 16 ? 4 : 3;
   auto swz = [](int row) { return ((row << 1) | ((row >> (CB - 1)) & 1)) & (CPR - 1); };
   auto slot = [&](int row, int chunk) { return row * ROWB + ((chunk ^ swz(row)) << 4); };
+  // Slot of 16-byte chunk `chunk` of K row `row`.  A QK^T operand read puts
+  // 16 lanes on 16 consecutive rows at one chunk; the LDS serves 16 lanes of
+  // a 128-bit read per pass over 64 four-byte banks, so those 16 slots must
+  // differ in their bank group: XOR with row & 15 for 256-byte rows; for
+  // 128-byte rows, rows of equal parity share bank halves, so (row >> 1) & 7.
+  // (The V swizzle above leaves this read 2-way conflicted.)
+  auto kswz = [](int row) { return CPR == 16 ? (row & 15) : ((row >> 1) & 7); };
+  auto kslot = [&](int row, int chunk) { return row * ROWB + ((chunk ^ kswz(row)) << 4); };
 
   for (int qi = 0; qi < kQueues; ++qi) {
     const int x = (home + qi) % kQueues;
@@ -163,9 +171,10 @@ __device__ __forceinline__ void prefill_items(const AttnArgs& a) {
         for (int p = 0; p < LPW; ++p) {
           const int row = RPW * wave + p * RPI + ln / CPR;
           const int j = min(t * BN + row, kend - 1);
-          const int gch = (ln % CPR) ^ swz(row);
-          const uint32_t voff = (uint32_t)(((j & (bsz - 1)) * (int)row_stride + gch * 8) * 2);
-          lds_dma16(kbase, voff, kdst + p * 1024);
+          const int rof = (j & (bsz - 1)) * (int)row_stride;
+          const uint32_t koff = (uint32_t)((rof + ((ln % CPR) ^ kswz(row)) * 8) * 2);
+          const uint32_t voff = (uint32_t)((rof + ((ln % CPR) ^ swz(row)) * 8) * 2);
+          lds_dma16(kbase, koff, kdst + p * 1024);
           lds_dma16(vbase, voff, kdst + TB + p * 1024);
         }
       };
@@ -246,7 +255,7 @@ __device__ __forceinline__ void prefill_items(const AttnArgs& a) {
           const int r4 = (lane & 15) >> 2, q4 = lane & 3, vk = kq;
           // Operands in groups of VG (u, t .. t+VG-1); group g+1 is read while
           // group g feeds its MFMAs (two register sets, fenced as in qk).
-          constexpr int VG = 2;
+          constexpr int VG = 4;
           constexpr int NG = (NK / 2) * NT / VG;
           auto vread = [&](int u, int t) {
             const int R0 = 32 * u + 4 * vk + r4;
@@ -296,14 +305,14 @@ __device__ __forceinline__ void prefill_items(const AttnArgs& a) {
         u32x4_t ka[2][NS];
 #pragma unroll
         for (int s = 0; s < NS; ++s)
-          ka[0][s] = *reinterpret_cast<const u32x4_t*>(kb + slot(kr, 4 * s + kk));
+          ka[0][s] = *reinterpret_cast<const u32x4_t*>(kb + kslot(kr, 4 * s + kk));
 #pragma unroll
         for (int kap = 0; kap < NK; ++kap) {
           if (kap + 1 < NK) {
 #pragma unroll
             for (int s = 0; s < NS; ++s)
               ka[(kap + 1) & 1][s] =
-                  *reinterpret_cast<const u32x4_t*>(kb + slot(16 * (kap + 1) + kr, 4 * s + kk));
+                  *reinterpret_cast<const u32x4_t*>(kb + kslot(16 * (kap + 1) + kr, 4 * s + kk));
           }
           __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
