@@ -295,17 +295,24 @@ __device__ __forceinline__ void prefill_items(const AttnArgs& a) {
       // S = K_t Q^T with K of tile t.  The K operands of 16-key group kap+1
       // are read while group kap feeds its MFMAs (two register sets; the
       // fences keep each group's reads a group ahead of their use, so the
-      // LDS latency hides under the previous group's 8 MFMAs).
+      // LDS latency hides under the previous group's 8 MFMAs).  Group 0's
+      // operands are read by qk_first, which the matrix-core phase issues
+      // before its P.V, so their latency hides under the P.V MFMAs.
+      u32x4_t ka[2][NS];
+      auto qk_first = [&](int t) {
+        const unsigned char* kb = lds + (t % NB) * 2 * TB;
+        const int ln = lane_here();
+        const int kr = ln & 15, kk = ln >> 4;
+#pragma unroll
+        for (int s = 0; s < NS; ++s)
+          ka[0][s] = *reinterpret_cast<const u32x4_t*>(kb + kslot(kr, 4 * s + kk));
+      };
       auto qk = [&](int t) {
         const unsigned char* kb = lds + (t % NB) * 2 * TB;
         // Per-lane K read offsets recomputed here (a few VALU ops per tile)
         // rather than held across the tile loop.
         const int ln = lane_here();
         const int kr = ln & 15, kk = ln >> 4;
-        u32x4_t ka[2][NS];
-#pragma unroll
-        for (int s = 0; s < NS; ++s)
-          ka[0][s] = *reinterpret_cast<const u32x4_t*>(kb + kslot(kr, 4 * s + kk));
 #pragma unroll
         for (int kap = 0; kap < NK; ++kap) {
           if (kap + 1 < NK) {
@@ -400,7 +407,10 @@ __device__ __forceinline__ void prefill_items(const AttnArgs& a) {
       const int nw = wave_kmax < 0 ? 0 : min(n, wave_kmax / BN + 1);
       const int nd = c > 0.f ? min(nw, (wave_kmin + 1) / BN) : 0;
 
-      // Issued at the start of tick 2i by every wave: request tile i+2.
+      // Request tile i+2: issued by each wave at the start of its softmax
+      // phase (group B: tick 2i, group A: tick 2i+1).  Issuing 32 copies at
+      // once can stall the issuing waves until the address unit drains them,
+      // which must not happen in a matrix-core phase.
       auto even_service = [&](int i) {
         if (i + 2 < n) issue(i + 2, blk_next);
       };
@@ -417,9 +427,10 @@ __device__ __forceinline__ void prefill_items(const AttnArgs& a) {
         if (i + 2 < n) wait_vmcnt<2 * LPW>(); else wait_vmcnt<0>();
       };
 
-      // Tick pair i (ticks 2i and 2i+1): tick 2i requests tile i+2; tick
-      // 2i+1 ends with tile i+1 complete.  Tile t lives in ring buffer t % 4:
-      // tile i+2 overwrites tile i-2, whose V was last read at tick 2i-1.
+      // Tick pair i (ticks 2i and 2i+1): ticks 2i and 2i+1 request tile i+2;
+      // tick 2i+1 ends with tile i+1 complete.  Tile t lives in ring buffer
+      // t % 4: tile i+2 overwrites tile i-2, whose V was last read at tick
+      // 2i-1.
       // Group A runs M_i = {P.V of tile i-1, QK^T of tile i} at tick 2i and
       // the softmax V_i at tick 2i+1; group B runs V_{i-1} at tick 2i and
       // M_i at tick 2i+1.  Both pass the same 2(n+1) barriers; the loops are
@@ -427,31 +438,35 @@ __device__ __forceinline__ void prefill_items(const AttnArgs& a) {
       if (grp == 0) {
         int i = 0;
         for (; i < nd; ++i) {
-          even_service(i);
+          qk_first(i);
+          __builtin_amdgcn_sched_barrier(0);
           if (i > 0) pv(i - 1);
           __builtin_amdgcn_sched_barrier(0);
           qk(i);
           __syncthreads();
+          even_service(i);
           fetch_service(i);
           softmax(i, Plain{});
           odd_service(i);
           __syncthreads();
         }
         for (; i < nw; ++i) {
-          even_service(i);
+          qk_first(i);
+          __builtin_amdgcn_sched_barrier(0);
           if (i > 0) pv(i - 1);
           __builtin_amdgcn_sched_barrier(0);
           qk(i);
           __syncthreads();
+          even_service(i);
           fetch_service(i);
           softmax(i, Masked{});
           odd_service(i);
           __syncthreads();
         }
         for (; i <= n; ++i) {
-          even_service(i);
           if (i == nw && i > 0) pv(i - 1);
           __syncthreads();
+          even_service(i);
           fetch_service(i);
           odd_service(i);
           __syncthreads();
@@ -461,7 +476,10 @@ __device__ __forceinline__ void prefill_items(const AttnArgs& a) {
         even_service(0);
         fetch_service(0);
         __syncthreads();
-        if (nw > 0) qk(0);
+        if (nw > 0) {
+          qk_first(0);
+          qk(0);
+        }
         odd_service(0);
         __syncthreads();
         int i = 1;
@@ -471,6 +489,8 @@ __device__ __forceinline__ void prefill_items(const AttnArgs& a) {
           fetch_service(i);
           softmax(i - 1, Plain{});
           __syncthreads();
+          qk_first(i);
+          __builtin_amdgcn_sched_barrier(0);
           pv(i - 1);
           __builtin_amdgcn_sched_barrier(0);
           qk(i);
@@ -482,6 +502,8 @@ __device__ __forceinline__ void prefill_items(const AttnArgs& a) {
           fetch_service(i);
           softmax(i - 1, Masked{});
           __syncthreads();
+          qk_first(i);
+          __builtin_amdgcn_sched_barrier(0);
           pv(i - 1);
           __builtin_amdgcn_sched_barrier(0);
           qk(i);
