@@ -212,6 +212,73 @@ pa_status_t pa_attention(const void* q, const int32_t* cu_seqlens_q,
                          void* stream);
 
 /*
+ * pa_scatter_kv_fp8 - pa_scatter_kv into fp8 caches: each new K/V element is
+ * quantized to an 8-bit float with a per-(KV head, channel) scale.
+ *
+ * Defines: the quantized KV cache of "[WebGPU] Initial PagedAttention
+ * implementation (1/n)", section "Roadmap" (phase 3: a cache element type
+ * apart from the query type, quantized KV first).  The page fixes no
+ * format; this library's reading: cache elements are OCP e4m3 (4 exponent
+ * bits, bias 7, 3 mantissa bits, largest finite 448, no infinities) and
+ *   code(x) = e4m3_round(sat(fp32(x) * fp32(1 / scale[h][d])))
+ * with 1/scale and the product rounded to float32, sat() clamping
+ * magnitudes above 448 (infinities included) to 448, and e4m3_round()
+ * rounding to the nearest e4m3 value, ties to the even mantissa (a NaN
+ * input gives a NaN code).  Element value on read: e4m3(code) * scale.
+ *
+ * k_new, v_new   [num_tokens, num_kv_heads, head_size] dtype, read only.
+ * slot_mapping   [num_tokens] int32, as for pa_scatter_kv.
+ * k_scale,
+ * v_scale        [num_kv_heads, head_size] float32, read only; finite and
+ *                > 0 (precondition).
+ * k_cache,
+ * v_cache        [num_blocks, block_size, num_kv_heads, head_size] uint8
+ *                e4m3 codes, updated in place.
+ * Limits and empty calls as for pa_scatter_kv.  Bit-exact with the
+ * definition above.
+ */
+pa_status_t pa_scatter_kv_fp8(const void* k_new, const void* v_new,
+                              const int32_t* slot_mapping, const float* k_scale,
+                              const float* v_scale, void* k_cache, void* v_cache,
+                              int64_t num_tokens, int64_t num_blocks,
+                              int32_t num_kv_heads, int32_t head_size,
+                              int32_t block_size, int32_t dtype, void* stream);
+
+/*
+ * pa_attention_fp8 - pa_attention over fp8 caches written by
+ * pa_scatter_kv_fp8, for decode-shaped batches.
+ *
+ * Defines: pa_attention's result with K_j and V_j replaced by their
+ * dequantized values e4m3(code) * scale[h / G][d] (section "Roadmap" of
+ * the PagedAttention page, phase 3, quantized KV in the decode path).
+ *
+ * Arguments as for pa_attention, plus:
+ * k_cache,
+ * v_cache      [num_blocks, block_size, num_kv_heads, head_size] uint8
+ *              e4m3 codes; read only.
+ * k_scale,
+ * v_scale      [num_kv_heads, head_size] float32, read only.
+ * max_q_len    host-known upper bound of every q_len_b; max_q_len * G must
+ *              be <= 16 (one decode tile of query columns: decode steps and
+ *              short speculative chunks), else PA_ERR_NOT_IMPLEMENTED.  A
+ *              sequence whose q_len_b * G exceeds 16 despite the bound
+ *              (precondition violation) gets no work: its output rows are
+ *              left unwritten.
+ * workspace    at least pa_attention_workspace_size(...) bytes, as for
+ *              pa_attention.
+ * Other limits, status codes and empty calls as for pa_attention.
+ */
+pa_status_t pa_attention_fp8(const void* q, const int32_t* cu_seqlens_q,
+                             const int32_t* seqlens_kv, const int32_t* block_table,
+                             const void* k_cache, const void* v_cache,
+                             const float* k_scale, const float* v_scale, void* out,
+                             int32_t num_seqs, int64_t num_tokens, int32_t max_q_len,
+                             int32_t max_blocks_per_seq, int64_t num_blocks,
+                             float scale, int32_t num_heads, int32_t num_kv_heads,
+                             int32_t head_size, int32_t block_size, int32_t dtype,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * pa_validate_metadata - debug/test check of the device metadata that
  * pa_attention / pa_scatter_kv trust.  Copies the arrays to the host
  * (synchronising `stream`) and writes a bit mask of violations to
@@ -241,14 +308,15 @@ const char* pa_status_string(int32_t status);
 const char* pa_last_error(void);
 
 /*
- * Kernel timing for measurement tools.  While enabled, pa_scatter_kv and
- * pa_attention bracket each kernel launch with a pair of HIP events on the
- * caller's stream.  pa_profile_read waits for the recorded events and
- * returns, per kernel kind, the summed milliseconds and launch counts
- * (host arrays of n entries; kinds: 0 scatter (both scatter entry points),
- * 1 plan (and pa_seqlens_from_past), 2 attention (the one launch that runs
- * prefill tiles and split-KV decode items), 3 split-KV combine), then
- * forgets them.  Not for concurrent use.
+ * Kernel timing for measurement tools.  While enabled, the scatter and
+ * attention entry points bracket each kernel launch with a pair of HIP
+ * events on the caller's stream.  pa_profile_read waits for the recorded
+ * events and returns, per kernel kind, the summed milliseconds and launch
+ * counts (host arrays of n entries; kinds: 0 scatter (all three scatter
+ * entry points), 1 plan (and pa_seqlens_from_past), 2 attention (the one
+ * launch that runs prefill tiles and split-KV decode items; the fp8 launch
+ * of pa_attention_fp8), 3 split-KV combine), then forgets them.  Not for
+ * concurrent use.
  */
 #define PA_PROFILE_KINDS 4
 pa_status_t pa_profile_enable(int32_t enable);

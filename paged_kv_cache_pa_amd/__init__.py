@@ -11,7 +11,8 @@ import ctypes
 
 from ._lib import (PA_BF16, PA_F16, PROFILE_KINDS, PAError, check, lib)  # noqa: F401
 
-__all__ = ["pa_scatter_kv", "pa_scatter_kv_paged", "pa_seqlens_from_past", "pa_attention",
+__all__ = ["pa_scatter_kv", "pa_scatter_kv_paged", "pa_scatter_kv_fp8", "pa_seqlens_from_past",
+           "pa_attention", "pa_attention_fp8",
            "pa_attention_workspace_size", "pa_validate_metadata", "profile_enable",
            "profile_read", "PAError"]
 
@@ -137,6 +138,64 @@ def pa_attention(q, cu_seqlens_q, seqlens_kv, block_table, k_cache, v_cache, sca
         float(scale), num_heads, num_kv_heads, d, bs, _dtype_code(q),
         _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
         _stream_ptr(q, stream)))
+    return out
+
+
+def pa_scatter_kv_fp8(k_new, v_new, slot_mapping, k_scale, v_scale, k_cache, v_cache,
+                      stream=None):
+    """Quantize new K/V rows [T, Hk, D] (fp16/bf16) into fp8 (e4m3) caches
+    [NB, bs, Hk, D] (uint8 codes) with float32 per-channel scales [Hk, D], at
+    int32 ``slot_mapping`` [T] (negative = skip), in place."""
+    import torch
+    T, hk, d = k_new.shape
+    nb, bs = k_cache.shape[0], k_cache.shape[1]
+    if tuple(v_new.shape) != (T, hk, d) or tuple(k_cache.shape) != (nb, bs, hk, d) \
+            or tuple(v_cache.shape) != (nb, bs, hk, d) or slot_mapping.shape != (T,) \
+            or tuple(k_scale.shape) != (hk, d) or tuple(v_scale.shape) != (hk, d):
+        raise ValueError("inconsistent shapes")
+    if k_new.dtype != v_new.dtype or k_cache.dtype != torch.uint8 or v_cache.dtype != torch.uint8:
+        raise ValueError("K/V share one 16-bit dtype; the caches hold uint8 codes")
+    check(lib().pa_scatter_kv_fp8(
+        _dev(k_new, "k_new"), _dev(v_new, "v_new"), _dev(slot_mapping, "slot_mapping", torch.int32),
+        _dev(k_scale, "k_scale", torch.float32), _dev(v_scale, "v_scale", torch.float32),
+        _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), T, nb, hk, d, bs,
+        _dtype_code(k_new), _stream_ptr(k_cache, stream)))
+
+
+def pa_attention_fp8(q, cu_seqlens_q, seqlens_kv, block_table, k_cache, v_cache, k_scale,
+                     v_scale, scale, num_heads, num_kv_heads, max_q_len, out=None,
+                     workspace=None, stream=None):
+    """pa_attention over fp8 (e4m3) caches [NB, bs, Hk, D] (uint8 codes) with
+    float32 per-channel scales [Hk, D], for batches whose every q_len * G is
+    at most 16 (``max_q_len`` is a host-side bound of q_len)."""
+    import torch
+    T = q.shape[0]
+    d = k_cache.shape[-1]
+    nb, bs = k_cache.shape[0], k_cache.shape[1]
+    B = seqlens_kv.shape[0]
+    MB = block_table.shape[1]
+    if q.numel() != T * num_heads * d or cu_seqlens_q.shape != (B + 1,) \
+            or block_table.shape[0] != B or tuple(v_cache.shape) != tuple(k_cache.shape) \
+            or k_cache.shape[2] != num_kv_heads or tuple(k_scale.shape) != (num_kv_heads, d) \
+            or tuple(v_scale.shape) != (num_kv_heads, d):
+        raise ValueError("inconsistent shapes")
+    if k_cache.dtype != torch.uint8 or v_cache.dtype != torch.uint8:
+        raise ValueError("fp8 caches hold uint8 codes")
+    if out is None:
+        out = torch.empty((T, num_heads, d), dtype=q.dtype, device=q.device)
+    elif out.numel() != q.numel() or out.dtype != q.dtype:
+        raise ValueError("out must match q")
+    need = pa_attention_workspace_size(B, T, MB, num_heads, num_kv_heads, d, bs)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    check(lib().pa_attention_fp8(
+        _dev(q, "q"), _dev(cu_seqlens_q, "cu_seqlens_q", torch.int32),
+        _dev(seqlens_kv, "seqlens_kv", torch.int32), _dev(block_table, "block_table", torch.int32),
+        _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+        _dev(k_scale, "k_scale", torch.float32), _dev(v_scale, "v_scale", torch.float32),
+        _dev(out, "out"), B, T, int(max_q_len), MB, nb, float(scale), num_heads, num_kv_heads, d,
+        bs, _dtype_code(q), _dev(workspace, "workspace"),
+        workspace.numel() * workspace.element_size(), _stream_ptr(q, stream)))
     return out
 
 

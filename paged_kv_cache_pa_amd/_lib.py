@@ -21,8 +21,8 @@ PA_F16 = 0
 PA_BF16 = 1
 PROFILE_KINDS = ("scatter", "plan", "attention", "combine")
 
-EXPORTS = ("pa_scatter_kv", "pa_scatter_kv_paged", "pa_seqlens_from_past",
-           "pa_attention_workspace_size", "pa_attention",
+EXPORTS = ("pa_scatter_kv", "pa_scatter_kv_paged", "pa_scatter_kv_fp8", "pa_seqlens_from_past",
+           "pa_attention_workspace_size", "pa_attention", "pa_attention_fp8",
            "pa_validate_metadata", "pa_status_string", "pa_last_error",
            "pa_profile_enable", "pa_profile_read")
 
@@ -52,6 +52,8 @@ def lib():
     L.pa_scatter_kv_paged.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i64, i32, i32,
                                       i32, i32, vp]
     L.pa_scatter_kv_paged.restype = i32
+    L.pa_scatter_kv_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i32, i32, i32, i32, vp]
+    L.pa_scatter_kv_fp8.restype = i32
     L.pa_seqlens_from_past.argtypes = [vp, vp, vp, i32, vp]
     L.pa_seqlens_from_past.restype = i32
     L.pa_attention_workspace_size.argtypes = [i32, i64, i32, i32, i32, i32, i32]
@@ -59,6 +61,9 @@ def lib():
     L.pa_attention.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i64, f32, i32, i32,
                                i32, i32, i32, vp, sz, vp]
     L.pa_attention.restype = i32
+    L.pa_attention_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i64,
+                                   f32, i32, i32, i32, i32, i32, vp, sz, vp]
+    L.pa_attention_fp8.restype = i32
     L.pa_validate_metadata.argtypes = [vp, vp, vp, vp, i32, i64, i32, i64, i32,
                                        ctypes.POINTER(ctypes.c_uint32), vp]
     L.pa_validate_metadata.restype = i32

@@ -208,6 +208,35 @@ pa_status_t pa_scatter_kv(const void* k_new, const void* v_new, const int32_t* s
   return PA_OK;
 }
 
+pa_status_t pa_scatter_kv_fp8(const void* k_new, const void* v_new, const int32_t* slot_mapping,
+                              const float* k_scale, const float* v_scale, void* k_cache,
+                              void* v_cache, int64_t num_tokens, int64_t num_blocks,
+                              int32_t num_kv_heads, int32_t head_size, int32_t block_size,
+                              int32_t dtype, void* stream) {
+  g_err[0] = 0;
+  if (dtype != PA_F16 && dtype != PA_BF16)
+    return fail(PA_ERR_NOT_IMPLEMENTED, "dtype=%d (supported: PA_F16, PA_BF16)", dtype);
+  if (num_tokens < 0) return fail(PA_ERR_INVALID_ARGUMENT, "num_tokens < 0");
+  if (num_kv_heads < 1 || head_size < 1 || block_size < 1 || num_blocks < 1)
+    return fail(PA_ERR_INVALID_ARGUMENT, "sizes must be >= 1");
+  if (head_size % 8 != 0)
+    return fail(PA_ERR_NOT_IMPLEMENTED, "head_size=%d is not a multiple of 8", head_size);
+  if (num_blocks * (int64_t)block_size > INT32_MAX)
+    return fail(PA_ERR_NOT_IMPLEMENTED, "num_blocks * block_size exceeds INT32_MAX");
+  const int64_t row_elems = (int64_t)num_kv_heads * head_size;
+  if (row_elems * 2 > INT32_MAX) return fail(PA_ERR_NOT_IMPLEMENTED, "row too large");
+  if (num_tokens == 0) return PA_OK;
+  if (!k_new || !v_new || !slot_mapping || !k_scale || !v_scale || !k_cache || !v_cache)
+    return fail(PA_ERR_INVALID_ARGUMENT, "null pointer argument");
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e = timed(0, st, [&] {
+    return pa::launch_scatter_fp8(k_new, v_new, slot_mapping, k_scale, v_scale, k_cache, v_cache,
+                                  num_tokens, (int32_t)row_elems, dtype, st);
+  });
+  if (e != hipSuccess) return hip_fail(e, "fp8 scatter launch");
+  return PA_OK;
+}
+
 pa_status_t pa_scatter_kv_paged(const void* k_new, const void* v_new, const int32_t* cu_seqlens_q,
                                 const int32_t* seqlens_kv, const int32_t* block_table,
                                 void* k_cache, void* v_cache, int32_t num_seqs,
@@ -267,14 +296,17 @@ size_t pa_attention_workspace_size(int32_t num_seqs, int64_t num_tokens, int32_t
   return pa::workspace_layout(s).total;
 }
 
-pa_status_t pa_attention(const void* q, const int32_t* cu_seqlens_q, const int32_t* seqlens_kv,
-                         const int32_t* block_table, const void* k_cache, const void* v_cache,
-                         void* out, int32_t num_seqs, int64_t num_tokens,
-                         int32_t max_blocks_per_seq, int64_t num_blocks, float scale,
-                         int32_t num_heads, int32_t num_kv_heads, int32_t head_size,
-                         int32_t block_size, int32_t dtype, void* workspace,
-                         size_t workspace_bytes, void* stream) {
-  g_err[0] = 0;
+// Shared by pa_attention (16-bit caches) and pa_attention_fp8 (kv8: e4m3
+// caches with per-channel scales, decode path only).
+static pa_status_t attention_impl(const void* q, const int32_t* cu_seqlens_q,
+                                  const int32_t* seqlens_kv, const int32_t* block_table,
+                                  const void* k_cache, const void* v_cache, const float* k_scale,
+                                  const float* v_scale, void* out, int32_t num_seqs,
+                                  int64_t num_tokens, int32_t max_blocks_per_seq,
+                                  int64_t num_blocks, float scale, int32_t num_heads,
+                                  int32_t num_kv_heads, int32_t head_size, int32_t block_size,
+                                  int32_t dtype, void* workspace, size_t workspace_bytes,
+                                  void* stream, bool kv8) {
   if (dtype != PA_F16 && dtype != PA_BF16)
     return fail(PA_ERR_NOT_IMPLEMENTED, "dtype=%d (supported: PA_F16, PA_BF16)", dtype);
   const pa::Shape s{num_seqs, num_tokens, max_blocks_per_seq, num_heads, num_kv_heads, head_size,
@@ -288,6 +320,7 @@ pa_status_t pa_attention(const void* q, const int32_t* cu_seqlens_q, const int32
   if (num_tokens == 0) return PA_OK;
   if (!q || !cu_seqlens_q || !seqlens_kv || !block_table || !k_cache || !v_cache || !out)
     return fail(PA_ERR_INVALID_ARGUMENT, "null pointer argument");
+  if (kv8 && (!k_scale || !v_scale)) return fail(PA_ERR_INVALID_ARGUMENT, "null scale pointer");
   const pa::Layout L = pa::workspace_layout(s);
   if (L.max_part_rows > INT32_MAX)
     return fail(PA_ERR_NOT_IMPLEMENTED, "split-KV partial rows exceed INT32_MAX");
@@ -315,11 +348,13 @@ pa_status_t pa_attention(const void* q, const int32_t* cu_seqlens_q, const int32
   pl.group = G;
   pl.num_kv_heads = num_kv_heads;
   pl.tokens_per_tile = tq;
+  pl.decode_only = kv8 ? 1 : 0;
   // Persistent grid: what the device holds at once, but no more groups than
   // there are prefill items plus groups of 8 decode waves.
-  const int64_t max_groups = L.max_pf_items + (L.max_dec_pairs * num_kv_heads + 7) / 8;
+  const int64_t max_groups =
+      (kv8 ? 0 : L.max_pf_items) + (L.max_dec_pairs * num_kv_heads + 7) / 8;
   const int workers = (int)std::max<int64_t>(
-      1, std::min<int64_t>(pa::attention_workers(dtype, head_size, cus), max_groups));
+      1, std::min<int64_t>(pa::attention_workers(dtype, head_size, cus, kv8), max_groups));
   pl.num_workers = workers;
   hipError_t e = timed(1, st, [&] { return pa::launch_plan(pl, st); });
   if (e != hipSuccess) return hip_fail(e, "plan launch");
@@ -337,6 +372,8 @@ pa_status_t pa_attention(const void* q, const int32_t* cu_seqlens_q, const int32
   a.pf_items = pl.pf_items;
   a.part_ml = (float2*)(ws + L.part_ml);
   a.part_acc = (float*)(ws + L.part_acc);
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
   a.num_seqs = num_seqs;
   a.num_heads = num_heads;
   a.num_kv_heads = num_kv_heads;
@@ -348,13 +385,49 @@ pa_status_t pa_attention(const void* q, const int32_t* cu_seqlens_q, const int32
   a.scale_log2 = scale * pa::kLog2e;
   a.inv_group = 1.0f / (float)G;
 
-  e = timed(2, st, [&] { return pa::launch_attention(a, dtype, head_size, workers, st); });
+  e = timed(2, st, [&] { return pa::launch_attention(a, dtype, head_size, workers, st, kv8); });
   if (e != hipSuccess) return hip_fail(e, "attention launch");
   if (L.max_part_rows > 0) {
     e = timed(3, st, [&] { return pa::launch_combine(a, dtype, head_size, st); });
     if (e != hipSuccess) return hip_fail(e, "combine launch");
   }
   return PA_OK;
+}
+
+pa_status_t pa_attention(const void* q, const int32_t* cu_seqlens_q, const int32_t* seqlens_kv,
+                         const int32_t* block_table, const void* k_cache, const void* v_cache,
+                         void* out, int32_t num_seqs, int64_t num_tokens,
+                         int32_t max_blocks_per_seq, int64_t num_blocks, float scale,
+                         int32_t num_heads, int32_t num_kv_heads, int32_t head_size,
+                         int32_t block_size, int32_t dtype, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  g_err[0] = 0;
+  return attention_impl(q, cu_seqlens_q, seqlens_kv, block_table, k_cache, v_cache, nullptr,
+                        nullptr, out, num_seqs, num_tokens, max_blocks_per_seq, num_blocks, scale,
+                        num_heads, num_kv_heads, head_size, block_size, dtype, workspace,
+                        workspace_bytes, stream, false);
+}
+
+pa_status_t pa_attention_fp8(const void* q, const int32_t* cu_seqlens_q,
+                             const int32_t* seqlens_kv, const int32_t* block_table,
+                             const void* k_cache, const void* v_cache, const float* k_scale,
+                             const float* v_scale, void* out, int32_t num_seqs,
+                             int64_t num_tokens, int32_t max_q_len, int32_t max_blocks_per_seq,
+                             int64_t num_blocks, float scale, int32_t num_heads,
+                             int32_t num_kv_heads, int32_t head_size, int32_t block_size,
+                             int32_t dtype, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+  g_err[0] = 0;
+  if (max_q_len < 0) return fail(PA_ERR_INVALID_ARGUMENT, "max_q_len < 0");
+  if (num_kv_heads >= 1 && num_heads >= 1 && num_heads % num_kv_heads == 0 &&
+      (int64_t)max_q_len * (num_heads / num_kv_heads) > pa::kDecodeCols)
+    return fail(PA_ERR_NOT_IMPLEMENTED,
+                "fp8 caches: max_q_len * G = %lld exceeds %d (decode-shaped batches only)",
+                (long long)max_q_len * (num_heads / num_kv_heads), pa::kDecodeCols);
+  return attention_impl(q, cu_seqlens_q, seqlens_kv, block_table, k_cache, v_cache, k_scale,
+                        v_scale, out, num_seqs, num_tokens, max_blocks_per_seq, num_blocks, scale,
+                        num_heads, num_kv_heads, head_size, block_size, dtype, workspace,
+                        workspace_bytes, stream, true);
 }
 
 pa_status_t pa_validate_metadata(const int32_t* cu_seqlens_q, const int32_t* seqlens_kv,

@@ -33,33 +33,50 @@ __global__ __launch_bounds__(512, 1) void attention_kernel(AttnArgs a) {
   if (prefill_first) decode_items<T, D>(a);
 }
 
+// fp8 caches: decode items only (the plan gives every sequence the decode
+// path); waves are independent and use no LDS.
 template <typename T, int D>
-static const void* attention_fn() {
-  return (const void*)&attention_kernel<T, D>;
+__global__ __launch_bounds__(512) void attention_kernel_fp8(AttnArgs a) {
+  decode_items<T, D, true>(a);
 }
 
-static const void* attention_fn(int dtype, int head_size) {
-  if (dtype == 0) return head_size == 128 ? attention_fn<F16, 128>() : attention_fn<F16, 64>();
-  return head_size == 128 ? attention_fn<BF16, 128>() : attention_fn<BF16, 64>();
+template <typename T, int D>
+static const void* attention_fn(bool kv8) {
+  return kv8 ? (const void*)&attention_kernel_fp8<T, D> : (const void*)&attention_kernel<T, D>;
 }
 
-int attention_workers(int dtype, int head_size, int num_cus) {
-  return resident_blocks(attention_fn(dtype, head_size), num_cus, 512);
+static const void* attention_fn(int dtype, int head_size, bool kv8) {
+  if (dtype == 0)
+    return head_size == 128 ? attention_fn<F16, 128>(kv8) : attention_fn<F16, 64>(kv8);
+  return head_size == 128 ? attention_fn<BF16, 128>(kv8) : attention_fn<BF16, 64>(kv8);
+}
+
+int attention_workers(int dtype, int head_size, int num_cus, bool kv8) {
+  return resident_blocks(attention_fn(dtype, head_size, kv8), num_cus, 512);
 }
 
 template <typename T>
-static hipError_t attention_dispatch(const AttnArgs& a, int head_size, int grid, hipStream_t st) {
-  if (head_size == 128)
-    hipLaunchKernelGGL((attention_kernel<T, 128>), dim3((unsigned)grid), dim3(512), 0, st, a);
-  else
-    hipLaunchKernelGGL((attention_kernel<T, 64>), dim3((unsigned)grid), dim3(512), 0, st, a);
+static hipError_t attention_dispatch(const AttnArgs& a, int head_size, int grid, hipStream_t st,
+                                     bool kv8) {
+  const dim3 g((unsigned)grid), b(512);
+  if (kv8) {
+    if (head_size == 128)
+      hipLaunchKernelGGL((attention_kernel_fp8<T, 128>), g, b, 0, st, a);
+    else
+      hipLaunchKernelGGL((attention_kernel_fp8<T, 64>), g, b, 0, st, a);
+  } else {
+    if (head_size == 128)
+      hipLaunchKernelGGL((attention_kernel<T, 128>), g, b, 0, st, a);
+    else
+      hipLaunchKernelGGL((attention_kernel<T, 64>), g, b, 0, st, a);
+  }
   return hipGetLastError();
 }
 
 hipError_t launch_attention(const AttnArgs& a, int dtype, int head_size, int grid,
-                            hipStream_t st) {
-  return dtype == 0 ? attention_dispatch<F16>(a, head_size, grid, st)
-                    : attention_dispatch<BF16>(a, head_size, grid, st);
+                            hipStream_t st, bool kv8) {
+  return dtype == 0 ? attention_dispatch<F16>(a, head_size, grid, st, kv8)
+                    : attention_dispatch<BF16>(a, head_size, grid, st, kv8);
 }
 
 template <typename T>

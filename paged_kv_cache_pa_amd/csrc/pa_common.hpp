@@ -51,6 +51,17 @@ template <> struct Elt<F16> {
   __device__ static inline float sum2(uint32_t packed, float acc) {
     return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, packed), half2_t{1, 1}, acc, false);
   }
+  // The two packed values as fp32 (exact).
+  __device__ static inline float2 unpack2(uint32_t packed) {
+    const half2_t h = __builtin_bit_cast(half2_t, packed);
+    return make_float2((float)h[0], (float)h[1]);
+  }
+  // fp8 e4m3 bytes 2W, 2W+1 of src -> two packed fp16 (exact: every e4m3
+  // value is an fp16 value; scale operand 1.0).
+  template <int W>
+  __device__ static inline uint32_t from_fp8x2(uint32_t src) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)src, 1.0f, W != 0));
+  }
 };
 
 template <> struct Elt<BF16> {
@@ -70,6 +81,16 @@ template <> struct Elt<BF16> {
   __device__ static inline float sum2(uint32_t packed, float acc) {
     return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, packed),
                                            bf16x2_t{1, 1}, acc, false);
+  }
+  // The two packed values as fp32 (exact: bf16 is the top half of fp32).
+  __device__ static inline float2 unpack2(uint32_t packed) {
+    return make_float2(__builtin_bit_cast(float, packed << 16),
+                       __builtin_bit_cast(float, packed & 0xffff0000u));
+  }
+  // fp8 e4m3 bytes 2W, 2W+1 of src -> two packed bf16 (exact; scale 1.0).
+  template <int W>
+  __device__ static inline uint32_t from_fp8x2(uint32_t src) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)src, 1.0f, W != 0));
   }
 };
 

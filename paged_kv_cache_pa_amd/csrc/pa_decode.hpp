@@ -32,7 +32,20 @@
 // A sequence with one split writes its normalised output directly; longer
 // sequences write (m, l, unnormalised acc) per split and column, merged by
 // combine_kernel:  O = sum_s 2^(m_s - M) acc_s / sum_s 2^(m_s - M) l_s.
+//
+// fp8 caches (KV8; e4m3 elements with a float32 scale per KV head and
+// channel, the quantized KV cache of the "Roadmap", phase 3): the same
+// matrix-core program on half the bytes.  A lane's K bytes are made
+// contiguous by giving lane group kq the contraction chunks NS*kq .. +NS-1
+// (Q^T loaded with the same chunk order), so a lane loads 8*NS bytes of its
+// key row and NT bytes of each of its four value rows.  Chunks stay as raw
+// bytes in flight and are widened to fp16/bf16 (exact) just before their
+// MFMAs.  The K scale of channel d multiplies q_d once per item (in fp32,
+// then rounded to the MFMA type with the rest of Q^T); the V scale
+// multiplies the accumulators before they are stored.
 #pragma once
+
+#include <type_traits>
 
 #include "pa_common.hpp"
 #include "pa_internal.hpp"
@@ -41,7 +54,7 @@ namespace pa {
 
 // Runs decode work items on the calling wave until the decode counter is
 // exhausted.  Every wave is independent (no barriers, no LDS).
-template <typename T, int D>
+template <typename T, int D, bool KV8 = false>
 __device__ __forceinline__ void decode_items(const AttnArgs& a) {
   constexpr int NS = D / 32;    // QK^T contraction steps (8 halfs per lane)
   constexpr int NT = D / 16;    // O^T tiles; also halfs per lane per V row
@@ -54,8 +67,9 @@ __device__ __forceinline__ void decode_items(const AttnArgs& a) {
   const int hk = a.num_kv_heads, G = a.group, hq = a.num_heads;
   const int64_t row_stride = (int64_t)hk * D;   // elements between token rows
   const uint16_t* __restrict__ qp = (const uint16_t*)a.q;
-  const uint16_t* __restrict__ kc = (const uint16_t*)a.k_cache;
-  const uint16_t* __restrict__ vc = (const uint16_t*)a.v_cache;
+  typedef typename std::conditional<KV8, uint8_t, uint16_t>::type CT;   // cache element
+  const CT* __restrict__ kc = (const CT*)a.k_cache;
+  const CT* __restrict__ vc = (const CT*)a.v_cache;
   uint16_t* __restrict__ op = (uint16_t*)a.out;
   const int n_items = a.counters[kNumDecPairs] * hk;
 
@@ -85,9 +99,27 @@ __device__ __forceinline__ void decode_items(const AttnArgs& a) {
       const int tok = si.cu + (valid ? ng : 0);
       const int h = kh * G + (valid ? n - ng * G : 0);
       const uint16_t* qrow = qp + ((int64_t)tok * hq + h) * D;
+      if constexpr (!KV8) {
 #pragma unroll
-      for (int s = 0; s < NS; ++s) {
-        qreg[s] = valid ? ld16(qrow + (4 * s + kq) * 8) : u32x4_t{0, 0, 0, 0};
+        for (int s = 0; s < NS; ++s) {
+          qreg[s] = valid ? ld16(qrow + (4 * s + kq) * 8) : u32x4_t{0, 0, 0, 0};
+        }
+      } else {
+        const float* ks = a.k_scale + (int64_t)kh * D;
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+          const int d0 = (NS * kq + s) * 8;
+          const u32x4_t x = ld16(qrow + d0);
+          const float4_t s0 = *reinterpret_cast<const float4_t*>(ks + d0);
+          const float4_t s1 = *reinterpret_cast<const float4_t*>(ks + d0 + 4);
+          const float2 f0 = Elt<T>::unpack2(x[0]), f1 = Elt<T>::unpack2(x[1]);
+          const float2 f2 = Elt<T>::unpack2(x[2]), f3 = Elt<T>::unpack2(x[3]);
+          const u32x4_t y = {Elt<T>::pack2(f0.x * s0[0], f0.y * s0[1]),
+                             Elt<T>::pack2(f1.x * s0[2], f1.y * s0[3]),
+                             Elt<T>::pack2(f2.x * s1[0], f2.y * s1[1]),
+                             Elt<T>::pack2(f3.x * s1[2], f3.y * s1[3])};
+          qreg[s] = valid ? y : u32x4_t{0, 0, 0, 0};
+        }
       }
     }
     // Causal limit of column n: token n / G sees keys <= past + n / G
@@ -105,36 +137,66 @@ __device__ __forceinline__ void decode_items(const AttnArgs& a) {
 #pragma unroll
     for (int t = 0; t < NT; ++t) acc[t] = float4_t{0.f, 0.f, 0.f, 0.f};
 
-    // K/V registers of one 16-key chunk.
+    // K/V registers of one 16-key chunk, as loaded: 16-bit elements, or fp8
+    // codes (KV8: NS/2 16-byte K loads and NT/4 dwords per value row).
+    constexpr int KW = KV8 ? NS / 2 : NS;
+    constexpr int VW = KV8 ? NT / 4 : NT / 2;
     struct Chunk {
-      u32x4_t k[NS];
-      uint32_t v[4][NT / 2];
+      u32x4_t k[KW];
+      uint32_t v[4][VW];
     };
     auto load = [&](int c0, Chunk& ch) {
       const int blk = __builtin_amdgcn_readlane(my_blk, (c0 >> a.block_shift) - blk0);
       const int64_t base =
           ((int64_t)blk * a.block_size + (c0 & (a.block_size - 1))) * row_stride + (int64_t)kh * D;
-      const uint16_t* krow = kc + base + r16 * row_stride;
+      const CT* krow = kc + base + r16 * row_stride;
+      if constexpr (!KV8) {
 #pragma unroll
-      for (int s = 0; s < NS; ++s) ch.k[s] = ld16(krow + (4 * s + kq) * 8);
+        for (int s = 0; s < NS; ++s) ch.k[s] = ld16(krow + (4 * s + kq) * 8);
+      } else {
+#pragma unroll
+        for (int s = 0; s < KW; ++s)
+          ch.k[s] = *reinterpret_cast<const u32x4_t*>(krow + NS * kq * 8 + 16 * s);
+      }
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const uint16_t* vrow = vc + base + (4 * kq + e) * row_stride + r16 * NT;
-        if constexpr (NT == 8) {
-          const u32x4_t x = ld16(vrow);
+        const CT* vrow = vc + base + (4 * kq + e) * row_stride + r16 * NT;
+        if constexpr (VW == 4) {
+          const u32x4_t x = *reinterpret_cast<const u32x4_t*>(vrow);
 #pragma unroll
           for (int w = 0; w < 4; ++w) ch.v[e][w] = x[w];
-        } else {
-          const u32x2_t x = ld8(vrow);
+        } else if constexpr (VW == 2) {
+          const u32x2_t x = *reinterpret_cast<const u32x2_t*>(vrow);
 #pragma unroll
           for (int w = 0; w < 2; ++w) ch.v[e][w] = x[w];
+        } else {
+          ch.v[e][0] = *reinterpret_cast<const uint32_t*>(vrow);
         }
+      }
+    };
+    // Operand of QK^T step s: 8 elements of the lane's key row.
+    auto k_operand = [&](const Chunk& ch, int s) -> u32x4_t {
+      if constexpr (!KV8) {
+        return ch.k[s];
+      } else {
+        const uint32_t lo = ch.k[s >> 1][2 * (s & 1)], hi = ch.k[s >> 1][2 * (s & 1) + 1];
+        return u32x4_t{Elt<T>::template from_fp8x2<0>(lo), Elt<T>::template from_fp8x2<1>(lo),
+                       Elt<T>::template from_fp8x2<0>(hi), Elt<T>::template from_fp8x2<1>(hi)};
+      }
+    };
+    // Dword w (two elements) of value row e, as 16-bit elements.
+    auto v_word = [&](const Chunk& ch, int e, int w) -> uint32_t {
+      if constexpr (!KV8) {
+        return ch.v[e][w];
+      } else {
+        const uint32_t x = ch.v[e][w >> 1];
+        return (w & 1) ? Elt<T>::template from_fp8x2<1>(x) : Elt<T>::template from_fp8x2<0>(x);
       }
     };
     auto compute = [&](int c0, const Chunk& ch) {
       float4_t sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int s = 0; s < NS; ++s) sc = Elt<T>::mfma32(ch.k[s], qreg[s], sc);
+      for (int s = 0; s < NS; ++s) sc = Elt<T>::mfma32(k_operand(ch, s), qreg[s], sc);
       float sv[4];
       float cmax = -INFINITY;
 #pragma unroll
@@ -172,7 +234,7 @@ __device__ __forceinline__ void decode_items(const AttnArgs& a) {
       for (int e = 0; e < 4; ++e) {
         const bool live = c0 + 4 * kq + e < k1;
 #pragma unroll
-        for (int w = 0; w < NT / 2; ++w) vz[e][w] = live ? ch.v[e][w] : 0u;
+        for (int w = 0; w < NT / 2; ++w) vz[e][w] = live ? v_word(ch, e, w) : 0u;
       }
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
@@ -204,6 +266,17 @@ __device__ __forceinline__ void decode_items(const AttnArgs& a) {
     if (nch & 1) compute(last_c0, ca);
 
     const float l_tot = sum_xor16_32(l);
+    if constexpr (KV8) {   // V scale of channel d = (4kq + r) * NT + t
+      const float* vs = a.v_scale + (int64_t)kh * D;
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int t = 0; t < NT; t += 4) {
+          const float4_t f = *reinterpret_cast<const float4_t*>(vs + (4 * kq + r) * NT + t);
+#pragma unroll
+          for (int u = 0; u < 4; ++u) acc[t + u][r] *= f[u];
+        }
+    }
     const int n = r16;
     if (n >= ncols) {
       // padding column: nothing to store

@@ -86,6 +86,8 @@ struct PlanArgs {
   int4* pf_items;
   int32_t num_seqs, group, num_kv_heads, tokens_per_tile;
   int32_t num_workers;  // grid size of the attention kernel
+  int32_t decode_only;  // fp8 caches: only the decode path; a sequence with
+                        // more than kDecodeCols columns gets no work items
 };
 
 struct AttnArgs {
@@ -101,6 +103,8 @@ struct AttnArgs {
   const int4* pf_items;
   float2* part_ml;
   float* part_acc;
+  const float* k_scale;   // fp8 caches: [num_kv_heads, head_size] float32
+  const float* v_scale;
   int32_t num_seqs, num_heads, num_kv_heads, group, max_blocks_per_seq;
   int32_t block_size, block_shift, tokens_per_tile;
   float scale_log2;  // scale * log2(e)
@@ -109,6 +113,10 @@ struct AttnArgs {
 
 hipError_t launch_scatter(const void* k_new, const void* v_new, const int32_t* slots, void* kc,
                           void* vc, int64_t num_tokens, int32_t row_bytes, hipStream_t st);
+hipError_t launch_scatter_fp8(const void* k_new, const void* v_new, const int32_t* slots,
+                              const float* k_scale, const float* v_scale, void* kc, void* vc,
+                              int64_t num_tokens, int32_t row_elems, int32_t dtype,
+                              hipStream_t st);
 hipError_t launch_scatter_paged(const void* k_new, const void* v_new, const int32_t* cu,
                                 const int32_t* lens, const int32_t* table, void* kc, void* vc,
                                 int32_t num_seqs, int64_t num_tokens, int32_t max_blocks,
@@ -120,9 +128,10 @@ hipError_t launch_plan(const PlanArgs& a, hipStream_t st);
 // device holds at once.  Work-groups [0, counters[kPrefillFirst]) run prefill
 // items first and then decode items; the others run decode items first, so
 // compute-bound prefill and bandwidth-bound decode overlap across CUs.
-int attention_workers(int dtype, int head_size, int num_cus);
+// kv8: the kernel for fp8 caches, which runs decode items only.
+int attention_workers(int dtype, int head_size, int num_cus, bool kv8 = false);
 hipError_t launch_attention(const AttnArgs& a, int dtype, int head_size, int grid,
-                            hipStream_t st);
+                            hipStream_t st, bool kv8 = false);
 hipError_t launch_combine(const AttnArgs& a, int dtype, int head_size, hipStream_t st);
 
 // Work-groups of `kernel` (`threads` per group) resident at once.

@@ -77,6 +77,7 @@ __device__ inline SeqCounts seq_counts(const PlanArgs& a, int b) {
   c.L = a.seqlens_kv[b];
   if (c.q_len <= 0) return c;
   const int ncols = c.q_len * a.group;
+  if (a.decode_only && ncols > kDecodeCols) return c;   // no work (precondition violated)
   if (ncols <= kDecodeCols) {
     c.nsplit = (c.L + kSplitKeys - 1) / kSplitKeys;
     if (c.nsplit > 1) c.prows = a.num_kv_heads * c.nsplit * ncols;

@@ -43,6 +43,70 @@ hipError_t launch_scatter(const void* k_new, const void* v_new, const int32_t* s
   return hipGetLastError();
 }
 
+// Scatter into fp8 (e4m3) caches with per-channel scales: the quantized KV
+// cache ("[WebGPU] Initial PagedAttention implementation (1/n)", "Roadmap",
+// phase 3: a cache element type apart from the query type, quantized KV
+// first).  The pages define no format; the one taken: OCP e4m3 elements and
+// one float32 scale per (KV head, channel) for K and for V.  Element x of a
+// row is stored as e4m3(y), y = x * (1 / scale) with the reciprocal and the
+// product rounded to fp32, |y| > 448 (infinities too) saturated to 448, NaN
+// kept, then rounded to nearest even by v_cvt_pk_fp8_f32 (which alone would
+// turn magnitudes above 464 into NaN).  Each thread quantizes one chunk of
+// 8 elements: a 16-byte load of K and of V, two 16-byte scale loads each, and
+// an 8-byte store of codes per cache.
+__device__ inline float sat_e4m3(float y) { return fabsf(y) > 448.f ? copysignf(448.f, y) : y; }
+
+template <typename T>
+__device__ inline u32x2_t quantize8(const u32x4_t x, const float4_t s0, const float4_t s1) {
+  float y[8];
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const float2 f = Elt<T>::unpack2(x[w]);
+    const float sa = w < 2 ? s0[2 * w] : s1[2 * w - 4];
+    const float sb = w < 2 ? s0[2 * w + 1] : s1[2 * w - 3];
+    y[2 * w] = sat_e4m3(f.x * (1.0f / sa));
+    y[2 * w + 1] = sat_e4m3(f.y * (1.0f / sb));
+  }
+  int lo = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
+  lo = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], lo, true);
+  int hi = __builtin_amdgcn_cvt_pk_fp8_f32(y[4], y[5], 0, false);
+  hi = __builtin_amdgcn_cvt_pk_fp8_f32(y[6], y[7], hi, true);
+  return u32x2_t{(uint32_t)lo, (uint32_t)hi};
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void scatter_fp8_kernel(
+    const u32x4_t* __restrict__ k_new, const u32x4_t* __restrict__ v_new,
+    const int32_t* __restrict__ slots, const float4_t* __restrict__ k_scale,
+    const float4_t* __restrict__ v_scale, u32x2_t* __restrict__ kc, u32x2_t* __restrict__ vc,
+    int64_t total_chunks, int32_t row_chunks) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total_chunks; i += stride) {
+    const int64_t t = i / row_chunks;
+    const int32_t c = (int32_t)(i - t * row_chunks);
+    const int32_t s = slots[t];
+    if (s < 0) continue;
+    const int64_t dst = (int64_t)s * row_chunks + c;
+    kc[dst] = quantize8<T>(k_new[i], k_scale[2 * c], k_scale[2 * c + 1]);
+    vc[dst] = quantize8<T>(v_new[i], v_scale[2 * c], v_scale[2 * c + 1]);
+  }
+}
+
+hipError_t launch_scatter_fp8(const void* k_new, const void* v_new, const int32_t* slots,
+                              const float* k_scale, const float* v_scale, void* kc, void* vc,
+                              int64_t num_tokens, int32_t row_elems, int32_t dtype,
+                              hipStream_t st) {
+  const int32_t row_chunks = row_elems / 8;
+  const int64_t total = num_tokens * row_chunks;
+  int64_t blocks = (total + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  auto kern = dtype == 1 ? scatter_fp8_kernel<BF16> : scatter_fp8_kernel<F16>;
+  hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(256), 0, st, (const u32x4_t*)k_new,
+                     (const u32x4_t*)v_new, slots, (const float4_t*)k_scale,
+                     (const float4_t*)v_scale, (u32x2_t*)kc, (u32x2_t*)vc, total, row_chunks);
+  return hipGetLastError();
+}
+
 // Scatter with the slots computed on the device from the batch metadata
 // ("[WebGPU] Initial PagedAttention implementation (1/n)", section
 // "Description": the op derives each new token's cache slot from the

@@ -268,3 +268,18 @@ def make_values(wl, device="cpu", backend="numpy"):
     else:
         raise ValueError(backend)
     return {"q": out[0], "k_all": out[1], "v_all": out[2]}
+
+
+def fp8_scales(wl, seed=None):
+    """Per-(KV head, channel) float32 scales of fp8 (e4m3) caches for the
+    workload's K and V: c * (1 + 0.5 u), u ~ U[0, 1) from a seeded stream,
+    with c = bound / 448 for the value range (bound 1.25 for U(-1,1) values,
+    4.5 for N(0,1)), so values within the bound never saturate.  Returns
+    numpy (k_scale, v_scale), each [num_kv_heads, head_size]."""
+    rng = np.random.default_rng(int(wl.seed) + 7919 if seed is None else seed)
+    bound = 1.25 if wl.dist == "uniform" else 4.5
+    c = bound / 448.0
+    shape = (wl.num_kv_heads, wl.head_size)
+    ks = (c * (1.0 + 0.5 * rng.uniform(0.0, 1.0, size=shape))).astype(np.float32)
+    vs = (c * (1.0 + 0.5 * rng.uniform(0.0, 1.0, size=shape))).astype(np.float32)
+    return ks, vs

@@ -14,7 +14,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 def _declared_symbols():
     text = open(os.path.join(ROOT, "include", "pa.h")).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(pa_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(pa_[a-z0-9_]+)\s*\(", text)))
 
 
 @pytest.fixture(scope="module")
@@ -143,3 +143,64 @@ def test_seqlens_from_past_rejects_on_host(L):
     assert L.pa_seqlens_from_past(FAKE, FAKE, FAKE, 0, None) == _lib.PA_ERR_INVALID_ARGUMENT
     assert L.pa_seqlens_from_past(FAKE, None, FAKE, 3, None) == _lib.PA_ERR_INVALID_ARGUMENT
     assert L.pa_seqlens_from_past(FAKE, FAKE, None, 3, None) == _lib.PA_ERR_INVALID_ARGUMENT
+
+
+# ---------------------------------------------------------------- fp8 caches
+
+def _scatter8(L, **kw):
+    a = dict(k=FAKE, v=FAKE, slots=FAKE, ks=FAKE, vs=FAKE, kc=FAKE, vc=FAKE, T=5, NB=8, hk=2,
+             d=64, bs=16, dtype=0, st=None)
+    a.update(kw)
+    return L.pa_scatter_kv_fp8(a["k"], a["v"], a["slots"], a["ks"], a["vs"], a["kc"], a["vc"],
+                               a["T"], a["NB"], a["hk"], a["d"], a["bs"], a["dtype"], a["st"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=2), _lib.PA_ERR_NOT_IMPLEMENTED),
+    (dict(d=60), _lib.PA_ERR_NOT_IMPLEMENTED),
+    (dict(T=-1), _lib.PA_ERR_INVALID_ARGUMENT),
+    (dict(hk=0), _lib.PA_ERR_INVALID_ARGUMENT),
+    (dict(ks=None), _lib.PA_ERR_INVALID_ARGUMENT),
+    (dict(vs=None), _lib.PA_ERR_INVALID_ARGUMENT),
+    (dict(kc=None), _lib.PA_ERR_INVALID_ARGUMENT),
+    (dict(NB=1 << 30, bs=16), _lib.PA_ERR_NOT_IMPLEMENTED),
+])
+def test_scatter_fp8_rejects_on_host(L, kw, status):
+    assert _scatter8(L, **kw) == status
+    assert L.pa_last_error() != b""
+
+
+def test_scatter_fp8_empty_call_is_ok(L):
+    assert _scatter8(L, T=0, k=None, v=None, ks=None, vs=None) == _lib.PA_OK
+
+
+def _attn8(L, **kw):
+    a = dict(q=FAKE, cu=FAKE, lens=FAKE, table=FAKE, kc=FAKE, vc=FAKE, ks=FAKE, vs=FAKE, out=FAKE,
+             B=2, T=5, mq=4, MB=2, NB=8, scale=0.125, hq=4, hk=2, d=64, bs=16, dtype=0, ws=FAKE,
+             wsb=0, st=None)
+    a.update(kw)
+    return L.pa_attention_fp8(a["q"], a["cu"], a["lens"], a["table"], a["kc"], a["vc"], a["ks"],
+                              a["vs"], a["out"], a["B"], a["T"], a["mq"], a["MB"], a["NB"],
+                              a["scale"], a["hq"], a["hk"], a["d"], a["bs"], a["dtype"], a["ws"],
+                              a["wsb"], a["st"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(mq=9), _lib.PA_ERR_NOT_IMPLEMENTED),          # 9 * G 2 = 18 columns > 16
+    (dict(hq=34, mq=1), _lib.PA_ERR_NOT_IMPLEMENTED),   # G 17
+    (dict(mq=-1), _lib.PA_ERR_INVALID_ARGUMENT),
+    (dict(ks=None), _lib.PA_ERR_INVALID_ARGUMENT),
+    (dict(vs=None), _lib.PA_ERR_INVALID_ARGUMENT),
+    (dict(dtype=2), _lib.PA_ERR_NOT_IMPLEMENTED),
+    (dict(d=96), _lib.PA_ERR_NOT_IMPLEMENTED),
+    (dict(bs=24), _lib.PA_ERR_NOT_IMPLEMENTED),
+    (dict(scale=float("nan")), _lib.PA_ERR_INVALID_ARGUMENT),
+    (dict(), _lib.PA_ERR_WORKSPACE_TOO_SMALL),
+])
+def test_attention_fp8_rejects_on_host(L, kw, status):
+    assert _attn8(L, **kw) == status
+    assert L.pa_last_error() != b""
+
+
+def test_attention_fp8_empty_call_is_ok(L):
+    assert _attn8(L, T=0, mq=0) == _lib.PA_OK
