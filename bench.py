@@ -29,10 +29,11 @@ WORKLOADS = {"tiny": 1, "small": 2, "decode": 3, "prefill": 4, "mixed": 5}
 
 
 # ------------------------------------------------------------- accounting
-def attention_work(wl, sel=None):
+def attention_work(wl, sel=None, kv_es=ES):
     """Algorithmic bytes and FLOPs of pa_attention over the sequences in
-    ``sel``: every visible K/V element once, Q, O, block ids and length
-    metadata; FLOPs = 4*D per visible (query row, key, head)."""
+    ``sel``: every visible K/V element once (kv_es bytes each: 2, or 1 for
+    fp8 caches, whose per-channel scales are added), Q, O, block ids and
+    length metadata; FLOPs = 4*D per visible (query row, key, head)."""
     q = wl.q_lens.astype(np.int64)
     L = wl.seqlens_kv.astype(np.int64)
     if sel is None:
@@ -40,16 +41,16 @@ def attention_work(wl, sel=None):
     q, L = q[sel], L[sel]
     past = L - q
     D, hq, hk, bs = wl.head_size, wl.num_heads, wl.num_kv_heads, wl.block_size
-    kv = int((L * hk * D * 2 * ES).sum())
+    kv = int((L * hk * D * 2 * kv_es).sum()) + (2 * hk * D * 4 if kv_es == 1 else 0)
     qo = int(2 * q.sum() * hq * D * ES)
     ids = int((-(-L // bs)).sum() * 4 + (2 * len(q) + 1) * 4)
     flops = int(4 * D * hq * (q * past + q * (q + 1) // 2).sum())
     return kv + qo + ids, flops
 
 
-def scatter_work(wl):
+def scatter_work(wl, kv_es=ES):
     T = wl.num_tokens
-    return 2 * 2 * T * wl.num_kv_heads * wl.head_size * ES + 4 * T
+    return 2 * T * wl.num_kv_heads * wl.head_size * (ES + kv_es) + 4 * T
 
 
 def roofline_time(nbytes, flops):
@@ -57,21 +58,29 @@ def roofline_time(nbytes, flops):
 
 
 # ------------------------------------------------------------- GPU side
-def setup(wl, torch, pa, W):
+def setup(wl, torch, pa, W, fp8=False):
     vals = W.make_values(wl, device="cuda", backend="torch")
     dt = W.torch_dtype(wl)
     shape = (wl.num_blocks, wl.block_size, wl.num_kv_heads, wl.head_size)
-    kc = torch.zeros(shape, dtype=dt, device="cuda")
+    kc = torch.zeros(shape, dtype=torch.uint8 if fp8 else dt, device="cuda")
     vc = torch.zeros_like(kc)
     slots_all = torch.from_numpy(wl.kv_slots).cuda()
-    pa.pa_scatter_kv(vals["k_all"], vals["v_all"], slots_all, kc, vc)
+    extra = {}
+    if fp8:
+        ks, vs = W.fp8_scales(wl)
+        extra = dict(fp8=True, ks=torch.from_numpy(ks).cuda(), vs=torch.from_numpy(vs).cuda(),
+                     max_q_len=int(wl.q_lens.max()))
+        pa.pa_scatter_kv_fp8(vals["k_all"], vals["v_all"], slots_all, extra["ks"], extra["vs"],
+                             kc, vc)
+    else:
+        pa.pa_scatter_kv(vals["k_all"], vals["v_all"], slots_all, kc, vc)
     new_rows = torch.from_numpy(wl.new_rows).cuda()
     st = dict(q=vals["q"], k_new=vals["k_all"][new_rows].contiguous(),
               v_new=vals["v_all"][new_rows].contiguous(), kc=kc, vc=vc,
               slots=torch.from_numpy(wl.slot_mapping.astype(np.int32)).cuda(),
               cu=torch.from_numpy(wl.cu_seqlens_q).cuda(),
               lens=torch.from_numpy(wl.seqlens_kv.astype(np.int32)).cuda(),
-              table=torch.from_numpy(wl.block_table.astype(np.int32)).cuda(), vals=vals)
+              table=torch.from_numpy(wl.block_table.astype(np.int32)).cuda(), vals=vals, **extra)
     st["out"] = torch.empty((wl.num_tokens, wl.num_heads, wl.head_size), dtype=dt, device="cuda")
     n = pa.pa_attention_workspace_size(wl.num_seqs, wl.num_tokens, wl.max_blocks_per_seq,
                                        wl.num_heads, wl.num_kv_heads, wl.head_size,
@@ -82,6 +91,13 @@ def setup(wl, torch, pa, W):
 
 
 def step(wl, st, pa):
+    if st.get("fp8"):
+        pa.pa_scatter_kv_fp8(st["k_new"], st["v_new"], st["slots"], st["ks"], st["vs"], st["kc"],
+                             st["vc"])
+        pa.pa_attention_fp8(st["q"], st["cu"], st["lens"], st["table"], st["kc"], st["vc"],
+                            st["ks"], st["vs"], wl.scale, wl.num_heads, wl.num_kv_heads,
+                            st["max_q_len"], out=st["out"], workspace=st["ws"])
+        return
     pa.pa_scatter_kv(st["k_new"], st["v_new"], st["slots"], st["kc"], st["vc"])
     pa.pa_attention(st["q"], st["cu"], st["lens"], st["table"], st["kc"], st["vc"], wl.scale,
                     wl.num_heads, wl.num_kv_heads, out=st["out"], workspace=st["ws"])
@@ -125,12 +141,12 @@ def sub_batch(wl, st, sel, torch, pa):
     return sub
 
 
-def time_workload(wl, steps, warmup, torch, pa, W, extras=False):
+def time_workload(wl, steps, warmup, torch, pa, W, extras=False, fp8=False):
     """Back-to-back timing of `steps` steps (the headline figure) and the
     per-kernel averages; with `extras`, also per-rep scrubbed timing of the
     step and, for a batch that mixes both kinds, its decode-only and
     prefill-only sub-batches timed as separate pa_attention calls."""
-    st = setup(wl, torch, pa, W)
+    st = setup(wl, torch, pa, W, fp8=fp8)
     for _ in range(warmup):
         step(wl, st, pa)
     torch.cuda.synchronize()
@@ -154,6 +170,10 @@ def time_workload(wl, steps, warmup, torch, pa, W, extras=False):
     if extras:
         scrub = torch.empty(SCRUB_BYTES, dtype=torch.uint8, device="cuda")
         more["step_reps"] = per_rep_times(lambda: step(wl, st, pa), steps, torch, scrub)
+        if fp8:
+            del scrub, st
+            torch.cuda.empty_cache()
+            return ms, wall / steps * 1e3, per_kernel, more
         # Both scatter entry points on this step's new tokens: slots from the
         # host-side slot_mapping, and slots derived on the GPU from the
         # block table (pa_scatter_kv_paged).
@@ -202,11 +222,12 @@ def time_workload(wl, steps, warmup, torch, pa, W, extras=False):
     return ms, wall / steps * 1e3, per_kernel, more
 
 
-def summarize(wl, ms, per_kernel):
+def summarize(wl, ms, per_kernel, kv_es=ES):
     """Throughputs of one step and of its attention kernel (the one launch
-    that runs both the prefill tiles and the split-KV decode items)."""
-    att_bytes, att_flops = attention_work(wl)
-    nbytes = att_bytes + scatter_work(wl)
+    that runs both the prefill tiles and the split-KV decode items); kv_es 1
+    for fp8 caches."""
+    att_bytes, att_flops = attention_work(wl, kv_es=kv_es)
+    nbytes = att_bytes + scatter_work(wl, kv_es=kv_es)
     t = ms * 1e-3
     dec_sel = (wl.q_lens * (wl.num_heads // wl.num_kv_heads) <= 16) & (wl.q_lens > 0)
     pf_sel = wl.q_lens * (wl.num_heads // wl.num_kv_heads) > 16
@@ -352,6 +373,9 @@ def main():
     ap.add_argument("--workload", default="mixed", choices=sorted(WORKLOADS))
     ap.add_argument("--no-extra", action="store_true", help="skip the decode/prefill figures")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--fp8", action="store_true",
+                    help="fp8 (e4m3) caches (pa_scatter_kv_fp8 + pa_attention_fp8); "
+                         "decode-shaped workloads only")
     ap.add_argument("--copy-only", action="store_true",
                     help="only the 2 GiB copy (reference for counter calibration)")
     args = ap.parse_args()
@@ -373,9 +397,12 @@ def main():
     copy_gbps = copy_bandwidth(torch)
 
     wl = W.by_index(WORKLOADS[args.workload])
+    if args.fp8 and (wl.q_lens * (wl.num_heads // wl.num_kv_heads)).max() > 16:
+        print("--fp8 needs a decode-shaped workload (every q_len * G <= 16)", file=sys.stderr)
+        sys.exit(2)
     ms, wall_ms, per_kernel, more = time_workload(wl, args.steps, args.warmup, torch, pa, W,
-                                                  extras=not args.no_extra)
-    head = summarize(wl, ms, per_kernel)
+                                                  extras=not args.no_extra, fp8=args.fp8)
+    head = summarize(wl, ms, per_kernel, kv_es=1 if args.fp8 else ES)
     if head.get("attention_bound") == "mfma":
         ach = head["attention_TFLOPs"]
         roof = {"bound": "mfma", "kernel": "attention_kernel", "achieved": ach, "peak": 2500.0,
@@ -386,8 +413,10 @@ def main():
         roof = {"bound": "hbm", "kernel": "attention_kernel", "achieved": ach, "peak": 8000.0,
                 "unit": "GB/s", "frac": ach / 8000.0,
                 "alg_bytes_per_launch": head.get("attention_alg_bytes")}
+    if args.fp8:
+        roof["kernel"] = "attention_kernel_fp8"
     roof["avg_launch_ms"] = per_kernel.get("attention", 0.0)
-    roof["traffic"] = measured_traffic(roof["kernel"], args.workload)
+    roof["traffic"] = measured_traffic(roof["kernel"], args.workload + ("_fp8" if args.fp8 else ""))
 
     extra = {}
     if not args.no_extra and args.workload == "mixed":
@@ -398,6 +427,18 @@ def main():
             extra[name] = summarize(w2, m2, k2)
             extra[name]["workload"] = w2.name
             extra[name]["step_reps"] = more2.get("step_reps")
+        # The pure-decode workload again on fp8 (e4m3) caches with per-channel
+        # scales (pa_scatter_kv_fp8 + pa_attention_fp8): half the cache bytes.
+        w2 = W.by_index(WORKLOADS["decode"])
+        m2, _, k2, more2 = time_workload(w2, max(5, args.steps // 2), 3, torch, pa, W,
+                                         extras=True, fp8=True)
+        e = summarize(w2, m2, k2, kv_es=1)
+        e["workload"] = w2.name + ", fp8 e4m3 caches with per-channel scales"
+        e["step_reps"] = more2.get("step_reps")
+        a16 = extra["decode"]["kernel_ms"].get("attention", 0.0)
+        a8 = e["kernel_ms"].get("attention", 0.0)
+        e["attention_speedup_vs_16bit_cache"] = a16 / a8 if a8 > 0 else None
+        extra["decode_fp8"] = e
 
     line = {
         "metric": "paged-attn decode HBM TB/s + prefill TFLOP/s, % of MI355X roofline",
