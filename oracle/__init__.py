@@ -17,5 +17,6 @@ from .pa_oracle import (  # noqa: F401
     sdpa,
     seq_of_token,
     slots_from_block_table,
+    softcap_scores,
     validate_metadata,
 )

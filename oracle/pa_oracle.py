@@ -39,7 +39,11 @@ head_size]; ``seqlens_kv[b]`` is the total KV length including this step's
 new tokens; the causal mask is bottom-right aligned (key j is visible to new
 query row i iff j <= past_b + i); ``scale`` is used exactly as the float32
 value that crosses the C ABI, 0 included; a negative slot means "do not
-write this token".
+write this token".  The page also names two attention options it leaves
+undefined (its v1 rejects them up front, its roadmap lifts them in phase 2):
+``softcap`` c > 0 caps each scaled score as c * tanh(s / c) before the mask
+and the softmax, and ``local_window_size`` W > 0 limits new row i to its
+last W keys, past_b + i - W < j <= past_b + i.
 
 Every function here is pinned by tests in tests/test_oracle_pins.py against
 the printed examples, closed forms, invariants and brute force.
@@ -60,15 +64,27 @@ def _f64(x):
 # Core SDPA, as FlexAttention defines it ([FLEX] "FlexAttention Computation").
 # ----------------------------------------------------------------------------
 
-def sdpa(q, k, v, scale, visible=None):
+def softcap_scores(scores, softcap):
+    """The score soft cap: c * tanh(s / c) on the scaled scores for c > 0
+    (a score modifier in [FLEX]'s sense; the PagedAttention page names the
+    ``softcap`` option without defining it, this is the reading taken);
+    c <= 0 leaves the scores unchanged."""
+    c = float(np.float32(softcap))
+    if c <= 0.0:
+        return scores
+    return c * np.tanh(scores / c)
+
+
+def sdpa(q, k, v, scale, visible=None, softcap=0.0):
     """Scaled dot-product attention for one head.
 
     q: [Sq, D], k: [Skv, D], v: [Skv, Dv]; ``visible``: bool [Sq, Skv] or
-    None.  Masked scores become -inf before the softmax ([FLEX], masking
-    written as -inf).  Returns float64 [Sq, Dv].
+    None.  Scores are scaled, soft-capped (``softcap`` > 0), then masked
+    scores become -inf before the softmax ([FLEX], masking written as -inf).
+    Returns float64 [Sq, Dv].
     """
     q, k, v = _f64(q), _f64(k), _f64(v)
-    scores = (q @ k.T) * float(scale)
+    scores = softcap_scores((q @ k.T) * float(scale), softcap)
     if visible is not None:
         visible = np.asarray(visible, dtype=bool)
         if not visible.any(axis=-1).all():
@@ -174,7 +190,8 @@ def gather_sequence(cache, table_row, length, block_size):
 
 
 def _attention_impl(q, cu_seqlens_q, seqlens_kv, block_table, k_cache, v_cache,
-                    scale, num_heads, num_kv_heads, block_size, past_of):
+                    scale, num_heads, num_kv_heads, block_size, past_of, softcap=0.0,
+                    local_window_size=0):
     cu = np.asarray(cu_seqlens_q, dtype=np.int64)
     L = np.asarray(seqlens_kv, dtype=np.int64)
     table = np.asarray(block_table)
@@ -202,15 +219,17 @@ def _attention_impl(q, cu_seqlens_q, seqlens_kv, block_table, k_cache, v_cache,
         i = np.arange(q_len)[:, None]
         j = np.arange(int(L[b]))[None, :]
         visible = j <= past + i                  # causal length past + i + 1
+        if local_window_size > 0:                # the last W keys up to the row's own
+            visible &= j > past + i - int(local_window_size)
         rows = slice(int(cu[b]), int(cu[b + 1]))
         for h in range(num_heads):
             kh = h // group
-            out[rows, h] = sdpa(q[rows, h], Kb[:, kh], Vb[:, kh], scale, visible)
+            out[rows, h] = sdpa(q[rows, h], Kb[:, kh], Vb[:, kh], scale, visible, softcap)
     return out
 
 
 def attention(q, cu_seqlens_q, seqlens_kv, block_table, k_cache, v_cache,
-              scale, num_heads, num_kv_heads, block_size):
+              scale, num_heads, num_kv_heads, block_size, softcap=0.0, local_window_size=0):
     """Paged causal GQA attention over packed variable-length queries.
 
     q: [T, Hq, D] (or [T, Hq*D]); cu_seqlens_q: [B+1]; seqlens_kv: [B] (total
@@ -218,10 +237,17 @@ def attention(q, cu_seqlens_q, seqlens_kv, block_table, k_cache, v_cache,
     ``scatter_kv``.  For each sequence b with q_len_b = cu[b+1]-cu[b] and
     past_b = seqlens_kv[b] - q_len_b, new query row i attends to KV positions
     0..past_b+i, walking the block table.  Returns float64 [T, Hq, D].
+
+    Options the PagedAttention page names without defining (readings taken):
+    ``softcap`` c > 0 replaces each scaled score s by c * tanh(s / c) before
+    the mask and softmax; ``local_window_size`` W > 0 restricts row i to the
+    last W of its keys, past_b + i - W < j <= past_b + i (the row's own key
+    included).  0 disables either.
     """
     return _attention_impl(q, cu_seqlens_q, seqlens_kv, block_table, k_cache,
                            v_cache, scale, num_heads, num_kv_heads, block_size,
-                           past_of=lambda L, q_len, max_q: L - q_len)
+                           past_of=lambda L, q_len, max_q: L - q_len, softcap=softcap,
+                           local_window_size=local_window_size)
 
 
 def attention_buggy_clamp(q, cu_seqlens_q, seqlens_kv, block_table, k_cache,
@@ -235,12 +261,15 @@ def attention_buggy_clamp(q, cu_seqlens_q, seqlens_kv, block_table, k_cache,
 
 
 def attention_loops(q, cu_seqlens_q, seqlens_kv, block_table, k_cache, v_cache,
-                    scale, num_heads, num_kv_heads, block_size):
+                    scale, num_heads, num_kv_heads, block_size, softcap=0.0,
+                    local_window_size=0):
     """Pure-Python brute force of ``attention`` for tiny inputs.
 
     Walks every (token, head, key) with scalar float arithmetic and reads each
-    K/V row through block_table[b][j // block_size], offset j % block_size.
+    K/V row through block_table[b][j // block_size], offset j % block_size;
+    the window is a key range, the soft cap a scalar math.tanh.
     """
+    cap = float(np.float32(softcap))
     cu = [int(x) for x in cu_seqlens_q]
     L = [int(x) for x in seqlens_kv]
     T = cu[-1]
@@ -256,22 +285,27 @@ def attention_loops(q, cu_seqlens_q, seqlens_kv, block_table, k_cache, v_cache,
         q_len = cu[b + 1] - cu[b]
         past = L[b] - q_len
         i = t - cu[b]
+        j0 = max(0, past + i + 1 - local_window_size) if local_window_size > 0 else 0
+        keys = list(range(j0, past + i + 1))
         for h in range(num_heads):
             kh = h // group
             scores = []
-            for j in range(past + i + 1):
+            for j in keys:
                 blk = int(block_table[b][j // block_size])
                 krow = k_cache[blk][j % block_size][kh]
                 s = 0.0
                 for d in range(D):
                     s += float(q[t, h, d]) * float(krow[d])
-                scores.append(s * scale)
+                s *= scale
+                if cap > 0.0:
+                    s = cap * math.tanh(s / cap)
+                scores.append(s)
             m = max(scores)
             w = [math.exp(s - m) for s in scores]
             tot = sum(w)
             for d in range(D):
                 acc = 0.0
-                for j, wj in enumerate(w):
+                for j, wj in zip(keys, w):
                     blk = int(block_table[b][j // block_size])
                     acc += wj * float(v_cache[blk][j % block_size][kh][d])
                 out[t, h, d] = acc / tot
