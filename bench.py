@@ -58,7 +58,7 @@ def roofline_time(nbytes, flops):
 
 
 # ------------------------------------------------------------- GPU side
-def setup(wl, torch, pa, W, fp8=False):
+def setup(wl, torch, pa, W, fp8=False, opts=None):
     vals = W.make_values(wl, device="cuda", backend="torch")
     dt = W.torch_dtype(wl)
     shape = (wl.num_blocks, wl.block_size, wl.num_kv_heads, wl.head_size)
@@ -80,7 +80,8 @@ def setup(wl, torch, pa, W, fp8=False):
               slots=torch.from_numpy(wl.slot_mapping.astype(np.int32)).cuda(),
               cu=torch.from_numpy(wl.cu_seqlens_q).cuda(),
               lens=torch.from_numpy(wl.seqlens_kv.astype(np.int32)).cuda(),
-              table=torch.from_numpy(wl.block_table.astype(np.int32)).cuda(), vals=vals, **extra)
+              table=torch.from_numpy(wl.block_table.astype(np.int32)).cuda(), vals=vals,
+              opts=dict(opts or {}), **extra)
     st["out"] = torch.empty((wl.num_tokens, wl.num_heads, wl.head_size), dtype=dt, device="cuda")
     n = pa.pa_attention_workspace_size(wl.num_seqs, wl.num_tokens, wl.max_blocks_per_seq,
                                        wl.num_heads, wl.num_kv_heads, wl.head_size,
@@ -96,11 +97,12 @@ def step(wl, st, pa):
                              st["vc"])
         pa.pa_attention_fp8(st["q"], st["cu"], st["lens"], st["table"], st["kc"], st["vc"],
                             st["ks"], st["vs"], wl.scale, wl.num_heads, wl.num_kv_heads,
-                            st["max_q_len"], out=st["out"], workspace=st["ws"])
+                            st["max_q_len"], out=st["out"], workspace=st["ws"], **st["opts"])
         return
     pa.pa_scatter_kv(st["k_new"], st["v_new"], st["slots"], st["kc"], st["vc"])
     pa.pa_attention(st["q"], st["cu"], st["lens"], st["table"], st["kc"], st["vc"], wl.scale,
-                    wl.num_heads, wl.num_kv_heads, out=st["out"], workspace=st["ws"])
+                    wl.num_heads, wl.num_kv_heads, out=st["out"], workspace=st["ws"],
+                    **st["opts"])
 
 
 SCRUB_BYTES = 512 << 20     # written between separately timed reps (larger than the 256 MB MALL)
@@ -141,12 +143,13 @@ def sub_batch(wl, st, sel, torch, pa):
     return sub
 
 
-def time_workload(wl, steps, warmup, torch, pa, W, extras=False, fp8=False):
+def time_workload(wl, steps, warmup, torch, pa, W, extras=False, fp8=False, opts=None):
     """Back-to-back timing of `steps` steps (the headline figure) and the
     per-kernel averages; with `extras`, also per-rep scrubbed timing of the
     step and, for a batch that mixes both kinds, its decode-only and
-    prefill-only sub-batches timed as separate pa_attention calls."""
-    st = setup(wl, torch, pa, W, fp8=fp8)
+    prefill-only sub-batches timed as separate pa_attention calls.  `opts`:
+    attention options (softcap, local_window_size) of every call."""
+    st = setup(wl, torch, pa, W, fp8=fp8, opts=opts)
     for _ in range(warmup):
         step(wl, st, pa)
     torch.cuda.synchronize()
@@ -200,7 +203,8 @@ def time_workload(wl, steps, warmup, torch, pa, W, extras=False, fp8=False):
                 sb = sub_batch(wl, st, sel, torch, pa)
                 call = lambda sb=sb: pa.pa_attention(  # noqa: E731
                     sb["q"], sb["cu"], sb["lens"], sb["table"], sb["kc"], sb["vc"], wl.scale,
-                    wl.num_heads, wl.num_kv_heads, out=sb["out"], workspace=sb["ws"])
+                    wl.num_heads, wl.num_kv_heads, out=sb["out"], workspace=sb["ws"],
+                    **st["opts"])
                 for _ in range(3):
                     call()
                 r = per_rep_times(call, steps, torch, scrub)
@@ -301,10 +305,11 @@ def copy_bandwidth(torch, nbytes=2 << 30, reps=10):
 
 
 # ------------------------------------------------------------- CPU baseline
-def cpu_baseline(wl, W, torch, budget_s=20.0):
+def cpu_baseline(wl, W, torch, budget_s=20.0, opts=None):
     """The fp64 oracle (as it stands) on a bounded sample of the workload:
     the first decode sequences and, if any, the first prefill chunks;
-    reported in the metric's unit and as tokens/s."""
+    reported in the metric's unit and as tokens/s.  `opts`: the attention
+    options of the GPU run."""
     import oracle
     f64 = lambda t: t.float().cpu().numpy().astype(np.float64)  # noqa: E731
     vals = W.make_values(wl, device="cuda", backend="torch")
@@ -341,7 +346,7 @@ def cpu_baseline(wl, W, torch, budget_s=20.0):
     t_scatter = time.perf_counter() - t0
     t0 = time.perf_counter()
     oracle.attention(q, sub_cu, sub_lens, sub_table, kc, vc, wl.scale, wl.num_heads,
-                     wl.num_kv_heads, wl.block_size)
+                     wl.num_kv_heads, wl.block_size, **(opts or {}))
     t = time.perf_counter() - t0
     sel = np.zeros(wl.num_seqs, dtype=bool)
     sel[picks] = True
@@ -376,6 +381,10 @@ def main():
     ap.add_argument("--fp8", action="store_true",
                     help="fp8 (e4m3) caches (pa_scatter_kv_fp8 + pa_attention_fp8); "
                          "decode-shaped workloads only")
+    ap.add_argument("--softcap", type=float, default=0.0,
+                    help="score soft cap c of every attention call (0: off)")
+    ap.add_argument("--window", type=int, default=0,
+                    help="sliding window (local_window_size) of every attention call (0: off)")
     ap.add_argument("--copy-only", action="store_true",
                     help="only the 2 GiB copy (reference for counter calibration)")
     args = ap.parse_args()
@@ -400,8 +409,14 @@ def main():
     if args.fp8 and (wl.q_lens * (wl.num_heads // wl.num_kv_heads)).max() > 16:
         print("--fp8 needs a decode-shaped workload (every q_len * G <= 16)", file=sys.stderr)
         sys.exit(2)
+    opts = {}
+    if args.softcap > 0:
+        opts["softcap"] = args.softcap
+    if args.window > 0:
+        opts["local_window_size"] = args.window
     ms, wall_ms, per_kernel, more = time_workload(wl, args.steps, args.warmup, torch, pa, W,
-                                                  extras=not args.no_extra, fp8=args.fp8)
+                                                  extras=not args.no_extra, fp8=args.fp8,
+                                                  opts=opts)
     head = summarize(wl, ms, per_kernel, kv_es=1 if args.fp8 else ES)
     if head.get("attention_bound") == "mfma":
         ach = head["attention_TFLOPs"]
@@ -439,6 +454,21 @@ def main():
         a8 = e["kernel_ms"].get("attention", 0.0)
         e["attention_speedup_vs_16bit_cache"] = a16 / a8 if a8 > 0 else None
         extra["decode_fp8"] = e
+        # The headline batch again with the score options on: attention time
+        # against the plain call (a window also cuts the keys read).
+        if not opts:
+            a0 = head["kernel_ms"].get("attention", 0.0)
+            o = {}
+            for name, kw in (("softcap_50", dict(softcap=50.0)),
+                             ("window_4096", dict(local_window_size=4096)),
+                             ("softcap_50_window_4096", dict(softcap=50.0,
+                                                             local_window_size=4096))):
+                m2, _, k2, _ = time_workload(wl, max(5, args.steps // 2), 3, torch, pa, W,
+                                             opts=kw)
+                a2 = k2.get("attention", 0.0)
+                o[name] = {"ms_per_step": m2, "attention_ms": a2,
+                           "attention_time_vs_plain": a2 / a0 if a0 > 0 else None}
+            extra["options"] = o
 
     line = {
         "metric": "paged-attn decode HBM TB/s + prefill TFLOP/s, % of MI355X roofline",
@@ -450,7 +480,7 @@ def main():
         "dtype": wl.dtype, "data": "synthetic",
         "config": {"workload": wl.name, "num_seqs": wl.num_seqs, "num_tokens": wl.num_tokens,
                    "step": "pa_scatter_kv(new tokens) + pa_attention(whole batch)",
-                   "parallelism": "single GPU"},
+                   "parallelism": "single GPU", **opts},
         "tokens_per_s": head["tokens_per_s"],
         "attention_TBps": head.get("attention_TBps"),
         "attention_TFLOPs": head.get("attention_TFLOPs"),
@@ -465,8 +495,11 @@ def main():
         "scatter": more.get("scatter"),
         "extra": extra,
     }
+    if opts.get("local_window_size"):
+        line["note"] = ("algorithmic bytes and flops count the plain causal work; the window "
+                        "reads and computes less, so the rates above overstate it")
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(wl, W, torch)
+        line["cpu_baseline"] = cpu_baseline(wl, W, torch, opts=opts)
     print(json.dumps(line), flush=True)
 
 

@@ -192,6 +192,20 @@ size_t pa_attention_workspace_size(int32_t num_seqs, int64_t num_tokens,
  * out          [num_tokens, num_heads, head_size] dtype, fully written.
  * scale        finite float, used exactly as given (0 gives the mean of the
  *              visible V rows).
+ * softcap      score soft cap c: finite, >= 0.  c > 0 replaces every scaled
+ *              score x = scale * q . K_j by c * tanh(x / c) before the mask
+ *              and the softmax; 0 turns it off.  The PagedAttention page
+ *              names the option ("Description"; "Roadmap", phase 2 lifts
+ *              it) without defining it: this is the library's reading.
+ *              PA_ERR_INVALID_ARGUMENT for a negative or non-finite c, or
+ *              when scale / c overflows float.
+ * local_window_size
+ *              sliding window W: W > 0 limits new row i to its last W keys,
+ *              past_b + i - W < j <= past_b + i (same page and sections,
+ *              same reading); W <= 0 turns it off.  Whole 1024-key splits
+ *              (rows of sequences with q_len_b * G <= 16) and 64-key tiles
+ *              (other rows) before the window of a sequence's first new
+ *              row are skipped: those cache slots are not read.
  * workspace    device buffer of at least pa_attention_workspace_size(...)
  *              bytes, 256-byte aligned; contents need no initialisation and
  *              are scratch (plan lists, split-KV partial results).
@@ -206,7 +220,8 @@ pa_status_t pa_attention(const void* q, const int32_t* cu_seqlens_q,
                          const void* k_cache, const void* v_cache, void* out,
                          int32_t num_seqs, int64_t num_tokens,
                          int32_t max_blocks_per_seq, int64_t num_blocks,
-                         float scale, int32_t num_heads, int32_t num_kv_heads,
+                         float scale, float softcap, int32_t local_window_size,
+                         int32_t num_heads, int32_t num_kv_heads,
                          int32_t head_size, int32_t block_size, int32_t dtype,
                          void* workspace, size_t workspace_bytes,
                          void* stream);
@@ -252,7 +267,8 @@ pa_status_t pa_scatter_kv_fp8(const void* k_new, const void* v_new,
  * dequantized values e4m3(code) * scale[h / G][d] (section "Roadmap" of
  * the PagedAttention page, phase 3, quantized KV in the decode path).
  *
- * Arguments as for pa_attention, plus:
+ * Arguments (softcap and local_window_size included) as for pa_attention,
+ * plus:
  * k_cache,
  * v_cache      [num_blocks, block_size, num_kv_heads, head_size] uint8
  *              e4m3 codes; read only.
@@ -274,7 +290,8 @@ pa_status_t pa_attention_fp8(const void* q, const int32_t* cu_seqlens_q,
                              const float* k_scale, const float* v_scale, void* out,
                              int32_t num_seqs, int64_t num_tokens, int32_t max_q_len,
                              int32_t max_blocks_per_seq, int64_t num_blocks,
-                             float scale, int32_t num_heads, int32_t num_kv_heads,
+                             float scale, float softcap, int32_t local_window_size,
+                             int32_t num_heads, int32_t num_kv_heads,
                              int32_t head_size, int32_t block_size, int32_t dtype,
                              void* workspace, size_t workspace_bytes, void* stream);
 

@@ -129,9 +129,12 @@ class DequantizedCache:
 
 
 def attention_fp8(q, cu_seqlens_q, seqlens_kv, block_table, k_codes, v_codes, k_scale,
-                  v_scale, scale, num_heads, num_kv_heads, block_size):
+                  v_scale, scale, num_heads, num_kv_heads, block_size, softcap=0.0,
+                  local_window_size=0):
     """Paged attention over fp8 caches: the 16-bit path's attention over the
-    dequantized K and V (blocks dequantized as the block table is walked)."""
+    dequantized K and V (blocks dequantized as the block table is walked),
+    with the same score options."""
     return _attention(q, cu_seqlens_q, seqlens_kv, block_table,
                       DequantizedCache(k_codes, k_scale), DequantizedCache(v_codes, v_scale),
-                      scale, num_heads, num_kv_heads, block_size)
+                      scale, num_heads, num_kv_heads, block_size, softcap=softcap,
+                      local_window_size=local_window_size)

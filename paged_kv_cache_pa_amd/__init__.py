@@ -104,13 +104,16 @@ def pa_attention_workspace_size(num_seqs, num_tokens, max_blocks_per_seq, num_he
 
 
 def pa_attention(q, cu_seqlens_q, seqlens_kv, block_table, k_cache, v_cache, scale,
-                 num_heads, num_kv_heads, out=None, workspace=None, stream=None):
+                 num_heads, num_kv_heads, out=None, workspace=None, stream=None, softcap=0.0,
+                 local_window_size=0):
     """Paged causal GQA attention.
 
     q [T, Hq, D] (or [T, Hq*D]); cu_seqlens_q int32 [B+1]; seqlens_kv int32
     [B]; block_table int32 [B, MB]; caches [NB, bs, Hk, D].  Returns out
     [T, Hq, D].  ``workspace`` is a uint8 GPU tensor of at least
     pa_attention_workspace_size(...) bytes; one is allocated if omitted.
+    ``softcap`` c > 0 caps scaled scores as c tanh(x / c);
+    ``local_window_size`` W > 0 limits each row to its last W keys.
     """
     import torch
     T = q.shape[0]
@@ -135,7 +138,8 @@ def pa_attention(q, cu_seqlens_q, seqlens_kv, block_table, k_cache, v_cache, sca
         _dev(q, "q"), _dev(cu_seqlens_q, "cu_seqlens_q", torch.int32),
         _dev(seqlens_kv, "seqlens_kv", torch.int32), _dev(block_table, "block_table", torch.int32),
         _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), _dev(out, "out"), B, T, MB, nb,
-        float(scale), num_heads, num_kv_heads, d, bs, _dtype_code(q),
+        float(scale), float(softcap), int(local_window_size), num_heads, num_kv_heads, d, bs,
+        _dtype_code(q),
         _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
         _stream_ptr(q, stream)))
     return out
@@ -164,10 +168,11 @@ def pa_scatter_kv_fp8(k_new, v_new, slot_mapping, k_scale, v_scale, k_cache, v_c
 
 def pa_attention_fp8(q, cu_seqlens_q, seqlens_kv, block_table, k_cache, v_cache, k_scale,
                      v_scale, scale, num_heads, num_kv_heads, max_q_len, out=None,
-                     workspace=None, stream=None):
+                     workspace=None, stream=None, softcap=0.0, local_window_size=0):
     """pa_attention over fp8 (e4m3) caches [NB, bs, Hk, D] (uint8 codes) with
     float32 per-channel scales [Hk, D], for batches whose every q_len * G is
-    at most 16 (``max_q_len`` is a host-side bound of q_len)."""
+    at most 16 (``max_q_len`` is a host-side bound of q_len).  ``softcap``
+    and ``local_window_size`` as for pa_attention."""
     import torch
     T = q.shape[0]
     d = k_cache.shape[-1]
@@ -193,8 +198,8 @@ def pa_attention_fp8(q, cu_seqlens_q, seqlens_kv, block_table, k_cache, v_cache,
         _dev(seqlens_kv, "seqlens_kv", torch.int32), _dev(block_table, "block_table", torch.int32),
         _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
         _dev(k_scale, "k_scale", torch.float32), _dev(v_scale, "v_scale", torch.float32),
-        _dev(out, "out"), B, T, int(max_q_len), MB, nb, float(scale), num_heads, num_kv_heads, d,
-        bs, _dtype_code(q), _dev(workspace, "workspace"),
+        _dev(out, "out"), B, T, int(max_q_len), MB, nb, float(scale), float(softcap),
+        int(local_window_size), num_heads, num_kv_heads, d, bs, _dtype_code(q), _dev(workspace, "workspace"),
         workspace.numel() * workspace.element_size(), _stream_ptr(q, stream)))
     return out
 

@@ -58,11 +58,11 @@ def lib():
     L.pa_seqlens_from_past.restype = i32
     L.pa_attention_workspace_size.argtypes = [i32, i64, i32, i32, i32, i32, i32]
     L.pa_attention_workspace_size.restype = sz
-    L.pa_attention.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i64, f32, i32, i32,
-                               i32, i32, i32, vp, sz, vp]
+    L.pa_attention.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i64, f32, f32, i32,
+                               i32, i32, i32, i32, i32, vp, sz, vp]
     L.pa_attention.restype = i32
     L.pa_attention_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i64,
-                                   f32, i32, i32, i32, i32, i32, vp, sz, vp]
+                                   f32, f32, i32, i32, i32, i32, i32, i32, vp, sz, vp]
     L.pa_attention_fp8.restype = i32
     L.pa_validate_metadata.argtypes = [vp, vp, vp, vp, i32, i64, i32, i64, i32,
                                        ctypes.POINTER(ctypes.c_uint32), vp]

@@ -303,7 +303,8 @@ static pa_status_t attention_impl(const void* q, const int32_t* cu_seqlens_q,
                                   const void* k_cache, const void* v_cache, const float* k_scale,
                                   const float* v_scale, void* out, int32_t num_seqs,
                                   int64_t num_tokens, int32_t max_blocks_per_seq,
-                                  int64_t num_blocks, float scale, int32_t num_heads,
+                                  int64_t num_blocks, float scale, float softcap,
+                                  int32_t local_window_size, int32_t num_heads,
                                   int32_t num_kv_heads, int32_t head_size, int32_t block_size,
                                   int32_t dtype, void* workspace, size_t workspace_bytes,
                                   void* stream, bool kv8) {
@@ -317,6 +318,13 @@ static pa_status_t attention_impl(const void* q, const int32_t* cu_seqlens_q,
   if (num_blocks * (int64_t)block_size > INT32_MAX)
     return fail(PA_ERR_NOT_IMPLEMENTED, "num_blocks * block_size exceeds INT32_MAX");
   if (!isfinite(scale)) return fail(PA_ERR_INVALID_ARGUMENT, "scale is not finite");
+  if (!(softcap >= 0.f) || !isfinite(softcap))
+    return fail(PA_ERR_INVALID_ARGUMENT, "softcap must be finite and >= 0");
+  // Soft-cap constants (log2 units): cap_k = 2 (scale / c) log2(e) must be a
+  // finite float for the kernels' exp2 form.
+  const double cap_k = softcap > 0.f ? 2.0 * ((double)scale / softcap) * (double)pa::kLog2e : 0.0;
+  if (!(fabs(cap_k) <= 3.0e38))
+    return fail(PA_ERR_INVALID_ARGUMENT, "softcap too small for this scale (scale / softcap overflows)");
   if (num_tokens == 0) return PA_OK;
   if (!q || !cu_seqlens_q || !seqlens_kv || !block_table || !k_cache || !v_cache || !out)
     return fail(PA_ERR_INVALID_ARGUMENT, "null pointer argument");
@@ -349,6 +357,7 @@ static pa_status_t attention_impl(const void* q, const int32_t* cu_seqlens_q,
   pl.num_kv_heads = num_kv_heads;
   pl.tokens_per_tile = tq;
   pl.decode_only = kv8 ? 1 : 0;
+  pl.window = local_window_size > 0 ? local_window_size : 0;
   // Persistent grid: what the device holds at once, but no more groups than
   // there are prefill items plus groups of 8 decode waves.
   const int64_t max_groups =
@@ -384,6 +393,9 @@ static pa_status_t attention_impl(const void* q, const int32_t* cu_seqlens_q,
   a.tokens_per_tile = tq;
   a.scale_log2 = scale * pa::kLog2e;
   a.inv_group = 1.0f / (float)G;
+  a.cap_k = (float)cap_k;
+  a.cap_b = softcap > 0.f ? softcap * pa::kLog2e : 0.f;
+  a.window = pl.window;
 
   e = timed(2, st, [&] { return pa::launch_attention(a, dtype, head_size, workers, st, kv8); });
   if (e != hipSuccess) return hip_fail(e, "attention launch");
@@ -398,13 +410,13 @@ pa_status_t pa_attention(const void* q, const int32_t* cu_seqlens_q, const int32
                          const int32_t* block_table, const void* k_cache, const void* v_cache,
                          void* out, int32_t num_seqs, int64_t num_tokens,
                          int32_t max_blocks_per_seq, int64_t num_blocks, float scale,
-                         int32_t num_heads, int32_t num_kv_heads, int32_t head_size,
-                         int32_t block_size, int32_t dtype, void* workspace,
-                         size_t workspace_bytes, void* stream) {
+                         float softcap, int32_t local_window_size, int32_t num_heads,
+                         int32_t num_kv_heads, int32_t head_size, int32_t block_size,
+                         int32_t dtype, void* workspace, size_t workspace_bytes, void* stream) {
   g_err[0] = 0;
   return attention_impl(q, cu_seqlens_q, seqlens_kv, block_table, k_cache, v_cache, nullptr,
                         nullptr, out, num_seqs, num_tokens, max_blocks_per_seq, num_blocks, scale,
-                        num_heads, num_kv_heads, head_size, block_size, dtype, workspace,
+                        softcap, local_window_size, num_heads, num_kv_heads, head_size, block_size, dtype, workspace,
                         workspace_bytes, stream, false);
 }
 
@@ -413,7 +425,8 @@ pa_status_t pa_attention_fp8(const void* q, const int32_t* cu_seqlens_q,
                              const void* k_cache, const void* v_cache, const float* k_scale,
                              const float* v_scale, void* out, int32_t num_seqs,
                              int64_t num_tokens, int32_t max_q_len, int32_t max_blocks_per_seq,
-                             int64_t num_blocks, float scale, int32_t num_heads,
+                             int64_t num_blocks, float scale, float softcap,
+                             int32_t local_window_size, int32_t num_heads,
                              int32_t num_kv_heads, int32_t head_size, int32_t block_size,
                              int32_t dtype, void* workspace, size_t workspace_bytes,
                              void* stream) {
@@ -426,7 +439,7 @@ pa_status_t pa_attention_fp8(const void* q, const int32_t* cu_seqlens_q,
                 (long long)max_q_len * (num_heads / num_kv_heads), pa::kDecodeCols);
   return attention_impl(q, cu_seqlens_q, seqlens_kv, block_table, k_cache, v_cache, k_scale,
                         v_scale, out, num_seqs, num_tokens, max_blocks_per_seq, num_blocks, scale,
-                        num_heads, num_kv_heads, head_size, block_size, dtype, workspace,
+                        softcap, local_window_size, num_heads, num_kv_heads, head_size, block_size, dtype, workspace,
                         workspace_bytes, stream, true);
 }
 

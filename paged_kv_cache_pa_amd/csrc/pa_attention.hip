@@ -22,27 +22,30 @@
 
 namespace pa {
 
-template <typename T, int D>
+// CAP / WIN: the score soft cap / the sliding window is on (separate
+// instantiations, so the plain kernel carries no code for either).
+template <typename T, int D, bool CAP, bool WIN>
 __global__ __launch_bounds__(512, 1) void attention_kernel(AttnArgs a) {
   const bool prefill_first = (int)blockIdx.x < a.counters[kPrefillFirst];
   // Straight-line phases (no loop around them, so nothing of one body is
   // hoisted to stay live across the other); the small decode body appears
   // twice, the large prefill body once.
-  if (!prefill_first) decode_items<T, D>(a);
-  prefill_items<T, D>(a);
-  if (prefill_first) decode_items<T, D>(a);
+  if (!prefill_first) decode_items<T, D, false, CAP, WIN>(a);
+  prefill_items<T, D, CAP, WIN>(a);
+  if (prefill_first) decode_items<T, D, false, CAP, WIN>(a);
 }
 
 // fp8 caches: decode items only (the plan gives every sequence the decode
 // path); waves are independent and use no LDS.
-template <typename T, int D>
+template <typename T, int D, bool CAP, bool WIN>
 __global__ __launch_bounds__(512) void attention_kernel_fp8(AttnArgs a) {
-  decode_items<T, D, true>(a);
+  decode_items<T, D, true, CAP, WIN>(a);
 }
 
 template <typename T, int D>
 static const void* attention_fn(bool kv8) {
-  return kv8 ? (const void*)&attention_kernel_fp8<T, D> : (const void*)&attention_kernel<T, D>;
+  return kv8 ? (const void*)&attention_kernel_fp8<T, D, false, false>
+             : (const void*)&attention_kernel<T, D, false, false>;
 }
 
 static const void* attention_fn(int dtype, int head_size, bool kv8) {
@@ -51,25 +54,42 @@ static const void* attention_fn(int dtype, int head_size, bool kv8) {
   return head_size == 128 ? attention_fn<BF16, 128>(kv8) : attention_fn<BF16, 64>(kv8);
 }
 
+// One work-group per CU whatever the variant (launch bounds 512, 1), so the
+// uncapped kernel sizes the grid for all of them.
 int attention_workers(int dtype, int head_size, int num_cus, bool kv8) {
   return resident_blocks(attention_fn(dtype, head_size, kv8), num_cus, 512);
+}
+
+template <typename T, int D>
+static void attention_launch(const AttnArgs& a, dim3 g, hipStream_t st, bool kv8) {
+  const dim3 b(512);
+  const bool cap = a.cap_b > 0.f, win = a.window > 0;
+  if (kv8 && cap && win)
+    hipLaunchKernelGGL((attention_kernel_fp8<T, D, true, true>), g, b, 0, st, a);
+  else if (kv8 && cap)
+    hipLaunchKernelGGL((attention_kernel_fp8<T, D, true, false>), g, b, 0, st, a);
+  else if (kv8 && win)
+    hipLaunchKernelGGL((attention_kernel_fp8<T, D, false, true>), g, b, 0, st, a);
+  else if (kv8)
+    hipLaunchKernelGGL((attention_kernel_fp8<T, D, false, false>), g, b, 0, st, a);
+  else if (cap && win)
+    hipLaunchKernelGGL((attention_kernel<T, D, true, true>), g, b, 0, st, a);
+  else if (cap)
+    hipLaunchKernelGGL((attention_kernel<T, D, true, false>), g, b, 0, st, a);
+  else if (win)
+    hipLaunchKernelGGL((attention_kernel<T, D, false, true>), g, b, 0, st, a);
+  else
+    hipLaunchKernelGGL((attention_kernel<T, D, false, false>), g, b, 0, st, a);
 }
 
 template <typename T>
 static hipError_t attention_dispatch(const AttnArgs& a, int head_size, int grid, hipStream_t st,
                                      bool kv8) {
-  const dim3 g((unsigned)grid), b(512);
-  if (kv8) {
-    if (head_size == 128)
-      hipLaunchKernelGGL((attention_kernel_fp8<T, 128>), g, b, 0, st, a);
-    else
-      hipLaunchKernelGGL((attention_kernel_fp8<T, 64>), g, b, 0, st, a);
-  } else {
-    if (head_size == 128)
-      hipLaunchKernelGGL((attention_kernel<T, 128>), g, b, 0, st, a);
-    else
-      hipLaunchKernelGGL((attention_kernel<T, 64>), g, b, 0, st, a);
-  }
+  const dim3 g((unsigned)grid);
+  if (head_size == 128)
+    attention_launch<T, 128>(a, g, st, kv8);
+  else
+    attention_launch<T, 64>(a, g, st, kv8);
   return hipGetLastError();
 }
 

@@ -54,7 +54,9 @@ namespace pa {
 
 // Runs decode work items on the calling wave until the decode counter is
 // exhausted.  Every wave is independent (no barriers, no LDS).
-template <typename T, int D, bool KV8 = false>
+// CAP / WIN: the score soft cap / the sliding window is on (compile-time, so
+// the plain score loop carries no selects for them).
+template <typename T, int D, bool KV8 = false, bool CAP = false, bool WIN = false>
 __device__ __forceinline__ void decode_items(const AttnArgs& a) {
   constexpr int NS = D / 32;    // QK^T contraction steps (8 halfs per lane)
   constexpr int NT = D / 16;    // O^T tiles; also halfs per lane per V row
@@ -87,6 +89,7 @@ __device__ __forceinline__ void decode_items(const AttnArgs& a) {
     const int past = L - ql;
     const int ncols = ql * G;
     const int nsplit = (L + kSplitKeys - 1) / kSplitKeys;
+    const int live = nsplit - (WIN ? first_live_split(L, ql, a.window) : 0);   // splits with items
     const int k0 = split * kSplitKeys;
     const int k1 = min(L, k0 + kSplitKeys);
 
@@ -123,8 +126,10 @@ __device__ __forceinline__ void decode_items(const AttnArgs& a) {
       }
     }
     // Causal limit of column n: token n / G sees keys <= past + n / G
-    // (padding columns see every key and are never stored).
+    // (padding columns see every key and are never stored); with a sliding
+    // window W it sees only keys > col_limit - W.
     const int col_limit = past + div_small(r16, a.inv_group);
+    const int col_low = col_limit - (WIN ? a.window : 0);
 
     // Block ids of this split, one per lane.
     const int blk0 = k0 >> a.block_shift;
@@ -202,8 +207,13 @@ __device__ __forceinline__ void decode_items(const AttnArgs& a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int key = c0 + 4 * kq + i;
-        const bool vis = key < k1 && key <= col_limit;
-        sv[i] = vis ? sc[i] * a.scale_log2 : -INFINITY;
+        bool vis = key < k1 && key <= col_limit;
+        if constexpr (WIN) vis = vis && key > col_low;
+        // soft cap: c tanh(scale s / c), in log2 units (see AttnArgs)
+        const float s2 = CAP ? a.cap_b - 2.f * a.cap_b *
+                                              __builtin_amdgcn_rcpf(exp2_fast(sc[i] * a.cap_k) + 1.f)
+                                : sc[i] * a.scale_log2;
+        sv[i] = vis ? s2 : -INFINITY;
         cmax = fmaxf(cmax, sv[i]);
       }
       cmax = max_xor16_32(cmax);
@@ -280,7 +290,7 @@ __device__ __forceinline__ void decode_items(const AttnArgs& a) {
     const int n = r16;
     if (n >= ncols) {
       // padding column: nothing to store
-    } else if (nsplit == 1) {
+    } else if (live == 1) {
       const float inv = 1.f / l_tot;
       const int ng = div_small(n, a.inv_group);
       const int tok = si.cu + ng;
@@ -334,17 +344,19 @@ __global__ __launch_bounds__(256) void combine_kernel(AttnArgs a) {
   const int ncols = si.q_len * G;
   if (si.q_len <= 0 || ncols > kDecodeCols) return;
   const int nsplit = (si.kv_len + kSplitKeys - 1) / kSplitKeys;
-  if (nsplit <= 1) return;
+  const int s0 = first_live_split(si.kv_len, si.q_len, a.window);   // splits s0 .. nsplit-1
+  if (nsplit - s0 <= 1) return;
   const int64_t row0 = (int64_t)si.pbase + (int64_t)kh * nsplit * ncols;
   // Column n's weights: one 16-lane group of a wave per column.
   for (int n = threadIdx.x >> 4; n < ncols; n += blockDim.x >> 4) {
     const int lane16 = threadIdx.x & 15;
     float M = -INFINITY;
-    for (int s = lane16; s < nsplit; s += 16) M = fmaxf(M, a.part_ml[row0 + (int64_t)s * ncols + n].x);
+    for (int s = s0 + lane16; s < nsplit; s += 16)
+      M = fmaxf(M, a.part_ml[row0 + (int64_t)s * ncols + n].x);
 #pragma unroll
     for (int o = 8; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 16));
     float den = 0.f;
-    for (int s = lane16; s < nsplit; s += 16) {
+    for (int s = s0 + lane16; s < nsplit; s += 16) {
       const float2 ml = a.part_ml[row0 + (int64_t)s * ncols + n];
       const float w = ml.x == -INFINITY ? 0.f : exp2_fast(ml.x - M);
       if (s < MAXS) wts[n][s] = w;
@@ -362,7 +374,7 @@ __global__ __launch_bounds__(256) void combine_kernel(AttnArgs a) {
     const float* src = a.part_acc + (row0 + n) * D + d;
     const int64_t step = (int64_t)ncols * D;
     float4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-    int s = 0;
+    int s = s0;
     for (; s + 1 < nsplit; s += 2) {
       const float4_t v0 = *reinterpret_cast<const float4_t*>(src + s * step);
       const float4_t v1 = *reinterpret_cast<const float4_t*>(src + (s + 1) * step);

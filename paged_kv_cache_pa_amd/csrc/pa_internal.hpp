@@ -88,6 +88,7 @@ struct PlanArgs {
   int32_t num_workers;  // grid size of the attention kernel
   int32_t decode_only;  // fp8 caches: only the decode path; a sequence with
                         // more than kDecodeCols columns gets no work items
+  int32_t window;       // local_window_size (0: off)
 };
 
 struct AttnArgs {
@@ -109,7 +110,20 @@ struct AttnArgs {
   int32_t block_size, block_shift, tokens_per_tile;
   float scale_log2;  // scale * log2(e)
   float inv_group;   // 1 / group (exact small-integer division, see div_small)
+  // Score soft cap c > 0: capped score in log2 units = cap_b - 2 cap_b /
+  // (2^(s * cap_k) + 1) = c tanh(scale s / c) log2(e) for the raw dot product
+  // s, with cap_k = 2 (scale / c) log2(e) and cap_b = c log2(e); cap_b = 0: off.
+  float cap_k, cap_b;
+  int32_t window;    // local_window_size W: row sees keys (limit - W, limit]; 0: off
 };
+
+// First decode split of a sequence with a sliding window: splits wholly
+// below the window start of its first new row hold no visible key.
+__host__ __device__ inline int first_live_split(int kv_len, int q_len, int window) {
+  if (window <= 0) return 0;
+  const int lo = kv_len - q_len - window + 1;   // first visible key of row 0
+  return lo > 0 ? lo / kSplitKeys : 0;
+}
 
 hipError_t launch_scatter(const void* k_new, const void* v_new, const int32_t* slots, void* kc,
                           void* vc, int64_t num_tokens, int32_t row_bytes, hipStream_t st);

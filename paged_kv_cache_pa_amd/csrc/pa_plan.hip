@@ -66,11 +66,11 @@ __device__ void block_scan(int (&v)[W], int (&total)[W], int* lds) {
 }
 
 struct SeqCounts {
-  int cu0, q_len, L, nsplit, prows, ntiles;
+  int cu0, q_len, L, nsplit, prows, ntiles, s0;
 };
 
 __device__ inline SeqCounts seq_counts(const PlanArgs& a, int b) {
-  SeqCounts c{0, 0, 0, 0, 0, 0};
+  SeqCounts c{0, 0, 0, 0, 0, 0, 0};
   if (b >= a.num_seqs) return c;
   c.cu0 = a.cu_seqlens_q[b];
   c.q_len = a.cu_seqlens_q[b + 1] - c.cu0;
@@ -80,7 +80,8 @@ __device__ inline SeqCounts seq_counts(const PlanArgs& a, int b) {
   if (a.decode_only && ncols > kDecodeCols) return c;   // no work (precondition violated)
   if (ncols <= kDecodeCols) {
     c.nsplit = (c.L + kSplitKeys - 1) / kSplitKeys;
-    if (c.nsplit > 1) c.prows = a.num_kv_heads * c.nsplit * ncols;
+    c.s0 = first_live_split(c.L, c.q_len, a.window);
+    if (c.nsplit - c.s0 > 1) c.prows = a.num_kv_heads * c.nsplit * ncols;
   } else {
     c.ntiles = (c.q_len + a.tokens_per_tile - 1) / a.tokens_per_tile;
   }
@@ -114,16 +115,17 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
     const SeqCounts c = seq_counts(a, b);
     if (c.ntiles > 0) {   // key tiles per item ~ (past + mid-tile row) / 64, rounded up
       const float past = (float)(c.L - c.q_len);
-      cost_p += (float)c.ntiles * a.num_kv_heads *
-                ((past + 0.5f * (c.q_len + a.tokens_per_tile)) / kPrefillKeys + 0.5f);
+      float keys = past + 0.5f * (c.q_len + a.tokens_per_tile);
+      if (a.window > 0) keys = fminf(keys, (float)a.window + (float)a.tokens_per_tile);
+      cost_p += (float)c.ntiles * a.num_kv_heads * (keys / kPrefillKeys + 0.5f);
     } else if (c.q_len > 0) {
-      cost_d += (float)c.L * a.num_kv_heads;
+      cost_d += (float)(c.L - c.s0 * kSplitKeys) * a.num_kv_heads;
     }
     // Decode pairs: every full kSplitKeys split first (pass 1), then the
     // shorter last splits (pass 2), so the tail of the decode work is made
     // of short items.
     const int has_part = (c.L % kSplitKeys) != 0 && c.nsplit > 0;
-    const int nfull = c.nsplit - has_part;
+    const int nfull = max(0, c.nsplit - has_part - c.s0);   // live full splits: s0 ..
     int v[3 + kQueues], tot[3 + kQueues];
     v[0] = nfull;
     v[1] = c.prows;
@@ -134,7 +136,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
     if (b < a.num_seqs) {
       a.seqinfo[b] = SeqInfo{c.cu0, c.q_len, c.L, carry[1] + v[1]};
       const int off = carry[0] + v[0];
-      for (int s = 0; s < nfull; ++s) a.dec_items[off + s] = make_int2(b, s);
+      for (int s = 0; s < nfull; ++s) a.dec_items[off + s] = make_int2(b, c.s0 + s);
     }
 #pragma unroll
     for (int k = 0; k < 3 + kQueues; ++k) carry[k] += tot[k];

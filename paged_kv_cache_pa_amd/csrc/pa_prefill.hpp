@@ -78,7 +78,12 @@ __device__ inline void wait_vmcnt() {
 // the two halves of every SIMD keep the MFMA and VALU pipes busy together.
 // Runs prefill work items on the calling work-group (512 threads, all of
 // which must call it) until every queue is exhausted.
-template <typename T, int D>
+// CAP: scores soft-capped (c tanh(scale s / c)).  WIN: sliding window of
+// a.window keys: the item's tiles start at the first one holding a key its
+// first row sees, and tiles below a row's window start are masked like the
+// causal diagonal.  Each option is its own instantiation, so the plain
+// kernel keeps its short instruction stream and loop structure.
+template <typename T, int D, bool CAP = false, bool WIN = false>
 __device__ __forceinline__ void prefill_items(const AttnArgs& a) {
   constexpr int NS = D / 32;            // QK^T steps
   constexpr int NT = D / 16;            // O^T tiles
@@ -148,7 +153,11 @@ __device__ __forceinline__ void prefill_items(const AttnArgs& a) {
       const int i0 = tile * TQ;
       const int last_tok = min(i0 + TQ, ql) - 1;
       const int kend = past + last_tok + 1;   // keys visible to the tile's last row
-      const int n = (kend + BN - 1) / BN;      // key tiles of this item
+      const int n = (kend + BN - 1) / BN;      // key tiles of this item: t_lo .. n-1
+      const int W = WIN ? a.window : 0;
+      // first tile with a key the item's first row sees (its window start)
+      const int t_lo = W > 0 ? max(0, past + i0 - W + 1) / BN : 0;
+      const int nrel = n - t_lo;               // tiles processed, tick pairs 0 .. nrel
       // The block table is read-only here: read it through the constant
       // address space so uniform reads become scalar loads (tracked apart
       // from the vector-memory counter the tile copies use).
@@ -227,10 +236,10 @@ __device__ __forceinline__ void prefill_items(const AttnArgs& a) {
       float4_t sacc[NK][NR];   // scores of the tile between its M and V phases
       u32x4_t pb[NR][NK / 2];  // rounded P of the tile between its V and next M phases
 
-      // Prologue: tiles 0 and 1 resident, block id of tile 2 fetched.
-      issue(0, block_of(0));
-      if (n > 1) issue(1, block_of(1));
-      int blk_next = n > 2 ? block_of(2) : 0;
+      // Prologue: tiles t_lo and t_lo+1 resident, block id of the next fetched.
+      issue(t_lo, block_of(t_lo));
+      if (nrel > 1) issue(t_lo + 1, block_of(t_lo + 1));
+      int blk_next = nrel > 2 ? block_of(t_lo + 2) : 0;
       wait_vmcnt<0>();
       // The wait above is opaque to the compiler, which would otherwise
       // still count the Q loads as in flight and guard their first use in
@@ -333,10 +342,14 @@ __device__ __forceinline__ void prefill_items(const AttnArgs& a) {
         }
       };
 
+      // Soft-capped score in log2 units from the raw dot product (CAP).
+      auto capf = [&](float x) {
+        return a.cap_b - 2.f * a.cap_b * __builtin_amdgcn_rcpf(exp2_fast(x * a.cap_k) + 1.f);
+      };
       // Softmax of tile j into P (pb), running max / sum and rescale.
-      // kMasked: apply the causal mask (tiles crossing a row's diagonal, and
-      // every tile when scale <= 0); otherwise all 64 keys are visible to
-      // every row of the wave and scale > 0.
+      // kMasked: apply the causal mask and the window (tiles crossing a row's
+      // diagonal or window start, and every tile when scale <= 0); otherwise
+      // all 64 keys are visible to every row of the wave and scale > 0.
       auto softmax = [&](int j, auto masked_tag) {
         constexpr bool kMasked = decltype(masked_tag)::value;
         const int kt = j * BN;
@@ -348,12 +361,14 @@ __device__ __forceinline__ void prefill_items(const AttnArgs& a) {
           // share the offset.
           float mt = -INFINITY;
           if constexpr (kMasked) {
+            const int low = limit[rho] - W;   // with a window, row sees keys (low, limit]
 #pragma unroll
             for (int kap = 0; kap < NK; ++kap)
 #pragma unroll
               for (int i = 0; i < 4; ++i) {
                 const int key = kt + 16 * kap + 4 * kq + i;
-                sacc[kap][rho][i] = key <= limit[rho] ? sacc[kap][rho][i] * c : -INFINITY;
+                const float sc = CAP ? capf(sacc[kap][rho][i]) : sacc[kap][rho][i] * c;
+                sacc[kap][rho][i] = key <= limit[rho] && (!WIN || key > low) ? sc : -INFINITY;
                 mt = fmaxf(mt, sacc[kap][rho][i]);
               }
           } else {
@@ -361,7 +376,7 @@ __device__ __forceinline__ void prefill_items(const AttnArgs& a) {
             for (int kap = 0; kap < NK; ++kap)
 #pragma unroll
               for (int i = 0; i < 4; ++i) mt = fmaxf(mt, sacc[kap][rho][i]);
-            mt *= c;
+            mt = CAP ? capf(mt) : mt * c;   // the cap is increasing: max commutes
           }
           mt = max_xor16_32(mt);
           const bool raise = mt > m[rho] + kMaxSlack || m[rho] == -INFINITY;
@@ -382,6 +397,7 @@ __device__ __forceinline__ void prefill_items(const AttnArgs& a) {
 #pragma unroll
             for (int i = 0; i < 4; ++i)
               sv[kap][i] = kMasked ? exp2_fast(sacc[kap][rho][i] - base_m)
+                           : CAP   ? exp2_fast(capf(sacc[kap][rho][i]) - base_m)
                                    : exp2_fast(fmaf(sacc[kap][rho][i], c, -base_m));
           // P rounded to the input dtype feeds P.V; the denominator sums
           // the same rounded values.
@@ -402,131 +418,138 @@ __device__ __forceinline__ void prefill_items(const AttnArgs& a) {
       using Plain = std::integral_constant<bool, false>;
       using Masked = std::integral_constant<bool, true>;
 
-      // Tiles this wave computes: 0 .. nw-1 (later ones lie wholly above
-      // all its rows' diagonals); of those, tiles 0 .. nd-1 need no mask.
-      const int nw = wave_kmax < 0 ? 0 : min(n, wave_kmax / BN + 1);
-      const int nd = c > 0.f ? min(nw, (wave_kmin + 1) / BN) : 0;
+      // Tiles this wave computes, relative to t_lo: a0 .. a3-1, of which
+      // a0 .. a1-1 cross a row's window start (masked), a1 .. a2-1 need no
+      // mask and a2 .. a3-1 cross a row's diagonal (masked).  Absolute tile
+      // nw and later lie wholly above all its rows' diagonals, tiles below
+      // its first row's window start hold no visible key, and tiles from nd
+      // on cross the diagonal of the wave's first row; all from uniform
+      // values (wave_kmax / wave_kmin: last / first row's causal limit).
+      int a0 = 0, a1 = 0, a2 = 0, a3 = 0;
+      if constexpr (!WIN) {
+        a3 = wave_kmax < 0 ? 0 : min(n, wave_kmax / BN + 1);
+        a2 = c > 0.f ? min(a3, (wave_kmin + 1) / BN) : 0;
+      } else {
+        const int nw = wave_kmax < 0 ? 0 : min(n, wave_kmax / BN + 1);
+        const int nd = c > 0.f ? min(nw, (wave_kmin + 1) / BN) : 0;
+        const int first_lim = past + i0 + 32 * wave / G;          // the wave's first row
+        const int tA0 = W > 0 ? max(0, first_lim - W + 1) / BN : 0;
+        const int tA1 = W > 0 ? (max(0, wave_kmax - W + 1) + BN - 1) / BN : 0;
+        const int A0 = max(t_lo, min(tA0, nw));
+        if (nw > A0) {
+          const int A1 = min(max(tA1, A0), nw);
+          const int A2 = min(max(nd, A1), nw);
+          a0 = A0 - t_lo;
+          a1 = A1 - t_lo;
+          a2 = A2 - t_lo;
+          a3 = nw - t_lo;
+        }
+      }
 
       // Request tile i+2: issued by each wave at the start of its softmax
       // phase (group B: tick 2i, group A: tick 2i+1).  Issuing 32 copies at
       // once can stall the issuing waves until the address unit drains them,
       // which must not happen in a matrix-core phase.
       auto even_service = [&](int i) {
-        if (i + 2 < n) issue(i + 2, blk_next);
+        if (i + 2 < nrel) issue(t_lo + i + 2, blk_next);
       };
       // Block id of tile i+3 (a scalar load, first used at tick 2i+2), read
       // at the start of the wave's softmax phase: that phase has no LDS reads
       // and hides the load, whereas an SMEM load in flight during the
       // matrix-core phase would turn its LDS waits into full lgkmcnt drains.
       auto fetch_service = [&](int i) {
-        if (i + 3 < n) blk_next = block_of(i + 3);
+        if (i + 3 < nrel) blk_next = block_of(t_lo + i + 3);
       };
       // Run at the end of tick 2i+1 by every wave, before its barrier: all
       // copies but tile i+2's have landed, so tile i+1 is complete.
       auto odd_service = [&](int i) {
-        if (i + 2 < n) wait_vmcnt<2 * LPW>(); else wait_vmcnt<0>();
+        if (i + 2 < nrel) wait_vmcnt<2 * LPW>(); else wait_vmcnt<0>();
       };
 
-      // Tick pair i (ticks 2i and 2i+1): ticks 2i and 2i+1 request tile i+2;
-      // tick 2i+1 ends with tile i+1 complete.  Tile t lives in ring buffer
-      // t % 4: tile i+2 overwrites tile i-2, whose V was last read at tick
-      // 2i-1.
-      // Group A runs M_i = {P.V of tile i-1, QK^T of tile i} at tick 2i and
+      // Tick pair i (ticks 2i and 2i+1) of tile t = t_lo + i: ticks 2i and
+      // 2i+1 request tile t+2; tick 2i+1 ends with tile t+1 complete.  Tile t
+      // lives in ring buffer t % 4: tile t+2 overwrites tile t-2, whose V was
+      // last read at tick 2i-1.
+      // Group A runs M_i = {P.V of tile t-1, QK^T of tile t} at tick 2i and
       // the softmax V_i at tick 2i+1; group B runs V_{i-1} at tick 2i and
-      // M_i at tick 2i+1.  Both pass the same 2(n+1) barriers; the loops are
-      // split where a wave's tiles change kind so each body is straight-line.
+      // M_i at tick 2i+1.  Both pass the same 2(nrel+1) barriers; a wave
+      // idles through the pairs outside a0 .. a3, and the loops are split
+      // where its tiles change kind so each body is straight-line.
+      auto idle = [&](int i) {
+        __syncthreads();
+        even_service(i);
+        fetch_service(i);
+        odd_service(i);
+        __syncthreads();
+      };
       if (grp == 0) {
+        auto tick = [&](int i, auto kind) {
+          qk_first(t_lo + i);
+          __builtin_amdgcn_sched_barrier(0);
+          if (i > a0) pv(t_lo + i - 1);
+          __builtin_amdgcn_sched_barrier(0);
+          qk(t_lo + i);
+          __syncthreads();
+          even_service(i);
+          fetch_service(i);
+          softmax(t_lo + i, kind);
+          odd_service(i);
+          __syncthreads();
+        };
         int i = 0;
-        for (; i < nd; ++i) {
-          qk_first(i);
-          __builtin_amdgcn_sched_barrier(0);
-          if (i > 0) pv(i - 1);
-          __builtin_amdgcn_sched_barrier(0);
-          qk(i);
-          __syncthreads();
-          even_service(i);
-          fetch_service(i);
-          softmax(i, Plain{});
-          odd_service(i);
-          __syncthreads();
+        if constexpr (WIN) {   // (a0 = a1 = 0 without a window)
+          for (; i < a0; ++i) idle(i);
+          for (; i < a1; ++i) tick(i, Masked{});
         }
-        for (; i < nw; ++i) {
-          qk_first(i);
-          __builtin_amdgcn_sched_barrier(0);
-          if (i > 0) pv(i - 1);
-          __builtin_amdgcn_sched_barrier(0);
-          qk(i);
-          __syncthreads();
-          even_service(i);
-          fetch_service(i);
-          softmax(i, Masked{});
-          odd_service(i);
-          __syncthreads();
-        }
-        for (; i <= n; ++i) {
-          if (i == nw && i > 0) pv(i - 1);
-          __syncthreads();
-          even_service(i);
-          fetch_service(i);
-          odd_service(i);
-          __syncthreads();
+        for (; i < a2; ++i) tick(i, Plain{});
+        for (; i < a3; ++i) tick(i, Masked{});
+        for (; i <= nrel; ++i) {
+          if (i == a3 && a3 > a0) pv(t_lo + i - 1);
+          idle(i);
         }
       } else {
-        // Tick pair 0: M_0 = QK^T of tile 0 only.
-        even_service(0);
-        fetch_service(0);
+        int i = 0;
+        if constexpr (WIN)
+          for (; i < a0; ++i) idle(i);
+        // Tick pair a0: M_a0 = QK^T of the wave's first tile only.
+        even_service(i);
+        fetch_service(i);
         __syncthreads();
-        if (nw > 0) {
-          qk_first(0);
-          qk(0);
+        if (a3 > a0) {
+          qk_first(t_lo + i);
+          qk(t_lo + i);
         }
-        odd_service(0);
+        odd_service(i);
         __syncthreads();
-        int i = 1;
-        const int np = min(nd + 1, nw);
-        for (; i < np; ++i) {    // V_{i-1} plain, then M_i
+        ++i;
+        auto tick = [&](int i, auto kind) {   // V_{i-1}, then M_i
           even_service(i);
           fetch_service(i);
-          softmax(i - 1, Plain{});
+          softmax(t_lo + i - 1, kind);
           __syncthreads();
-          qk_first(i);
+          qk_first(t_lo + i);
           __builtin_amdgcn_sched_barrier(0);
-          pv(i - 1);
+          pv(t_lo + i - 1);
           __builtin_amdgcn_sched_barrier(0);
-          qk(i);
+          qk(t_lo + i);
           odd_service(i);
           __syncthreads();
-        }
-        for (; i < nw; ++i) {    // V_{i-1} masked, then M_i
+        };
+        if constexpr (WIN)
+          for (; i < min(a1 + 1, a3); ++i) tick(i, Masked{});
+        for (; i < min(a2 + 1, a3); ++i) tick(i, Plain{});
+        for (; i < a3; ++i) tick(i, Masked{});
+        if (i == a3 && a3 > a0) {   // V of the last tile (masked: a no-op on a plain one), P.V only
           even_service(i);
           fetch_service(i);
-          softmax(i - 1, Masked{});
+          softmax(t_lo + i - 1, Masked{});
           __syncthreads();
-          qk_first(i);
-          __builtin_amdgcn_sched_barrier(0);
-          pv(i - 1);
-          __builtin_amdgcn_sched_barrier(0);
-          qk(i);
-          odd_service(i);
-          __syncthreads();
-        }
-        if (i == nw && nw > 0) { // V_{nw-1} (the mask is a no-op on a plain tile), P.V only
-          even_service(i);
-          fetch_service(i);
-          softmax(i - 1, Masked{});
-          __syncthreads();
-          pv(i - 1);
+          pv(t_lo + i - 1);
           odd_service(i);
           __syncthreads();
           ++i;
         }
-        for (; i <= n; ++i) {
-          even_service(i);
-          fetch_service(i);
-          __syncthreads();
-          odd_service(i);
-          __syncthreads();
-        }
+        for (; i <= nrel; ++i) idle(i);
       }
 
       // Output rows: token and head recomputed here (not held in registers

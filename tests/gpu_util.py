@@ -58,16 +58,16 @@ def run_attention(wl, d, **kw):
     return out
 
 
-def oracle_full(wl, d):
+def oracle_full(wl, d, **opts):
     """Oracle output for the whole (small) workload from the generator's
-    values."""
+    values (``opts``: softcap, local_window_size)."""
     q = to_np64(d["q"])
     kc, vc = oracle_caches(wl, to_np64(d["k_all"]), to_np64(d["v_all"]))
     return oracle.attention(q, wl.cu_seqlens_q, wl.seqlens_kv, wl.block_table, kc, vc, wl.scale,
-                            wl.num_heads, wl.num_kv_heads, wl.block_size)
+                            wl.num_heads, wl.num_kv_heads, wl.block_size, **opts)
 
 
-def oracle_rows(wl, d, picks):
+def oracle_rows(wl, d, picks, **opts):
     """Oracle outputs for selected (sequence, new-row) pairs of a large
     workload.  Row i of sequence b equals a q_len=1 query whose total KV
     length is past_b + i + 1 over the same block-table row (incremental
@@ -85,7 +85,8 @@ def oracle_rows(wl, d, picks):
     lens = np.array([past[b] + i + 1 for b, i in picks], dtype=np.int32)
     table = wl.block_table[[b for b, _ in picks]]
     return oracle.attention(q, np.arange(len(picks) + 1, dtype=np.int32), lens, table, kc, vc,
-                            wl.scale, wl.num_heads, wl.num_kv_heads, wl.block_size), toks
+                            wl.scale, wl.num_heads, wl.num_kv_heads, wl.block_size,
+                            **opts), toks
 
 
 def max_err(gpu_out, ref):
@@ -165,15 +166,15 @@ def oracle_codes_fp8_for(wl, d, seqs):
     return kc, vc
 
 
-def oracle_full_fp8(wl, d):
+def oracle_full_fp8(wl, d, **opts):
     from oracle import kv_fp8
     kc, vc = oracle_codes_fp8(wl, d)
     return kv_fp8.attention_fp8(to_np64(d["q"]), wl.cu_seqlens_q, wl.seqlens_kv, wl.block_table,
                                 kc, vc, d["ks_np"], d["vs_np"], wl.scale, wl.num_heads,
-                                wl.num_kv_heads, wl.block_size)
+                                wl.num_kv_heads, wl.block_size, **opts)
 
 
-def oracle_rows_fp8(wl, d, picks):
+def oracle_rows_fp8(wl, d, picks, **opts):
     """oracle_rows for fp8 caches: one-token sequences per (sequence, row)."""
     from oracle import kv_fp8
     seqs = sorted({b for b, _ in picks})
@@ -186,4 +187,4 @@ def oracle_rows_fp8(wl, d, picks):
     table = wl.block_table[[b for b, _ in picks]]
     return kv_fp8.attention_fp8(q, np.arange(len(picks) + 1, dtype=np.int32), lens, table, kc, vc,
                                 d["ks_np"], d["vs_np"], wl.scale, wl.num_heads, wl.num_kv_heads,
-                                wl.block_size), toks
+                                wl.block_size, **opts), toks

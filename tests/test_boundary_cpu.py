@@ -50,11 +50,13 @@ FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: every call below fails be
 
 def _attn(L, **kw):
     a = dict(q=FAKE, cu=FAKE, lens=FAKE, table=FAKE, kc=FAKE, vc=FAKE, out=FAKE, B=2, T=5, MB=2,
-             NB=8, scale=0.125, hq=4, hk=2, d=64, bs=16, dtype=0, ws=FAKE, wsb=0, st=None)
+             NB=8, scale=0.125, cap=0.0, win=0, hq=4, hk=2, d=64, bs=16, dtype=0, ws=FAKE, wsb=0,
+             st=None)
     a.update(kw)
     return L.pa_attention(a["q"], a["cu"], a["lens"], a["table"], a["kc"], a["vc"], a["out"],
-                          a["B"], a["T"], a["MB"], a["NB"], a["scale"], a["hq"], a["hk"], a["d"],
-                          a["bs"], a["dtype"], a["ws"], a["wsb"], a["st"])
+                          a["B"], a["T"], a["MB"], a["NB"], a["scale"], a["cap"], a["win"],
+                          a["hq"], a["hk"], a["d"], a["bs"], a["dtype"], a["ws"], a["wsb"],
+                          a["st"])
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -67,6 +69,10 @@ def _attn(L, **kw):
     (dict(hq=256, hk=1), _lib.PA_ERR_NOT_IMPLEMENTED),
     (dict(scale=float("nan")), _lib.PA_ERR_INVALID_ARGUMENT),
     (dict(scale=float("inf")), _lib.PA_ERR_INVALID_ARGUMENT),
+    (dict(cap=-1.0), _lib.PA_ERR_INVALID_ARGUMENT),
+    (dict(cap=float("nan")), _lib.PA_ERR_INVALID_ARGUMENT),
+    (dict(cap=float("inf")), _lib.PA_ERR_INVALID_ARGUMENT),
+    (dict(cap=1e-40, scale=1e30), _lib.PA_ERR_INVALID_ARGUMENT),   # scale / cap overflows
     (dict(B=0), _lib.PA_ERR_INVALID_ARGUMENT),
     (dict(T=-1), _lib.PA_ERR_INVALID_ARGUMENT),
     (dict(q=None), _lib.PA_ERR_INVALID_ARGUMENT),
@@ -176,13 +182,13 @@ def test_scatter_fp8_empty_call_is_ok(L):
 
 def _attn8(L, **kw):
     a = dict(q=FAKE, cu=FAKE, lens=FAKE, table=FAKE, kc=FAKE, vc=FAKE, ks=FAKE, vs=FAKE, out=FAKE,
-             B=2, T=5, mq=4, MB=2, NB=8, scale=0.125, hq=4, hk=2, d=64, bs=16, dtype=0, ws=FAKE,
-             wsb=0, st=None)
+             B=2, T=5, mq=4, MB=2, NB=8, scale=0.125, cap=0.0, win=0, hq=4, hk=2, d=64, bs=16,
+             dtype=0, ws=FAKE, wsb=0, st=None)
     a.update(kw)
     return L.pa_attention_fp8(a["q"], a["cu"], a["lens"], a["table"], a["kc"], a["vc"], a["ks"],
                               a["vs"], a["out"], a["B"], a["T"], a["mq"], a["MB"], a["NB"],
-                              a["scale"], a["hq"], a["hk"], a["d"], a["bs"], a["dtype"], a["ws"],
-                              a["wsb"], a["st"])
+                              a["scale"], a["cap"], a["win"], a["hq"], a["hk"], a["d"], a["bs"],
+                              a["dtype"], a["ws"], a["wsb"], a["st"])
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -195,7 +201,9 @@ def _attn8(L, **kw):
     (dict(d=96), _lib.PA_ERR_NOT_IMPLEMENTED),
     (dict(bs=24), _lib.PA_ERR_NOT_IMPLEMENTED),
     (dict(scale=float("nan")), _lib.PA_ERR_INVALID_ARGUMENT),
+    (dict(cap=-0.5), _lib.PA_ERR_INVALID_ARGUMENT),
     (dict(), _lib.PA_ERR_WORKSPACE_TOO_SMALL),
+    (dict(cap=30.0, win=128), _lib.PA_ERR_WORKSPACE_TOO_SMALL),   # options accepted
 ])
 def test_attention_fp8_rejects_on_host(L, kw, status):
     assert _attn8(L, **kw) == status
