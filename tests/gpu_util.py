@@ -13,7 +13,7 @@ from paged_kv_cache_pa_amd import workloads as W
 from pa_testutil import oracle_caches, oracle_caches_for, to_np64
 
 TOL = {"f16": 2e-3, "bf16": 1.6e-2}
-NAN_BITS = 0x7E01   # a quiet-NaN payload in both fp16 and bf16 as stored bits
+NAN_BITS = 0x7FC1   # stored bits that are a quiet NaN in both fp16 (exponent 31) and bf16 (exponent 255)
 
 
 def require_gpu():

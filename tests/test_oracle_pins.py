@@ -324,7 +324,7 @@ def test_scatter_round_trip_and_sentinels():
     vals = W.make_values(wl)
     k_bits = vals["k_all"].view(torch.int16).numpy().view(np.uint16)
     v_bits = vals["v_all"].view(torch.int16).numpy().view(np.uint16)
-    sentinel = np.uint16(0x7E01)             # a quiet-NaN payload
+    sentinel = np.uint16(0x7E01)             # an fp16 quiet-NaN payload (the workload is fp16)
     shape = (wl.num_blocks, wl.block_size, wl.num_kv_heads, wl.head_size)
     kc = np.full(shape, sentinel, dtype=np.uint16)
     vc = np.full(shape, sentinel, dtype=np.uint16)
