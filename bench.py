@@ -220,6 +220,26 @@ def time_workload(wl, steps, warmup, torch, pa, W, extras=False, fp8=False, opts
                             "running both kinds in one launch gains")
             subs["sum_of_separate_ms"] = subs["decode_only"]["median_ms"] + subs["prefill_only"]["median_ms"]
             more["sub_batches"] = subs
+        # The fused step ahead of the attention on this batch's new tokens:
+        # packed QKV rows split, Q and K rotated over the whole head (split
+        # pairing), K/V scattered (pa_rotary_scatter_kv).  Timed last: it
+        # leaves rotated K in the cache.
+        T = wl.num_tokens
+        packed = torch.cat([st["q"].reshape(T, -1), st["k_new"].reshape(T, -1),
+                            st["v_new"].reshape(T, -1)], dim=1).contiguous()
+        cos, sin = W.rope_tables(int(wl.seqlens_kv.max()), wl.head_size, wl.dtype)
+        cos, sin = cos.cuda(), sin.cuda()
+        q_rot = torch.empty_like(st["q"])
+        fn = lambda: pa.pa_rotary_scatter_kv(  # noqa: E731
+            packed, st["cu"], st["lens"], st["table"], st["kc"], st["vc"], wl.num_heads,
+            wl.num_kv_heads, cos_cache=cos, sin_cache=sin, q_out=q_rot)
+        fn()
+        r = per_rep_times(fn, steps, torch, scrub)
+        nbytes = 2 * packed.numel() * packed.element_size()   # every element read once, written once
+        r.update({"bytes": nbytes, "GBps": nbytes / (r["median_ms"] * 1e-3) / 1e9,
+                  "rotary_dim": wl.head_size, "pairing": "split", "input": "packed QKV"})
+        more["rotary_scatter"] = r
+        del packed, q_rot
         del scrub
     del st
     torch.cuda.empty_cache()
@@ -493,6 +513,7 @@ def main():
         "step_reps": more.get("step_reps"),
         "sub_batches": more.get("sub_batches"),
         "scatter": more.get("scatter"),
+        "rotary_scatter": more.get("rotary_scatter"),
         "extra": extra,
     }
     if opts.get("local_window_size"):

@@ -151,6 +151,65 @@ pa_status_t pa_seqlens_from_past(const int32_t* cu_seqlens_q,
                                  void* stream);
 
 /*
+ * pa_rotary_scatter_kv - the steps ahead of the attention for one batch of
+ * new tokens, fused: split packed QKV rows, rotate Q and K by the rotary
+ * position embedding at each token's KV position, write the rotated Q to
+ * q_out and the rotated K and plain V into the paged caches at the slots
+ * the block table gives (as pa_scatter_kv_paged).
+ *
+ * Defines: "[WebGPU] Initial PagedAttention implementation (1/n)": the file
+ * summaries (a packed-QKV split program and a rotary program run ahead of
+ * the scatter) and the review's summary (interleaved and split pairing,
+ * the rotation's sign, pass-through of dimensions >= rotary_dim).  The
+ * pages define no formula; this library's reading is the rotary position
+ * embedding of Su et al. (RoFormer): for token i of sequence b at position
+ * p = past_b + i and pair k < rotary_dim / 2 with dimensions (x_a, x_b) =
+ * (2k, 2k+1) when interleaved, (k, k + rotary_dim / 2) otherwise:
+ *   x_a' = x_a cos - x_b sin,  x_b' = x_b cos + x_a sin,
+ *   cos = cos_cache[p][k], sin = sin_cache[p][k];
+ * dimensions >= rotary_dim are copied.  Computed in fp32 from the dtype
+ * inputs, rounded once to dtype (nearest even).
+ *
+ * query        [num_tokens, num_heads, head_size] dtype, or, when key and
+ *              value are NULL, packed rows [num_tokens, num_heads +
+ *              2 num_kv_heads, head_size]: each token's Q heads, then its K
+ *              heads, then its V heads.
+ * key, value   [num_tokens, num_kv_heads, head_size] dtype, or both NULL.
+ * cos_cache,
+ * sin_cache    [max_position, rotary_dim / 2] dtype, or both NULL (no
+ *              rotation: a split and scatter only).
+ * rotary_dim   multiple of 16 in [16, head_size] (others:
+ *              NOT_IMPLEMENTED); ignored without tables.
+ * interleaved  nonzero: interleaved pairing; 0: split pairing.
+ * cu_seqlens_q, seqlens_kv, block_table
+ *              as for pa_attention.  A negative table entry gives the token
+ *              no cache slot (its K/V are not written; its Q is).
+ * q_out        [num_tokens, num_heads, head_size] dtype, written (the Q
+ *              pa_attention then reads); must not overlap the inputs.
+ * k_cache,
+ * v_cache      paged caches, updated in place.
+ * All tensor pointers 16-byte aligned (else PA_ERR_INVALID_ARGUMENT).
+ * A token whose position is >= max_position (with tables) or negative
+ * (seqlens_kv[b] < q_len_b) breaks a precondition and is skipped whole:
+ * its q_out rows and cache slot are left as they were.
+ * Limits: head_size a multiple of 8; num_blocks * block_size and
+ * max_blocks_per_seq * block_size <= INT32_MAX.  num_tokens == 0 returns
+ * PA_OK without launching.
+ */
+pa_status_t pa_rotary_scatter_kv(const void* query, const void* key,
+                                 const void* value, const void* cos_cache,
+                                 const void* sin_cache, int32_t max_position,
+                                 int32_t rotary_dim, int32_t interleaved,
+                                 const int32_t* cu_seqlens_q,
+                                 const int32_t* seqlens_kv,
+                                 const int32_t* block_table, void* q_out,
+                                 void* k_cache, void* v_cache, int32_t num_seqs,
+                                 int64_t num_tokens, int32_t max_blocks_per_seq,
+                                 int64_t num_blocks, int32_t num_heads,
+                                 int32_t num_kv_heads, int32_t head_size,
+                                 int32_t block_size, int32_t dtype, void* stream);
+
+/*
  * pa_attention_workspace_size - bytes of device workspace pa_attention
  * needs for these host-known sizes (an upper bound over every metadata the
  * device could hold).  Returns 0 when the sizes are invalid.
@@ -332,10 +391,10 @@ const char* pa_last_error(void);
  * counts (host arrays of n entries; kinds: 0 scatter (all three scatter
  * entry points), 1 plan (and pa_seqlens_from_past), 2 attention (the one
  * launch that runs prefill tiles and split-KV decode items; the fp8 launch
- * of pa_attention_fp8), 3 split-KV combine), then forgets them.  Not for
- * concurrent use.
+ * of pa_attention_fp8), 3 split-KV combine, 4 pa_rotary_scatter_kv), then
+ * forgets them.  Not for concurrent use.
  */
-#define PA_PROFILE_KINDS 4
+#define PA_PROFILE_KINDS 5
 pa_status_t pa_profile_enable(int32_t enable);
 pa_status_t pa_profile_read(double* ms, int64_t* launches, int32_t n);
 

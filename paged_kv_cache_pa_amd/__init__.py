@@ -12,7 +12,7 @@ import ctypes
 from ._lib import (PA_BF16, PA_F16, PROFILE_KINDS, PAError, check, lib)  # noqa: F401
 
 __all__ = ["pa_scatter_kv", "pa_scatter_kv_paged", "pa_scatter_kv_fp8", "pa_seqlens_from_past",
-           "pa_attention", "pa_attention_fp8",
+           "pa_attention", "pa_attention_fp8", "pa_rotary_scatter_kv",
            "pa_attention_workspace_size", "pa_validate_metadata", "profile_enable",
            "profile_read", "PAError"]
 
@@ -94,6 +94,52 @@ def pa_seqlens_from_past(cu_seqlens_q, past_seqlens, out=None, stream=None):
         _dev(cu_seqlens_q, "cu_seqlens_q", torch.int32), _dev(past_seqlens, "past_seqlens", torch.int32),
         _dev(out, "out", torch.int32), B, _stream_ptr(out, stream)))
     return out
+
+
+def pa_rotary_scatter_kv(query, cu_seqlens_q, seqlens_kv, block_table, k_cache, v_cache,
+                         num_heads, num_kv_heads, key=None, value=None, cos_cache=None,
+                         sin_cache=None, interleaved=False, q_out=None, stream=None):
+    """Split packed QKV (``key``/``value`` None: ``query`` is [T, Hq + 2 Hk, D]
+    or [T, (Hq + 2 Hk) * D]), rotate Q and K at each token's KV position
+    with ``cos_cache``/``sin_cache`` [max_position, rotary_dim / 2] (None: no
+    rotation), write K/V into the caches at the block table's slots and
+    return the (rotated) Q [T, Hq, D]."""
+    import torch
+    T = query.shape[0]
+    nb, bs, hk, d = k_cache.shape
+    B = seqlens_kv.shape[0]
+    MB = block_table.shape[1]
+    if hk != num_kv_heads or tuple(v_cache.shape) != tuple(k_cache.shape) \
+            or cu_seqlens_q.shape != (B + 1,) or block_table.shape[0] != B:
+        raise ValueError("inconsistent shapes")
+    if key is None:
+        if value is not None or query.numel() != T * (num_heads + 2 * num_kv_heads) * d:
+            raise ValueError("packed QKV rows must hold Hq + 2 Hk heads")
+    elif query.numel() != T * num_heads * d or key.numel() != T * hk * d \
+            or value is None or value.numel() != T * hk * d:
+        raise ValueError("inconsistent Q/K/V shapes")
+    for t in (key, value, k_cache, v_cache, cos_cache, sin_cache):
+        if t is not None and t.dtype != query.dtype:
+            raise ValueError("all tensors share the query's dtype")
+    if (cos_cache is None) != (sin_cache is None):
+        raise ValueError("cos_cache and sin_cache go together")
+    max_pos, rdim = (0, 0) if cos_cache is None else (cos_cache.shape[0],
+                                                       2 * cos_cache.shape[1])
+    if sin_cache is not None and tuple(sin_cache.shape) != tuple(cos_cache.shape):
+        raise ValueError("cos_cache and sin_cache shapes differ")
+    if q_out is None:
+        q_out = torch.empty((T, num_heads, d), dtype=query.dtype, device=query.device)
+    elif q_out.numel() != T * num_heads * d or q_out.dtype != query.dtype:
+        raise ValueError("q_out must be [T, Hq, D] of the query's dtype")
+    opt = lambda t, n: None if t is None else _dev(t, n)  # noqa: E731
+    check(lib().pa_rotary_scatter_kv(
+        _dev(query, "query"), opt(key, "key"), opt(value, "value"), opt(cos_cache, "cos_cache"),
+        opt(sin_cache, "sin_cache"), max_pos, rdim, 1 if interleaved else 0,
+        _dev(cu_seqlens_q, "cu_seqlens_q", torch.int32), _dev(seqlens_kv, "seqlens_kv", torch.int32),
+        _dev(block_table, "block_table", torch.int32), _dev(q_out, "q_out"),
+        _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), B, T, MB, nb, num_heads, hk, d, bs,
+        _dtype_code(query), _stream_ptr(query, stream)))
+    return q_out
 
 
 def pa_attention_workspace_size(num_seqs, num_tokens, max_blocks_per_seq, num_heads,

@@ -19,9 +19,10 @@ PA_ERR_WORKSPACE_TOO_SMALL = 3
 PA_ERR_HIP = 4
 PA_F16 = 0
 PA_BF16 = 1
-PROFILE_KINDS = ("scatter", "plan", "attention", "combine")
+PROFILE_KINDS = ("scatter", "plan", "attention", "combine", "rotary")
 
-EXPORTS = ("pa_scatter_kv", "pa_scatter_kv_paged", "pa_scatter_kv_fp8", "pa_seqlens_from_past",
+EXPORTS = ("pa_scatter_kv", "pa_scatter_kv_paged", "pa_scatter_kv_fp8", "pa_rotary_scatter_kv",
+           "pa_seqlens_from_past",
            "pa_attention_workspace_size", "pa_attention", "pa_attention_fp8",
            "pa_validate_metadata", "pa_status_string", "pa_last_error",
            "pa_profile_enable", "pa_profile_read")
@@ -54,6 +55,9 @@ def lib():
     L.pa_scatter_kv_paged.restype = i32
     L.pa_scatter_kv_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i32, i32, i32, i32, vp]
     L.pa_scatter_kv_fp8.restype = i32
+    L.pa_rotary_scatter_kv.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, vp, vp, vp, vp, vp, vp,
+                                       i32, i64, i32, i64, i32, i32, i32, i32, i32, vp]
+    L.pa_rotary_scatter_kv.restype = i32
     L.pa_seqlens_from_past.argtypes = [vp, vp, vp, i32, vp]
     L.pa_seqlens_from_past.restype = i32
     L.pa_attention_workspace_size.argtypes = [i32, i64, i32, i32, i32, i32, i32]

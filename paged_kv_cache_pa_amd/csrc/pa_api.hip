@@ -273,6 +273,77 @@ pa_status_t pa_scatter_kv_paged(const void* k_new, const void* v_new, const int3
   return PA_OK;
 }
 
+pa_status_t pa_rotary_scatter_kv(const void* query, const void* key, const void* value,
+                                const void* cos_cache, const void* sin_cache,
+                                int32_t max_position, int32_t rotary_dim, int32_t interleaved,
+                                const int32_t* cu_seqlens_q, const int32_t* seqlens_kv,
+                                const int32_t* block_table, void* q_out, void* k_cache,
+                                void* v_cache, int32_t num_seqs, int64_t num_tokens,
+                                int32_t max_blocks_per_seq, int64_t num_blocks, int32_t num_heads,
+                                int32_t num_kv_heads, int32_t head_size, int32_t block_size,
+                                int32_t dtype, void* stream) {
+  g_err[0] = 0;
+  if (dtype != PA_F16 && dtype != PA_BF16)
+    return fail(PA_ERR_NOT_IMPLEMENTED, "dtype=%d (supported: PA_F16, PA_BF16)", dtype);
+  if (num_tokens < 0 || num_tokens > INT32_MAX)
+    return fail(PA_ERR_INVALID_ARGUMENT, "num_tokens outside [0, INT32_MAX]");
+  if (num_seqs < 1 || max_blocks_per_seq < 1)
+    return fail(PA_ERR_INVALID_ARGUMENT, "num_seqs and max_blocks_per_seq must be >= 1");
+  if (num_heads < 1 || num_kv_heads < 1 || head_size < 1 || block_size < 1 || num_blocks < 1)
+    return fail(PA_ERR_INVALID_ARGUMENT, "sizes must be >= 1");
+  if (head_size % 8 != 0)
+    return fail(PA_ERR_NOT_IMPLEMENTED, "head_size=%d is not a multiple of 8", head_size);
+  if (num_blocks * (int64_t)block_size > INT32_MAX)
+    return fail(PA_ERR_NOT_IMPLEMENTED, "num_blocks * block_size exceeds INT32_MAX");
+  if ((int64_t)max_blocks_per_seq * block_size > INT32_MAX)
+    return fail(PA_ERR_NOT_IMPLEMENTED, "max_blocks_per_seq * block_size exceeds INT32_MAX");
+  if ((key == nullptr) != (value == nullptr))
+    return fail(PA_ERR_INVALID_ARGUMENT, "key and value must both be given or both be null");
+  if ((cos_cache == nullptr) != (sin_cache == nullptr))
+    return fail(PA_ERR_INVALID_ARGUMENT, "cos_cache and sin_cache must both be given or both be null");
+  const bool rot = cos_cache != nullptr;
+  if (rot) {
+    if (rotary_dim < 1 || rotary_dim > head_size)
+      return fail(PA_ERR_INVALID_ARGUMENT, "rotary_dim=%d outside [1, head_size]", rotary_dim);
+    if (rotary_dim % 16 != 0)
+      return fail(PA_ERR_NOT_IMPLEMENTED, "rotary_dim=%d is not a multiple of 16", rotary_dim);
+    if (max_position < 1) return fail(PA_ERR_INVALID_ARGUMENT, "max_position < 1");
+  }
+  if (num_tokens == 0) return PA_OK;
+  if (!query || !cu_seqlens_q || !seqlens_kv || !block_table || !q_out || !k_cache || !v_cache)
+    return fail(PA_ERR_INVALID_ARGUMENT, "null pointer argument");
+  for (const void* ptr : {query, key, value, cos_cache, sin_cache, (const void*)q_out,
+                          (const void*)k_cache, (const void*)v_cache})
+    if (((uintptr_t)ptr & 15) != 0)
+      return fail(PA_ERR_INVALID_ARGUMENT, "tensor pointers must be 16-byte aligned");
+  pa::RotaryArgs a{};
+  a.query = query;
+  a.key = key;
+  a.value = value;
+  a.cos_cache = cos_cache;
+  a.sin_cache = sin_cache;
+  a.cu = cu_seqlens_q;
+  a.lens = seqlens_kv;
+  a.table = block_table;
+  a.q_out = q_out;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.num_tokens = num_tokens;
+  a.num_seqs = num_seqs;
+  a.max_blocks = max_blocks_per_seq;
+  a.block_size = block_size;
+  a.num_heads = num_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.head_size = head_size;
+  a.max_position = rot ? max_position : 0;
+  a.rotary_dim = rot ? rotary_dim : 0;
+  a.interleaved = interleaved ? 1 : 0;
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e = timed(4, st, [&] { return pa::launch_rotary_scatter(a, dtype, st); });
+  if (e != hipSuccess) return hip_fail(e, "rotary scatter launch");
+  return PA_OK;
+}
+
 pa_status_t pa_seqlens_from_past(const int32_t* cu_seqlens_q, const int32_t* past_seqlens,
                                  int32_t* seqlens_kv, int32_t num_seqs, void* stream) {
   g_err[0] = 0;

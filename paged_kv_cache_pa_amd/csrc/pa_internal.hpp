@@ -135,6 +135,25 @@ hipError_t launch_scatter_paged(const void* k_new, const void* v_new, const int3
                                 const int32_t* lens, const int32_t* table, void* kc, void* vc,
                                 int32_t num_seqs, int64_t num_tokens, int32_t max_blocks,
                                 int32_t block_size, int32_t row_bytes, hipStream_t st);
+// Rotary embedding + packed-QKV split + scatter of one batch of new tokens.
+struct RotaryArgs {
+  const void* query;      // [T, Hq, D], or packed [T, Hq + 2 Hk, D] when key is null
+  const void* key;        // [T, Hk, D] or null
+  const void* value;      // [T, Hk, D] or null
+  const void* cos_cache;  // [max_position, rotary_dim / 2] or null (no rotation)
+  const void* sin_cache;
+  const int32_t* cu;
+  const int32_t* lens;
+  const int32_t* table;
+  void* q_out;            // [T, Hq, D]
+  void* k_cache;
+  void* v_cache;
+  int64_t num_tokens;
+  int32_t num_seqs, max_blocks, block_size;
+  int32_t num_heads, num_kv_heads, head_size;
+  int32_t max_position, rotary_dim, interleaved;
+};
+hipError_t launch_rotary_scatter(const RotaryArgs& a, int dtype, hipStream_t st);
 hipError_t launch_seqlens_from_past(const int32_t* cu, const int32_t* past, int32_t* out,
                                     int32_t num_seqs, hipStream_t st);
 hipError_t launch_plan(const PlanArgs& a, hipStream_t st);

@@ -270,6 +270,17 @@ def make_values(wl, device="cpu", backend="numpy"):
     return {"q": out[0], "k_all": out[1], "v_all": out[2]}
 
 
+def rope_tables(max_position, rotary_dim, dtype="f16", base=10000.0):
+    """cos / sin tables [max_position, rotary_dim / 2] a caller of the rotary
+    scatter supplies: the usual rotary frequencies, angle p * base^(-2k / R)
+    for pair k at position p, rounded to the dtype (torch CPU tensors)."""
+    import torch
+    k = np.arange(rotary_dim // 2, dtype=np.float64)
+    ang = np.arange(max_position, dtype=np.float64)[:, None] * base ** (-2.0 * k / rotary_dim)
+    dt = torch.float16 if dtype == "f16" else torch.bfloat16
+    return torch.from_numpy(np.cos(ang)).to(dt), torch.from_numpy(np.sin(ang)).to(dt)
+
+
 def fp8_scales(wl, seed=None):
     """Per-(KV head, channel) float32 scales of fp8 (e4m3) caches for the
     workload's K and V: c * (1 + 0.5 u), u ~ U[0, 1) from a seeded stream,

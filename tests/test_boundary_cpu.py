@@ -145,6 +145,47 @@ def test_scatter_paged_empty_call_is_ok(L):
     assert _scatter_paged(L, T=0, k=None, v=None) == _lib.PA_OK
 
 
+def _rot(L, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, cos=FAKE, sin=FAKE, maxpos=64, rdim=64, inter=0, cu=FAKE,
+             lens=FAKE, table=FAKE, qo=FAKE, kc=FAKE, vc=FAKE, B=2, T=5, MB=2, NB=8, hq=4, hk=2,
+             d=64, bs=16, dtype=0)
+    a.update(kw)
+    return L.pa_rotary_scatter_kv(a["q"], a["k"], a["v"], a["cos"], a["sin"], a["maxpos"],
+                                  a["rdim"], a["inter"], a["cu"], a["lens"], a["table"], a["qo"],
+                                  a["kc"], a["vc"], a["B"], a["T"], a["MB"], a["NB"], a["hq"],
+                                  a["hk"], a["d"], a["bs"], a["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=2), _lib.PA_ERR_NOT_IMPLEMENTED),
+    (dict(d=60), _lib.PA_ERR_NOT_IMPLEMENTED),
+    (dict(rdim=24), _lib.PA_ERR_NOT_IMPLEMENTED),        # not a multiple of 16
+    (dict(NB=1 << 30, bs=16), _lib.PA_ERR_NOT_IMPLEMENTED),
+    (dict(T=-1), _lib.PA_ERR_INVALID_ARGUMENT),
+    (dict(B=0), _lib.PA_ERR_INVALID_ARGUMENT),
+    (dict(hq=0), _lib.PA_ERR_INVALID_ARGUMENT),
+    (dict(k=None), _lib.PA_ERR_INVALID_ARGUMENT),         # key without value
+    (dict(sin=None), _lib.PA_ERR_INVALID_ARGUMENT),       # cos without sin
+    (dict(rdim=0), _lib.PA_ERR_INVALID_ARGUMENT),
+    (dict(rdim=80), _lib.PA_ERR_INVALID_ARGUMENT),        # beyond head_size
+    (dict(maxpos=0), _lib.PA_ERR_INVALID_ARGUMENT),
+    (dict(q=None), _lib.PA_ERR_INVALID_ARGUMENT),
+    (dict(qo=None), _lib.PA_ERR_INVALID_ARGUMENT),
+    (dict(table=None), _lib.PA_ERR_INVALID_ARGUMENT),
+    (dict(qo=ctypes.c_void_p(0x1008)), _lib.PA_ERR_INVALID_ARGUMENT),   # unaligned
+    (dict(cos=ctypes.c_void_p(0x1004)), _lib.PA_ERR_INVALID_ARGUMENT),  # unaligned
+])
+def test_rotary_scatter_rejects_on_host(L, kw, status):
+    assert _rot(L, **kw) == status
+    assert L.pa_last_error() != b""
+
+
+def test_rotary_scatter_empty_call_is_ok(L):
+    assert _rot(L, T=0, q=None, qo=None) == _lib.PA_OK
+    # no tables: rotary_dim and max_position are not looked at
+    assert _rot(L, T=0, cos=None, sin=None, rdim=0, maxpos=0) == _lib.PA_OK
+
+
 def test_seqlens_from_past_rejects_on_host(L):
     assert L.pa_seqlens_from_past(FAKE, FAKE, FAKE, 0, None) == _lib.PA_ERR_INVALID_ARGUMENT
     assert L.pa_seqlens_from_past(FAKE, None, FAKE, 3, None) == _lib.PA_ERR_INVALID_ARGUMENT
