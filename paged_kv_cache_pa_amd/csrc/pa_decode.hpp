@@ -49,6 +49,7 @@
 
 #include "pa_common.hpp"
 #include "pa_internal.hpp"
+#include "pa_lds.hpp"
 
 namespace pa {
 
@@ -146,6 +147,24 @@ __device__ __forceinline__ void decode_items(const AttnArgs& a) {
     // codes (KV8: NS/2 16-byte K loads and NT/4 dwords per value row).
     constexpr int KW = KV8 ? NS / 2 : NS;
     constexpr int VW = KV8 ? NT / 4 : NT / 2;
+    // K is loaded in whole rows: each wave-wide load covers KRPI complete
+    // key rows (one 16-byte chunk per lane).  The matrix-core operand wants
+    // the other shape (16 rows x 64 bytes per load: half of 16 different
+    // 128-byte lines), and a CU streams that shape at about half the rate:
+    // a probe measured 80 vs 38 GB/s per CU on 16-32 CUs, 37.5 vs 33.7 on
+    // 128.  The chunk is turned into the operand layout through this wave's
+    // own 16-row LDS slice (XOR-swizzled so the 16-row reads and the row
+    // writes are conflict-free).  V loads already cover whole rows.
+    constexpr int KROWB = D * (int)sizeof(CT);     // bytes per K row
+    constexpr int KCPR = KROWB / 16;               // 16-byte chunks per row
+    constexpr int KRPI = 64 / KCPR;                // rows per wave-wide load
+    static_assert(16 / KRPI == KW && 8 * 16 * KROWB == decode_stage_bytes<D, sizeof(CT)>(),
+                  "K staging");
+    constexpr int KRP = 256 / KROWB;               // rows per 256 bytes (64 banks)
+    auto kswz = [](int row) { return (row / KRP) & (KCPR - 1); };
+    unsigned char* const kst =
+        decode_stage<T, D, CAP, WIN, (int)sizeof(CT)>() +
+        __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) * (16 * KROWB);
     struct Chunk {
       u32x4_t k[KW];
       uint32_t v[4][VW];
@@ -154,14 +173,18 @@ __device__ __forceinline__ void decode_items(const AttnArgs& a) {
       const int blk = __builtin_amdgcn_readlane(my_blk, (c0 >> a.block_shift) - blk0);
       const int64_t base =
           ((int64_t)blk * a.block_size + (c0 & (a.block_size - 1))) * row_stride + (int64_t)kh * D;
-      const CT* krow = kc + base + r16 * row_stride;
-      if constexpr (!KV8) {
+      // Load j: rows j * KRPI .. + KRPI - 1, chunk lane % KCPR of row
+      // j * KRPI + lane / KCPR.  fp8 caches (a pure-decode launch) take
+      // non-temporal loads, measured 0.9 % faster there; the 16-bit loads
+      // stay cached: in the fused launch beside prefill tiles the same hint
+      // was 4 % slower.
 #pragma unroll
-        for (int s = 0; s < NS; ++s) ch.k[s] = ld16(krow + (4 * s + kq) * 8);
-      } else {
-#pragma unroll
-        for (int s = 0; s < KW; ++s)
-          ch.k[s] = *reinterpret_cast<const u32x4_t*>(krow + NS * kq * 8 + 16 * s);
+      for (int j = 0; j < KW; ++j) {
+        const int row = j * KRPI + lane / KCPR;
+        const u32x4_t* src = reinterpret_cast<const u32x4_t*>(
+            reinterpret_cast<const unsigned char*>(kc + base + row * row_stride) +
+            (lane % KCPR) * 16);
+        ch.k[j] = KV8 ? __builtin_nontemporal_load(src) : *src;
       }
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -171,20 +194,38 @@ __device__ __forceinline__ void decode_items(const AttnArgs& a) {
 #pragma unroll
           for (int w = 0; w < 4; ++w) ch.v[e][w] = x[w];
         } else if constexpr (VW == 2) {
-          const u32x2_t x = *reinterpret_cast<const u32x2_t*>(vrow);
+          const u32x2_t x = KV8 ? __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(vrow))
+                                : *reinterpret_cast<const u32x2_t*>(vrow);
 #pragma unroll
           for (int w = 0; w < 2; ++w) ch.v[e][w] = x[w];
-        } else {
-          ch.v[e][0] = *reinterpret_cast<const uint32_t*>(vrow);
+        } else {   // fp8 caches, head_size 64
+          ch.v[e][0] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(vrow));
         }
       }
     };
+    // The chunk's K in the operand layout: piece j of lane (r16, kq) is
+    // 16-byte chunk 4j + kq (16-bit; 8 elements, QK^T step j) or KW kq + j
+    // (fp8; 16 codes, steps 2j and 2j+1) of key row r16.  Written as loaded,
+    // then read back, by this wave alone (in order, so no barrier).
+    auto k_pieces = [&](const Chunk& ch, u32x4_t (&kp)[KW]) {
+#pragma unroll
+      for (int j = 0; j < KW; ++j) {
+        const int row = j * KRPI + lane / KCPR, chunk = lane % KCPR;
+        *reinterpret_cast<u32x4_t*>(kst + row * KROWB + ((chunk ^ kswz(row)) << 4)) = ch.k[j];
+      }
+#pragma unroll
+      for (int j = 0; j < KW; ++j) {
+        const int chunk = KV8 ? KW * kq + j : 4 * j + kq;
+        kp[j] = *reinterpret_cast<const u32x4_t*>(kst + r16 * KROWB +
+                                                  ((chunk ^ kswz(r16)) << 4));
+      }
+    };
     // Operand of QK^T step s: 8 elements of the lane's key row.
-    auto k_operand = [&](const Chunk& ch, int s) -> u32x4_t {
+    auto k_operand = [&](const u32x4_t (&kp)[KW], int s) -> u32x4_t {
       if constexpr (!KV8) {
-        return ch.k[s];
+        return kp[s];
       } else {
-        const uint32_t lo = ch.k[s >> 1][2 * (s & 1)], hi = ch.k[s >> 1][2 * (s & 1) + 1];
+        const uint32_t lo = kp[s >> 1][2 * (s & 1)], hi = kp[s >> 1][2 * (s & 1) + 1];
         return u32x4_t{Elt<T>::template from_fp8x2<0>(lo), Elt<T>::template from_fp8x2<1>(lo),
                        Elt<T>::template from_fp8x2<0>(hi), Elt<T>::template from_fp8x2<1>(hi)};
       }
@@ -199,9 +240,11 @@ __device__ __forceinline__ void decode_items(const AttnArgs& a) {
       }
     };
     auto compute = [&](int c0, const Chunk& ch) {
+      u32x4_t kp[KW];
+      k_pieces(ch, kp);
       float4_t sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int s = 0; s < NS; ++s) sc = Elt<T>::mfma32(k_operand(ch, s), qreg[s], sc);
+      for (int s = 0; s < NS; ++s) sc = Elt<T>::mfma32(k_operand(kp, s), qreg[s], sc);
       float sv[4];
       float cmax = -INFINITY;
 #pragma unroll
@@ -259,9 +302,10 @@ __device__ __forceinline__ void decode_items(const AttnArgs& a) {
     // uniform trip count and its only exit is the loop test, so its body is
     // straight-line and the compiler's wait counts keep the younger chunk in
     // flight; the pair's second request past the split end re-reads the
-    // split's last chunk (cached) instead of branching.  A deeper ring
-    // measured no faster: a CU's streaming rate is bounded by its
-    // outstanding-miss capacity, not by how far ahead each wave issues.
+    // split's last chunk (cached) instead of branching.  A deeper ring (3 or
+    // 4 chunks) measured no faster: a CU's streaming rate is bounded by its
+    // outstanding-miss capacity (hence the whole-row K loads above), not by
+    // how far ahead each wave issues.
     const int nch = (k1 - k0 + 15) >> 4;
     const int last_c0 = k0 + 16 * (nch - 1);
     Chunk ca, cb;

@@ -31,6 +31,7 @@
 
 #include "pa_common.hpp"
 #include "pa_internal.hpp"
+#include "pa_lds.hpp"
 
 namespace pa {
 
@@ -101,7 +102,9 @@ __device__ __forceinline__ void prefill_items(const AttnArgs& a) {
   static_assert(LPW >= 1 && NK % 2 == 0, "tile shape");
   constexpr int NB = 4;                 // ring buffers of [K tile, V tile]
   __shared__ __attribute__((aligned(1024))) unsigned char lds[NB * 2 * TB];
-  __shared__ int item_sh;
+  // The item slot lives in the decode phase's staging buffer (never in use
+  // at the same time), so ring + staging fit the 160 KiB of LDS at D = 128.
+  int& item_sh = *reinterpret_cast<int*>(decode_stage<T, D, CAP, WIN, 2>());
   const uint32_t lds_addr = (uint32_t)(uintptr_t)(lds_ptr_t)lds;
 
   const int tid = threadIdx.x;
