@@ -174,28 +174,28 @@ __device__ __forceinline__ void decode_items(const AttnArgs& a) {
       const int64_t base =
           ((int64_t)blk * a.block_size + (c0 & (a.block_size - 1))) * row_stride + (int64_t)kh * D;
       // Load j: rows j * KRPI .. + KRPI - 1, chunk lane % KCPR of row
-      // j * KRPI + lane / KCPR.  fp8 caches (a pure-decode launch) take
-      // non-temporal loads, measured 0.9 % faster there; the 16-bit loads
-      // stay cached: in the fused launch beside prefill tiles the same hint
-      // was 4 % slower.
+      // j * KRPI + lane / KCPR.  K and V stream through once, so both take
+      // non-temporal loads: with every cache line requested by exactly one
+      // load, pure decode is 7 % faster and the mixed batch 2 % (with the
+      // older half-line K loads, where a line's second request relied on
+      // the L2, the same hint made the mixed batch 4 % slower).
 #pragma unroll
       for (int j = 0; j < KW; ++j) {
         const int row = j * KRPI + lane / KCPR;
         const u32x4_t* src = reinterpret_cast<const u32x4_t*>(
             reinterpret_cast<const unsigned char*>(kc + base + row * row_stride) +
             (lane % KCPR) * 16);
-        ch.k[j] = KV8 ? __builtin_nontemporal_load(src) : *src;
+        ch.k[j] = __builtin_nontemporal_load(src);
       }
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const CT* vrow = vc + base + (4 * kq + e) * row_stride + r16 * NT;
         if constexpr (VW == 4) {
-          const u32x4_t x = *reinterpret_cast<const u32x4_t*>(vrow);
+          const u32x4_t x = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(vrow));
 #pragma unroll
           for (int w = 0; w < 4; ++w) ch.v[e][w] = x[w];
         } else if constexpr (VW == 2) {
-          const u32x2_t x = KV8 ? __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(vrow))
-                                : *reinterpret_cast<const u32x2_t*>(vrow);
+          const u32x2_t x = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(vrow));
 #pragma unroll
           for (int w = 0; w < 2; ++w) ch.v[e][w] = x[w];
         } else {   // fp8 caches, head_size 64

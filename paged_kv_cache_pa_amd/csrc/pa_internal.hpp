@@ -26,12 +26,15 @@ constexpr int kDecodeCols = 16;
 constexpr int kPrefillRows = 256;
 constexpr int kPrefillKeys = 64;
 constexpr int kQueues = 8;  // one prefill work queue per XCD
-// Cost model of the attention kernel's role split: one CU spends about as
-// long on one prefill tile step (256 query rows x 64 keys) as on streaming
-// this many decode key rows (K and V of one KV head); both scale with
-// head_size.  Measured on MI355X: 2.8 us per bf16/fp16 tile step at
-// head_size 128, 13.5 ns per 512-byte key row with ~96 CUs streaming.
-constexpr float kPrefillStepCost = 200.f;
+// Cost model of the attention kernel's role split: one prefill tile step
+// (256 query rows x 64 keys) is weighed as this many decode key rows (K and
+// V of one KV head); both scale with head_size.  Per-CU measurements on
+// MI355X (2.8 us per bf16/fp16 tile step at head_size 128, 13.5 ns per
+// 512-byte key row with ~96 CUs streaming) put it near 200; with the
+// current decode loads an A/B on the large mixed batch settled on 160
+// (0.8 % faster than 200, in each of 4 interleaved reps; 250 was 1 %
+// slower).  Only batches with both kinds of sequence depend on it.
+constexpr float kPrefillStepCost = 160.f;
 constexpr int kMaxGroup = 128;  // largest supported num_heads / num_kv_heads
 constexpr float kLog2e = 1.4426950408889634f;
 
