@@ -26,8 +26,8 @@ __global__ __launch_bounds__(256) void scatter_kernel(const u32x4_t* __restrict_
     const int32_t s = slots[t];
     if (s < 0) continue;
     const int64_t dst = (int64_t)s * row_chunks + c;
-    kc[dst] = k_new[i];
-    vc[dst] = v_new[i];
+    kc[dst] = __builtin_nontemporal_load(&k_new[i]);   // new rows are read once
+    vc[dst] = __builtin_nontemporal_load(&v_new[i]);
   }
 }
 
@@ -87,8 +87,10 @@ __global__ __launch_bounds__(256) void scatter_fp8_kernel(
     const int32_t s = slots[t];
     if (s < 0) continue;
     const int64_t dst = (int64_t)s * row_chunks + c;
-    kc[dst] = quantize8<T>(k_new[i], k_scale[2 * c], k_scale[2 * c + 1]);
-    vc[dst] = quantize8<T>(v_new[i], v_scale[2 * c], v_scale[2 * c + 1]);
+    const u32x4_t kx = __builtin_nontemporal_load(&k_new[i]);   // new rows are read once
+    const u32x4_t vx = __builtin_nontemporal_load(&v_new[i]);
+    kc[dst] = quantize8<T>(kx, k_scale[2 * c], k_scale[2 * c + 1]);
+    vc[dst] = quantize8<T>(vx, v_scale[2 * c], v_scale[2 * c + 1]);
   }
 }
 
@@ -144,8 +146,8 @@ __global__ __launch_bounds__(256) void scatter_paged_kernel(
     for (int c = lane; c < row_chunks; c += 64) {
       const int64_t src = t * row_chunks + c;
       const int64_t dst = slot * row_chunks + c;
-      kc[dst] = k_new[src];
-      vc[dst] = v_new[src];
+      kc[dst] = __builtin_nontemporal_load(&k_new[src]);
+      vc[dst] = __builtin_nontemporal_load(&v_new[src]);
     }
   }
 }
