@@ -182,11 +182,25 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
     v[kQueues] = has_part;
     block_scan<kQueues + 1>(v, tot, lds);
     if (has_part) a.dec_items[nfull_total + qcarry[kQueues] + v[kQueues]] = make_int2(b, c.nsplit - 1);
-    if (c.ntiles > 0) {
-      for (int kh = 0; kh < a.num_kv_heads; ++kh) {
-        const int x = (int)(((int64_t)b * a.num_kv_heads + kh) & 7);
-        int pos = qstart[x] + qcarry[x] + v[x] + (kh >> 3) * c.ntiles;
-        for (int r = 0; r < c.ntiles; ++r) a.pf_items[pos + r] = make_int4(b, kh, c.ntiles - 1 - r, 0);
+    // A prefill sequence's Hk x ntiles items are written by its whole wave
+    // (the owning lane's values broadcast): one lane storing them in turn
+    // held the plan at ~25 us on a few long prefill chunks.
+    unsigned long long todo = __ballot(c.ntiles > 0);
+    while (todo) {
+      const int src = __builtin_ctzll(todo);
+      todo &= todo - 1;
+      const int bb = __shfl(b, src), nt = __shfl(c.ntiles, src);
+      int vx[kQueues];
+#pragma unroll
+      for (int x = 0; x < kQueues; ++x) vx[x] = __shfl(v[x], src);
+      for (int i = tid & 63; i < a.num_kv_heads * nt; i += 64) {
+        const int kh = i / nt, r = i - kh * nt;
+        const int x = (int)(((int64_t)bb * a.num_kv_heads + kh) & 7);
+        int pos = 0;   // first item of (bb, kh) in queue x
+#pragma unroll
+        for (int q = 0; q < kQueues; ++q)
+          if (q == x) pos = qstart[q] + qcarry[q] + vx[q] + (kh >> 3) * nt;
+        a.pf_items[pos + r] = make_int4(bb, kh, nt - 1 - r, 0);
       }
     }
 #pragma unroll
