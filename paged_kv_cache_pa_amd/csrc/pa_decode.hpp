@@ -417,16 +417,19 @@ __global__ __launch_bounds__(256) void combine_kernel(AttnArgs a) {
     const int d = (idx - n * (D / 4)) * 4;
     const float* src = a.part_acc + (row0 + n) * D + d;
     const int64_t step = (int64_t)ncols * D;
-    float4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+    // Four splits per step, so four independent 16-byte loads are in flight
+    // (two left the kernel waiting through one round trip per pair).
+    float4_t acc[4] = {};
     int s = s0;
-    for (; s + 1 < nsplit; s += 2) {
-      const float4_t v0 = *reinterpret_cast<const float4_t*>(src + s * step);
-      const float4_t v1 = *reinterpret_cast<const float4_t*>(src + (s + 1) * step);
-      acc0 += wts[n][s] * v0;
-      acc1 += wts[n][s + 1] * v1;
+    for (; s + 3 < nsplit; s += 4) {
+      float4_t v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) v[u] = *reinterpret_cast<const float4_t*>(src + (s + u) * step);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) acc[u] += wts[n][s + u] * v[u];
     }
-    if (s < nsplit) acc0 += wts[n][s] * *reinterpret_cast<const float4_t*>(src + s * step);
-    const float4_t o = (acc0 + acc1) * inv_den[n];
+    for (; s < nsplit; ++s) acc[0] += wts[n][s] * *reinterpret_cast<const float4_t*>(src + s * step);
+    const float4_t o = ((acc[0] + acc[1]) + (acc[2] + acc[3])) * inv_den[n];
     const int tok = si.cu + n / G;
     const int h = kh * G + n % G;
     *reinterpret_cast<u32x2_t*>(op + ((int64_t)tok * a.num_heads + h) * D + d) =
