@@ -21,13 +21,17 @@
 //   online softmax per column n       fp32, exp2 with log2(e) folded in
 //   O^T[d][n]  += V_chunk^T . P^T      16x16x16 MFMA, D/16 tiles
 //
-// Lane (kq = l/16, r = l%16) loads, per chunk, 64 B of key row r (the A
+// Lane (kq = l/16, r = l%16) uses, per chunk, 64 B of key row r (the A
 // operand of S^T: contraction elements = 16-byte chunks 4s+kq of the row)
 // and 16 B of each of value rows 4kq..4kq+3 (d range [r*D/16, (r+1)*D/16)),
 // so V needs only register permutes to become the A operand of O^T: tile t
-// row r stands for d = r*D/16 + t.  The accumulator tile of O^T keeps
-// column n in lane n%16, the same lane that owns column n's softmax state,
-// so rescaling is a per-lane multiply.
+// row r stands for d = r*D/16 + t.  Every load instruction covers whole
+// cache rows: the V loads do as they stand; K is loaded with the lanes along
+// its rows and turned into the operand layout through a per-wave LDS slice
+// (a CU streams whole-row loads about twice as fast as the operand shape,
+// 16 rows x 64 B, when few CUs stream).  K and V take non-temporal loads.
+// The accumulator tile of O^T keeps column n in lane n%16, the same lane
+// that owns column n's softmax state, so rescaling is a per-lane multiply.
 //
 // A sequence with one split writes its normalised output directly; longer
 // sequences write (m, l, unnormalised acc) per split and column, merged by
@@ -37,8 +41,9 @@
 // channel, the quantized KV cache of the "Roadmap", phase 3): the same
 // matrix-core program on half the bytes.  A lane's K bytes are made
 // contiguous by giving lane group kq the contraction chunks NS*kq .. +NS-1
-// (Q^T loaded with the same chunk order), so a lane loads 8*NS bytes of its
-// key row and NT bytes of each of its four value rows.  Chunks stay as raw
+// (Q^T loaded with the same chunk order), so a lane uses 8*NS bytes of its
+// key row (staged as above) and loads NT bytes of each of its four value
+// rows.  Chunks stay as raw
 // bytes in flight and are widened to fp16/bf16 (exact) just before their
 // MFMAs.  The K scale of channel d multiplies q_d once per item (in fp32,
 // then rounded to the MFMA type with the rest of Q^T); the V scale
