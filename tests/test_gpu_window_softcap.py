@@ -77,6 +77,26 @@ def test_window_softcap_small(name, make, cap, win):
     assert err <= TOL[wl.dtype]
 
 
+# The plain-attention edge cases (empty sequences, split boundaries, the
+# q_len * G = 16 / 17 path switch, MHA, G = 3, G = 128, block 1024, D 64)
+# with a short window and a cap, and with a longer window alone.
+from test_gpu_parity import EDGE  # noqa: E402
+
+EDGE_OPTS = [(1.5, 37), (0.0, 300)]
+
+
+@pytest.mark.parametrize("case", EDGE, ids=[str(i) for i in range(len(EDGE))])
+@pytest.mark.parametrize("cap,win", EDGE_OPTS, ids=["cap1.5-W37", "W300"])
+def test_window_softcap_edge_cases(case, cap, win):
+    q_lens, lens, hq, hk, dd, bs, dt = case
+    wl = W.custom(q_lens, lens, hq, hk, dd, bs, dtype=dt, seed=11)
+    _log(f"edge softcap={cap} window={win}: {wl.name}")
+    d = device_inputs(wl)
+    out = run_attention(wl, d, softcap=cap, local_window_size=win)
+    assert torch.isfinite(out).all()
+    assert max_err(out, oracle_full(wl, d, softcap=cap, local_window_size=win)) <= TOL[dt]
+
+
 def test_options_change_the_result():
     """The options are not silently ignored: each moves the output far
     beyond the tolerance on the same inputs."""
