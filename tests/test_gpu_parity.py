@@ -14,7 +14,7 @@ import paged_kv_cache_pa_amd as pa
 from paged_kv_cache_pa_amd import workloads as W
 from gpu_util import (NAN_BITS, TOL, device_inputs, max_err, nan_cache, oracle_full, oracle_rows,
                       require_gpu, run_attention)
-from pa_testutil import embed_flex_example, load_golden, to_np64
+from pa_testutil import embed_flex_example, load_golden, oracle_caches, to_np64
 
 pytestmark = pytest.mark.gpu
 
@@ -384,3 +384,20 @@ def test_validate_metadata_through_abi():
     dup[1] = dup[2]
     assert pa.pa_validate_metadata(d["cu"], d["lens"], d["table"], wl.num_blocks, wl.block_size,
                                    slot_mapping=dup, num_tokens=wl.num_tokens) & (1 << 7)
+
+
+def test_longest_context():
+    """The longest context the decode path takes (262144 keys = 256 splits,
+    all combined) with 16 columns (q_len 2, G 8), beside a prefill-path
+    chunk over 32768 keys; plain and with a cap and a window."""
+    wl = W.custom([2, 24], [262144, 32768], 8, 1, 128, 256, dtype="bf16", seed=13)
+    _log(f"longest context: {wl.name}")
+    d = device_inputs(wl, backend="torch")
+    q = to_np64(d["q"])
+    kc, vc = oracle_caches(wl, to_np64(d["k_all"]), to_np64(d["v_all"]))
+    for opts in ({}, {"softcap": 30.0, "local_window_size": 70000}):
+        out = run_attention(wl, d, **opts)
+        ref = oracle.attention(q, wl.cu_seqlens_q, wl.seqlens_kv, wl.block_table, kc, vc,
+                               wl.scale, wl.num_heads, wl.num_kv_heads, wl.block_size, **opts)
+        assert np.isfinite(to_np64(out)).all()
+        assert max_err(out, ref) <= TOL["bf16"], opts
