@@ -401,3 +401,25 @@ def test_longest_context():
                                wl.scale, wl.num_heads, wl.num_kv_heads, wl.block_size, **opts)
         assert np.isfinite(to_np64(out)).all()
         assert max_err(out, ref) <= TOL["bf16"], opts
+
+
+def test_maximum_sequence_count():
+    """65536 sequences (the largest batch the boundary accepts): empty
+    sequences, decodes, 2- and 3-token rows and 20-token prefill chunks over
+    short contexts, checked on sampled rows including the batch's last."""
+    rng = np.random.default_rng(21)
+    B = 65536
+    q_lens = rng.choice([0, 1, 1, 1, 2, 3, 20], size=B).astype(np.int32)
+    lens = q_lens + rng.integers(0, 40, size=B, endpoint=True)
+    lens[q_lens == 0] = 0
+    q_lens[-1], lens[-1] = 3, 45
+    wl = W.custom(q_lens, lens, 8, 2, 64, 16, dtype="f16", seed=21)
+    _log(f"maximum sequence count: {B} sequences, {wl.num_tokens} tokens")
+    d = device_inputs(wl, backend="torch")
+    out = run_attention(wl, d)
+    live = np.flatnonzero(wl.q_lens > 0)
+    picks = [(int(b), int(rng.integers(0, wl.q_lens[b]))) for b in rng.choice(live, 200, replace=False)]
+    picks += [(int(live[0]), 0), (B - 1, 0), (B - 1, 2)]
+    ref, toks = oracle_rows(wl, d, picks)
+    assert np.isfinite(to_np64(out)).all()
+    assert max_err(out[torch.from_numpy(toks).cuda()], ref) <= TOL["f16"]
