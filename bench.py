@@ -153,7 +153,11 @@ def time_workload(wl, steps, warmup, torch, pa, W, extras=False, fp8=False, opts
     for _ in range(warmup):
         step(wl, st, pa)
     torch.cuda.synchronize()
+    # Only the attention kernel is bracketed with events in the timed steps
+    # (events around all four kernels add about 30 us to a 2.3 ms step); the
+    # other kernels' averages come from an untimed pass afterwards.
     pa.profile_read()                       # drop anything recorded earlier
+    pa.profile_select(["attention"])
     pa.profile_enable(True)
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
@@ -168,6 +172,13 @@ def time_workload(wl, steps, warmup, torch, pa, W, extras=False, fp8=False, opts
     pa.profile_enable(False)
     kern = pa.profile_read()
     ms = e0.elapsed_time(e1) / steps
+    pa.profile_select(None)
+    pa.profile_enable(True)
+    for _ in range(steps):
+        step(wl, st, pa)
+    torch.cuda.synchronize()
+    pa.profile_enable(False)
+    kern = {k: (kern[k] if k == "attention" else v) for k, v in pa.profile_read().items()}
     per_kernel = {k: (v[0] / v[1] if v[1] else 0.0) for k, v in kern.items()}
     more = {}
     if extras:
@@ -281,9 +292,13 @@ def summarize(wl, ms, per_kernel, kv_es=ES):
 
 
 def kernel_source_hash():
+    """Hash of the sources the kernels are compiled from: every file under
+    csrc/ except pa_api.hip, the C-ABI host code, which holds no kernel."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "paged_kv_cache_pa_amd", "csrc")
     for f in sorted(os.listdir(csrc)):
+        if f == "pa_api.hip":
+            continue
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]

@@ -397,6 +397,11 @@ const char* pa_last_error(void);
 #define PA_PROFILE_KINDS 5
 pa_status_t pa_profile_enable(int32_t enable);
 pa_status_t pa_profile_read(double* ms, int64_t* launches, int32_t n);
+/* Which kinds profiling brackets with events: bit k of kind_mask selects
+ * kind k (default: every kind).  Launches of other kinds get no events, so
+ * a measurement that needs one kernel's duration adds nothing around the
+ * rest.  Bits from PA_PROFILE_KINDS up are ignored. */
+pa_status_t pa_profile_select(uint32_t kind_mask);
 
 #ifdef __cplusplus
 }

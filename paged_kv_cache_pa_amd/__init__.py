@@ -272,6 +272,19 @@ def profile_enable(on=True):
     check(lib().pa_profile_enable(1 if on else 0))
 
 
+def profile_select(kinds=None):
+    """Time only the kernel kinds named in ``kinds`` (names from
+    PROFILE_KINDS); None: every kind."""
+    if kinds is None:
+        mask = (1 << len(PROFILE_KINDS)) - 1
+    else:
+        unknown = set(kinds) - set(PROFILE_KINDS)
+        if unknown:
+            raise ValueError(f"unknown kernel kinds {sorted(unknown)}")
+        mask = sum(1 << PROFILE_KINDS.index(k) for k in kinds)
+    check(lib().pa_profile_select(mask))
+
+
 def profile_read():
     """{kernel kind: (total ms, launches)} since the last read."""
     n = len(PROFILE_KINDS)

@@ -25,7 +25,7 @@ EXPORTS = ("pa_scatter_kv", "pa_scatter_kv_paged", "pa_scatter_kv_fp8", "pa_rota
            "pa_seqlens_from_past",
            "pa_attention_workspace_size", "pa_attention", "pa_attention_fp8",
            "pa_validate_metadata", "pa_status_string", "pa_last_error",
-           "pa_profile_enable", "pa_profile_read")
+           "pa_profile_enable", "pa_profile_select", "pa_profile_read")
 
 
 class PAError(RuntimeError):
@@ -77,6 +77,8 @@ def lib():
     L.pa_last_error.restype = ctypes.c_char_p
     L.pa_profile_enable.argtypes = [i32]
     L.pa_profile_enable.restype = i32
+    L.pa_profile_select.argtypes = [ctypes.c_uint32]
+    L.pa_profile_select.restype = i32
     L.pa_profile_read.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64),
                                   i32]
     L.pa_profile_read.restype = i32

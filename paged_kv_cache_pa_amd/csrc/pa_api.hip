@@ -55,6 +55,7 @@ struct ProfEvent {
 };
 std::mutex g_prof_mu;
 bool g_prof_on = false;
+uint32_t g_prof_mask = ~0u;   // kinds bracketed while profiling is on
 std::vector<ProfEvent> g_prof_pending;
 std::vector<hipEvent_t> g_prof_pool;
 
@@ -72,7 +73,7 @@ hipEvent_t prof_event() {
 // Runs `launch` on `st`, bracketed by timing events while profiling is on.
 template <typename F>
 hipError_t timed(int kind, hipStream_t st, F&& launch) {
-  if (!g_prof_on) return launch();
+  if (!g_prof_on || !((g_prof_mask >> kind) & 1u)) return launch();
   std::lock_guard<std::mutex> lk(g_prof_mu);
   ProfEvent pe{kind, prof_event(), prof_event()};
   if (pe.start) (void)hipEventRecord(pe.start, st);
@@ -570,6 +571,12 @@ pa_status_t pa_validate_metadata(const int32_t* cu_seqlens_q, const int32_t* seq
 pa_status_t pa_profile_enable(int32_t enable) {
   std::lock_guard<std::mutex> lk(g_prof_mu);
   g_prof_on = enable != 0;
+  return PA_OK;
+}
+
+pa_status_t pa_profile_select(uint32_t kind_mask) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  g_prof_mask = kind_mask;
   return PA_OK;
 }
 

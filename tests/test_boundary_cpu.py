@@ -253,3 +253,17 @@ def test_attention_fp8_rejects_on_host(L, kw, status):
 
 def test_attention_fp8_empty_call_is_ok(L):
     assert _attn8(L, T=0, mq=0) == _lib.PA_OK
+
+
+def test_profile_kind_selection(L):
+    """Profiling state is host-only: selecting kinds, enabling and reading
+    with nothing recorded need no GPU; unknown kind names are rejected."""
+    import paged_kv_cache_pa_amd as pa
+    pa.profile_select(["attention"])
+    pa.profile_enable(True)
+    pa.profile_enable(False)
+    assert all(v == (0.0, 0) for v in pa.profile_read().values())
+    pa.profile_select(None)
+    assert L.pa_profile_select(0xFFFFFFFF) == 0
+    with pytest.raises(ValueError):
+        pa.profile_select(["attention", "softmax"])
