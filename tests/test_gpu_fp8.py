@@ -118,3 +118,18 @@ def test_attention_fp8_precondition_violation_leaves_rows():
     keep = np.r_[cu[0]:cu[1], cu[2]:cu[3]]
     err = max_err(out[torch.from_numpy(keep).cuda()], ref[keep])
     assert err <= TOL[wl.dtype]
+
+
+def test_attention_fp8_longest_context():
+    """fp8 caches at the longest decode context (262144 keys, 256 splits)
+    with 16 columns (q_len 2, G 8) and a 1-token decode beside it; plain and
+    with a cap and a window."""
+    wl = W.custom([2, 1], [262144, 200000], 8, 1, 128, 256, dtype="bf16", seed=17)
+    _log(f"fp8 longest context: {wl.name}")
+    d = device_inputs_fp8(wl, backend="torch")
+    for opts in ({}, {"softcap": 30.0, "local_window_size": 70000}):
+        out = run_attention_fp8(wl, d, **opts)
+        assert torch.isfinite(out).all()
+        err = max_err(out, oracle_full_fp8(wl, d, **opts))
+        _log(f"  {opts} max error {err:.3g}")
+        assert err <= TOL["bf16"], opts
