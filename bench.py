@@ -424,7 +424,7 @@ def main():
                     help="only the 2 GiB copy (reference for counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+        print("bench.py runs on one GPU only: the library has no multi-GPU path "
               "(the paged attention hot path is measured on a single MI355X).", file=sys.stderr)
         sys.exit(2)
 
