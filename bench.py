@@ -320,7 +320,7 @@ def measured_traffic(kernel, workload):
 
 def copy_bandwidth(torch, nbytes=2 << 30, reps=10):
     """Device-to-device copy of a 2 GiB buffer (read + write counted), the
-    measured reference for the HBM peak on this box."""
+    measured reference for the HBM peak on this machine."""
     src = torch.empty(nbytes // 2, dtype=torch.float16, device="cuda")
     src.fill_(1.0)
     dst = torch.empty_like(src)
