@@ -423,3 +423,28 @@ def test_maximum_sequence_count():
     ref, toks = oracle_rows(wl, d, picks)
     assert np.isfinite(to_np64(out)).all()
     assert max_err(out[torch.from_numpy(toks).cuda()], ref) <= TOL["f16"]
+
+
+def test_concurrent_calls_on_two_streams():
+    """Two batches on two streams with their own workspaces, launches
+    interleaved: each output is bitwise the one its batch gets alone."""
+    wl1 = W.custom([1, 40, 1, 3], [3000, 500, 20, 2100], 32, 8, 128, 16, seed=31)
+    wl2 = W.custom([2, 1, 17, 1], [5000, 70, 900, 1025], 32, 8, 128, 16, dtype="bf16", seed=32)
+    _log(f"two streams: {wl1.name} | {wl2.name}")
+    runs = []
+    for wl in (wl1, wl2):
+        d = device_inputs(wl)
+        ref = run_attention(wl, d).clone()
+        need = pa.pa_attention_workspace_size(wl.num_seqs, wl.num_tokens, wl.max_blocks_per_seq,
+                                              wl.num_heads, wl.num_kv_heads, wl.head_size,
+                                              wl.block_size)
+        ws = torch.empty(max(need, 256), dtype=torch.uint8, device="cuda")
+        runs.append((wl, d, ref, torch.empty_like(ref), ws, torch.cuda.Stream()))
+    torch.cuda.synchronize()
+    for _ in range(4):
+        for wl, d, _, out, ws, st in runs:
+            pa.pa_attention(d["q"], d["cu"], d["lens"], d["table"], d["kc"], d["vc"], wl.scale,
+                            wl.num_heads, wl.num_kv_heads, out=out, workspace=ws, stream=st)
+    torch.cuda.synchronize()
+    for wl, _, ref, out, _, _ in runs:
+        assert torch.equal(out, ref), wl.name
