@@ -27,7 +27,9 @@
  *   pointer after a call returns.
  * - `stream` is a hipStream_t passed as void*; NULL is the null stream.  All
  *   kernels are enqueued on it; pa_scatter_kv and pa_attention never
- *   synchronise the host (no device-to-host copies).
+ *   synchronise the host (no device-to-host copies).  Apart from kernel
+ *   launches they enqueue nothing (no memset or copy), so a stream capture
+ *   can record them into a graph that is replayed later.
  * - Element type `dtype`: PA_F16 (IEEE binary16) or PA_BF16 (bfloat16) for
  *   Q, new K/V, the caches and the output.  Arithmetic is fp32: QK^T and
  *   P.V accumulate in fp32 (matrix cores), the softmax runs in fp32, P is

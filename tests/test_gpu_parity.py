@@ -448,3 +448,44 @@ def test_concurrent_calls_on_two_streams():
     torch.cuda.synchronize()
     for wl, _, ref, out, _, _ in runs:
         assert torch.equal(out, ref), wl.name
+
+
+def test_step_under_graph_capture():
+    """The scatter of new rows plus the attention, captured in one graph
+    (caller-owned output and workspace; the entry points only launch
+    kernels): each replay, with eager work and synchronisation between
+    replays, equals the eager step bitwise."""
+    wl = W.custom([1, 40, 1, 3], [3000, 500, 20, 2100], 32, 8, 128, 16, seed=41)
+    _log(f"graph capture: {wl.name}")
+    d = device_inputs(wl)
+    rows = torch.from_numpy(wl.new_rows).cuda()
+    k_new, v_new = d["k_all"][rows].contiguous(), d["v_all"][rows].contiguous()
+    need = pa.pa_attention_workspace_size(wl.num_seqs, wl.num_tokens, wl.max_blocks_per_seq,
+                                          wl.num_heads, wl.num_kv_heads, wl.head_size,
+                                          wl.block_size)
+    ws = torch.empty(max(need, 256), dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(d["q"])
+
+    def step():
+        pa.pa_scatter_kv(k_new, v_new, d["slots_new"], d["kc"], d["vc"])
+        pa.pa_attention(d["q"], d["cu"], d["lens"], d["table"], d["kc"], d["vc"], wl.scale,
+                        wl.num_heads, wl.num_kv_heads, out=out, workspace=ws)
+
+    step()
+    torch.cuda.synchronize()
+    ref = out.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for _ in range(3):
+        out.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref)
