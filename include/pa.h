@@ -59,6 +59,26 @@
 extern "C" {
 #endif
 
+/*
+ * Status codes.
+ *
+ * Defines: the error convention of "[WebGPU] Initial PagedAttention
+ * implementation (1/n)":
+ * - section "Description": the v1 op rejects the options it does not
+ *   support (softcap, local_window_size, bfloat16) up front with
+ *   NOT_IMPLEMENTED; the maintainer review's second cross-cutting point and
+ *   the author's reply do the same for the KV-cache quantization option.
+ *   Here: a shape or option outside this library's limits (head size,
+ *   block size, group size, context length, dtype) is
+ *   PA_ERR_NOT_IMPLEMENTED, returned before any HIP call.
+ * - the design document quoted in the page's later review rounds
+ *   ("Cache-output aliasing"): a violated argument contract (there, cache
+ *   outputs that do not alias the inputs) fails with INVALID_ARGUMENT, as
+ *   the CUDA op does.  Here: a null pointer, a misaligned buffer, a count
+ *   out of range or a non-finite scale is PA_ERR_INVALID_ARGUMENT.
+ * PA_ERR_WORKSPACE_TOO_SMALL (a workspace below the size this library
+ * reports) and PA_ERR_HIP (a failed kernel launch) are this library's own.
+ */
 typedef enum pa_status {
   PA_OK = 0,
   PA_ERR_INVALID_ARGUMENT = 1,
@@ -88,8 +108,9 @@ typedef enum pa_dtype { PA_F16 = 0, PA_BF16 = 1 } pa_dtype_t;
  * v_cache        [num_blocks, block_size, num_kv_heads, head_size] dtype,
  *                updated in place.  Bytes are copied verbatim (bit-exact).
  * Limits: head_size % 8 == 0, num_kv_heads >= 1, block_size >= 1,
- * num_blocks * block_size <= INT32_MAX.  num_tokens == 0 returns PA_OK
- * without launching.
+ * num_blocks * block_size <= INT32_MAX.  k_new, v_new and the caches must be
+ * 16-byte aligned (else PA_ERR_INVALID_ARGUMENT).  num_tokens == 0 returns
+ * PA_OK without launching.
  */
 pa_status_t pa_scatter_kv(const void* k_new, const void* v_new,
                           const int32_t* slot_mapping, void* k_cache,
@@ -215,6 +236,15 @@ pa_status_t pa_rotary_scatter_kv(const void* query, const void* key,
  * pa_attention_workspace_size - bytes of device workspace pa_attention
  * needs for these host-known sizes (an upper bound over every metadata the
  * device could hold).  Returns 0 when the sizes are invalid.
+ *
+ * Defines: the scratch-buffer sizing of "[WebGPU] Initial PagedAttention
+ * implementation (1/n)": the review names WebGPU resource limits (checked
+ * dispatch size, scratch-buffer and storage-binding limits) as a finding
+ * area and the author's reply takes them on; "Roadmap" defers graph capture
+ * until an attention-metadata sizing bound exists.  This library's reading:
+ * every grid and scratch size comes from host-known bounds alone (counts
+ * and max_blocks_per_seq, never device metadata), so the size is known
+ * before the call, needs no readback, and suits capture.
  */
 size_t pa_attention_workspace_size(int32_t num_seqs, int64_t num_tokens,
                                    int32_t max_blocks_per_seq,
@@ -273,8 +303,15 @@ size_t pa_attention_workspace_size(int32_t num_seqs, int64_t num_tokens,
  * Limits: head_size in {64, 128}; block_size a power of two in [16, 1024];
  * num_heads % num_kv_heads == 0 with G <= 128; num_blocks * block_size
  * <= INT32_MAX; max_blocks_per_seq * block_size <= 262144 tokens;
- * num_seqs <= 65536.  Other shapes return PA_ERR_NOT_IMPLEMENTED.
- * num_tokens == 0 returns PA_OK without launching.
+ * num_seqs <= 65536; block_size * num_kv_heads * head_size * 2 (the bytes
+ * of one cache block) <= INT32_MAX; and the work the sizes can produce fits
+ * the kernels' 32-bit counts: num_seqs * ceil(max_blocks_per_seq *
+ * block_size / 1024) * num_kv_heads decode items, the prefill tile items
+ * and the split-KV partial rows each <= 2^30.  Other shapes return
+ * PA_ERR_NOT_IMPLEMENTED (pa_attention_workspace_size returns 0 for them).
+ * q, out and the caches must be 16-byte aligned (else
+ * PA_ERR_INVALID_ARGUMENT).  num_tokens == 0 returns PA_OK without
+ * launching.
  */
 pa_status_t pa_attention(const void* q, const int32_t* cu_seqlens_q,
                          const int32_t* seqlens_kv, const int32_t* block_table,
@@ -358,9 +395,23 @@ pa_status_t pa_attention_fp8(const void* q, const int32_t* cu_seqlens_q,
 
 /*
  * pa_validate_metadata - debug/test check of the device metadata that
- * pa_attention / pa_scatter_kv trust.  Copies the arrays to the host
- * (synchronising `stream`) and writes a bit mask of violations to
- * *violations (host pointer):
+ * pa_attention / pa_scatter_kv trust.
+ *
+ * Defines: the maintainer review of "[WebGPU] Initial PagedAttention
+ * implementation (1/n)" ("Summary": findings concentrated on host-side
+ * validation of device-derived values; first cross-cutting point: two
+ * blocking device-to-host readbacks of the metadata per node and run, which
+ * flush the queue) and the PackedSparseAttentionIndexer commit message
+ * quoted on the "[WebGPU] Implement SparseAttentionIndexer" page
+ * ("Description": packed metadata validated on the device, without host
+ * synchronisation, in the normal provider paths).  This library's reading:
+ * the hot-path entry points never read metadata back and never synchronise;
+ * they trust it and check only host-known sizes.  The full check of the
+ * device arrays is this separate call, for tests and debugging, and it is
+ * the one entry point that synchronises.
+ *
+ * Copies the arrays to the host (synchronising `stream`) and writes a bit
+ * mask of violations to *violations (host pointer):
  *   bit 0 cu_seqlens_q[0] != 0        bit 1 cu_seqlens_q decreasing
  *   bit 2 cu_seqlens_q[num_seqs] != num_tokens
  *   bit 3 seqlens_kv[b] < q_len_b     bit 4 seqlens_kv[b] beyond the table row
@@ -378,7 +429,10 @@ pa_status_t pa_validate_metadata(const int32_t* cu_seqlens_q,
                                  int64_t num_blocks, int32_t block_size,
                                  uint32_t* violations, void* stream);
 
-/* Human-readable name of a status code (static storage). */
+/* Human-readable name of a status code (static storage): the names of the
+ * pa_status_t convention above ("[WebGPU] Initial PagedAttention
+ * implementation (1/n)", "Description" and the review rounds' cache-output
+ * aliasing contract); "PA_ERR_UNKNOWN" for any other value. */
 const char* pa_status_string(int32_t status);
 
 /* Message describing the calling thread's most recent failed call

@@ -33,6 +33,17 @@ def _stream_ptr(t, stream):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
+def _alloc_on(stream, ref, shape, dtype):
+    """A new GPU tensor allocated on the stream the kernels will use, so that
+    the caching allocator does not hand its bytes to other work on another
+    stream while those kernels still run (the tensor may be dropped as soon
+    as the call returns)."""
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream(ref.device)
+    with torch.cuda.stream(s):
+        return torch.empty(shape, dtype=dtype, device=ref.device)
+
+
 def _dev(t, name, dtype=None):
     import torch
     if not isinstance(t, torch.Tensor) or not t.is_cuda:
@@ -89,7 +100,7 @@ def pa_seqlens_from_past(cu_seqlens_q, past_seqlens, out=None, stream=None):
     if past_seqlens.shape != (B,):
         raise ValueError("inconsistent shapes")
     if out is None:
-        out = torch.empty(B, dtype=torch.int32, device=past_seqlens.device)
+        out = _alloc_on(stream, past_seqlens, (B,), torch.int32)
     check(lib().pa_seqlens_from_past(
         _dev(cu_seqlens_q, "cu_seqlens_q", torch.int32), _dev(past_seqlens, "past_seqlens", torch.int32),
         _dev(out, "out", torch.int32), B, _stream_ptr(out, stream)))
@@ -128,7 +139,7 @@ def pa_rotary_scatter_kv(query, cu_seqlens_q, seqlens_kv, block_table, k_cache, 
     if sin_cache is not None and tuple(sin_cache.shape) != tuple(cos_cache.shape):
         raise ValueError("cos_cache and sin_cache shapes differ")
     if q_out is None:
-        q_out = torch.empty((T, num_heads, d), dtype=query.dtype, device=query.device)
+        q_out = _alloc_on(stream, query, (T, num_heads, d), query.dtype)
     elif q_out.numel() != T * num_heads * d or q_out.dtype != query.dtype:
         raise ValueError("q_out must be [T, Hq, D] of the query's dtype")
     opt = lambda t, n: None if t is None else _dev(t, n)  # noqa: E731
@@ -174,12 +185,12 @@ def pa_attention(q, cu_seqlens_q, seqlens_kv, block_table, k_cache, v_cache, sca
     if not (q.dtype == k_cache.dtype == v_cache.dtype):
         raise ValueError("q and caches must share one dtype")
     if out is None:
-        out = torch.empty((T, num_heads, d), dtype=q.dtype, device=q.device)
+        out = _alloc_on(stream, q, (T, num_heads, d), q.dtype)
     elif out.numel() != q.numel() or out.dtype != q.dtype:
         raise ValueError("out must match q")
     need = pa_attention_workspace_size(B, T, MB, num_heads, num_kv_heads, d, bs)
     if workspace is None:
-        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+        workspace = _alloc_on(stream, q, (max(need, 256),), torch.uint8)
     check(lib().pa_attention(
         _dev(q, "q"), _dev(cu_seqlens_q, "cu_seqlens_q", torch.int32),
         _dev(seqlens_kv, "seqlens_kv", torch.int32), _dev(block_table, "block_table", torch.int32),
@@ -233,12 +244,12 @@ def pa_attention_fp8(q, cu_seqlens_q, seqlens_kv, block_table, k_cache, v_cache,
     if k_cache.dtype != torch.uint8 or v_cache.dtype != torch.uint8:
         raise ValueError("fp8 caches hold uint8 codes")
     if out is None:
-        out = torch.empty((T, num_heads, d), dtype=q.dtype, device=q.device)
+        out = _alloc_on(stream, q, (T, num_heads, d), q.dtype)
     elif out.numel() != q.numel() or out.dtype != q.dtype:
         raise ValueError("out must match q")
     need = pa_attention_workspace_size(B, T, MB, num_heads, num_kv_heads, d, bs)
     if workspace is None:
-        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+        workspace = _alloc_on(stream, q, (max(need, 256),), torch.uint8)
     check(lib().pa_attention_fp8(
         _dev(q, "q"), _dev(cu_seqlens_q, "cu_seqlens_q", torch.int32),
         _dev(seqlens_kv, "seqlens_kv", torch.int32), _dev(block_table, "block_table", torch.int32),

@@ -15,6 +15,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <initializer_list>
 #include <mutex>
 #include <vector>
 
@@ -121,7 +122,26 @@ pa_status_t check_shape(const pa::Shape& s) {
   if ((int64_t)s.max_blocks_per_seq * s.block_size > (int64_t)pa::kSplitKeys * pa::kMaxSplitsCombine)
     return fail(PA_ERR_NOT_IMPLEMENTED, "max_blocks_per_seq * block_size exceeds %d tokens",
                 pa::kSplitKeys * pa::kMaxSplitsCombine);
+  // The kernels' 32-bit quantities: a prefill lane's byte offset inside a
+  // cache block, and the work-item, queue and partial-row counts the plan
+  // writes and the fetch counters run past by at most one per wave.
+  if ((int64_t)s.block_size * s.num_kv_heads * s.head_size * 2 > INT32_MAX)
+    return fail(PA_ERR_NOT_IMPLEMENTED, "block_size * num_kv_heads * head_size * 2 bytes exceed "
+                "INT32_MAX");
+  const pa::Layout L = pa::workspace_layout(s);
+  if (L.max_dec_pairs * s.num_kv_heads > pa::kMaxWorkItems || L.max_pf_items > pa::kMaxWorkItems ||
+      L.max_part_rows > pa::kMaxWorkItems)
+    return fail(PA_ERR_NOT_IMPLEMENTED, "work items or split-KV partial rows exceed %d "
+                "(decode items %lld, prefill items %lld, partial rows %lld)", pa::kMaxWorkItems,
+                (long long)(L.max_dec_pairs * s.num_kv_heads), (long long)L.max_pf_items,
+                (long long)L.max_part_rows);
   return PA_OK;
+}
+
+bool aligned16(std::initializer_list<const void*> ptrs) {
+  for (const void* p : ptrs)
+    if (((uintptr_t)p & 15) != 0) return false;
+  return true;
 }
 
 }  // namespace
@@ -200,6 +220,8 @@ pa_status_t pa_scatter_kv(const void* k_new, const void* v_new, const int32_t* s
   if (num_tokens == 0) return PA_OK;
   if (!k_new || !v_new || !slot_mapping || !k_cache || !v_cache)
     return fail(PA_ERR_INVALID_ARGUMENT, "null pointer argument");
+  if (!aligned16({k_new, v_new, k_cache, v_cache}))
+    return fail(PA_ERR_INVALID_ARGUMENT, "tensor pointers must be 16-byte aligned");
   hipStream_t st = (hipStream_t)stream;
   hipError_t e = timed(0, st, [&] {
     return pa::launch_scatter(k_new, v_new, slot_mapping, k_cache, v_cache, num_tokens,
@@ -229,6 +251,8 @@ pa_status_t pa_scatter_kv_fp8(const void* k_new, const void* v_new, const int32_
   if (num_tokens == 0) return PA_OK;
   if (!k_new || !v_new || !slot_mapping || !k_scale || !v_scale || !k_cache || !v_cache)
     return fail(PA_ERR_INVALID_ARGUMENT, "null pointer argument");
+  if (!aligned16({k_new, v_new, k_scale, v_scale, k_cache, v_cache}))
+    return fail(PA_ERR_INVALID_ARGUMENT, "tensor pointers must be 16-byte aligned");
   hipStream_t st = (hipStream_t)stream;
   hipError_t e = timed(0, st, [&] {
     return pa::launch_scatter_fp8(k_new, v_new, slot_mapping, k_scale, v_scale, k_cache, v_cache,
@@ -264,6 +288,8 @@ pa_status_t pa_scatter_kv_paged(const void* k_new, const void* v_new, const int3
   if (num_tokens == 0) return PA_OK;
   if (!k_new || !v_new || !cu_seqlens_q || !seqlens_kv || !block_table || !k_cache || !v_cache)
     return fail(PA_ERR_INVALID_ARGUMENT, "null pointer argument");
+  if (!aligned16({k_new, v_new, k_cache, v_cache}))
+    return fail(PA_ERR_INVALID_ARGUMENT, "tensor pointers must be 16-byte aligned");
   hipStream_t st = (hipStream_t)stream;
   hipError_t e = timed(0, st, [&] {
     return pa::launch_scatter_paged(k_new, v_new, cu_seqlens_q, seqlens_kv, block_table, k_cache,
@@ -401,9 +427,9 @@ static pa_status_t attention_impl(const void* q, const int32_t* cu_seqlens_q,
   if (!q || !cu_seqlens_q || !seqlens_kv || !block_table || !k_cache || !v_cache || !out)
     return fail(PA_ERR_INVALID_ARGUMENT, "null pointer argument");
   if (kv8 && (!k_scale || !v_scale)) return fail(PA_ERR_INVALID_ARGUMENT, "null scale pointer");
+  if (!aligned16({q, out, k_cache, v_cache}) || (kv8 && !aligned16({k_scale, v_scale})))
+    return fail(PA_ERR_INVALID_ARGUMENT, "tensor pointers must be 16-byte aligned");
   const pa::Layout L = pa::workspace_layout(s);
-  if (L.max_part_rows > INT32_MAX)
-    return fail(PA_ERR_NOT_IMPLEMENTED, "split-KV partial rows exceed INT32_MAX");
   if (!workspace) return fail(PA_ERR_INVALID_ARGUMENT, "null workspace");
   if (((uintptr_t)workspace & 255) != 0)
     return fail(PA_ERR_INVALID_ARGUMENT, "workspace is not 256-byte aligned");

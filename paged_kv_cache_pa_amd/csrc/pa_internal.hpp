@@ -36,6 +36,10 @@ constexpr int kQueues = 8;  // one prefill work queue per XCD
 // slower).  Only batches with both kinds of sequence depend on it.
 constexpr float kPrefillStepCost = 160.f;
 constexpr int kMaxGroup = 128;  // largest supported num_heads / num_kv_heads
+// Largest count of decode items, prefill items or split-KV partial rows a
+// call may produce: these are 32-bit on the device, and the fetch counters
+// run past the item count by at most one per wave.
+constexpr int kMaxWorkItems = 1 << 30;
 constexpr float kLog2e = 1.4426950408889634f;
 
 // Counter block at the start of the workspace (int32 slots).  Every fetch

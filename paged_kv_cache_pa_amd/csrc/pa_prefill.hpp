@@ -44,17 +44,16 @@ constexpr int kSchedMfma = 0x008;
 constexpr int kSchedDsRead = 0x100;
 
 // 16-byte-per-lane copy global -> LDS (global_load_lds_dwordx4): lane l
-// copies the 16 bytes at base + voff (base wave-uniform in SGPRs, voff a
-// 32-bit per-lane byte offset) to LDS byte lds_base + 16 * l.  Issued from
-// inline asm so that the compiler does not treat later LDS reads of *other*
-// ring buffers as dependent on it; the kernel orders these copies itself
-// with explicit vmcnt waits and barriers.  The instruction has no register
-// results.
+// copies the 16 bytes at base + voff (base wave-uniform, voff a 32-bit
+// per-lane byte offset) to LDS byte lds_base + 16 * l.  The compiler emits
+// the SGPR-base form and sets M0 (the LDS destination) itself.  The kernel
+// orders these copies with explicit vmcnt waits and barriers; the compiler
+// adds no waits of its own in the tile loops (the instruction listing has
+// the same waits as a hand-written form).
 __device__ inline void lds_dma16(const void* base, uint32_t voff, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
-               :
-               : "s"(lds_base), "v"(voff), "s"(base)
-               : "memory", "m0");
+  __builtin_amdgcn_global_load_lds((const unsigned char*)base + voff,
+                                   (__attribute__((address_space(3))) void*)(uintptr_t)lds_base,
+                                   16, 0, 0);
 }
 
 // Wait until at most N vector-memory operations of this wave are in flight.

@@ -116,6 +116,21 @@ int main() {
                           PA_F16, P, ws, nullptr),
          PA_ERR_HIP, "fp8 attention valid (stubbed launch)");
 
+  // Shapes at the kernels' 32-bit limits, and misaligned tensors.
+  if (pa_attention_workspace_size(1, 8, 1, 8191, 8191, 128, 1024) == 0) ++g_failures;
+  if (pa_attention_workspace_size(1, 8, 1, 8192, 8192, 128, 1024) != 0) ++g_failures;
+  if (pa_attention_workspace_size(65536, 65536, 16384, 64, 64, 128, 16) == 0) ++g_failures;
+  if (pa_attention_workspace_size(65536, 65536, 16384, 65, 65, 128, 16) != 0) ++g_failures;
+  expect(pa_attention(P, I, I, I, P, P, P, 65536, 5, 16384, 8, 0.125f, 0.f, 0, 65, 65, 128, 16,
+                      PA_F16, P, ws, nullptr),
+         PA_ERR_NOT_IMPLEMENTED, "attention decode items beyond 2^30");
+  void* const P8 = (void*)(uintptr_t)0x1008;
+  expect(pa_attention(P8, I, I, I, P, P, P, 2, 5, 2, 8, 0.125f, 0.f, 0, 4, 2, 64, 16, PA_F16, P,
+                      ws, nullptr),
+         PA_ERR_INVALID_ARGUMENT, "attention misaligned q");
+  expect(pa_scatter_kv(P, P, I, P8, P, 5, 8, 2, 64, 16, PA_F16, nullptr),
+         PA_ERR_INVALID_ARGUMENT, "scatter misaligned cache");
+
   // Metadata validator and profiling arguments.
   uint32_t viol = 0;
   expect(pa_validate_metadata(nullptr, I, I, nullptr, 2, 5, 2, 8, 16, &viol, nullptr),

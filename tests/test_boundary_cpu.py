@@ -45,6 +45,18 @@ def test_workspace_size(L):
     assert L.pa_attention_workspace_size(2, 5, 2, 4, 2, 64, 24) == 0      # block size
 
 
+def test_workspace_size_at_device_arithmetic_limits(L):
+    """Shapes whose 32-bit device quantities would overflow are rejected
+    (size 0), and the largest accepted ones still get a size."""
+    # One cache block of 1024 x 8191 heads x 128 x 2 bytes fits 31 bits; 8192 heads do not.
+    assert L.pa_attention_workspace_size(1, 8, 1, 8191, 8191, 128, 1024) > 0
+    assert L.pa_attention_workspace_size(1, 8, 1, 8192, 8192, 128, 1024) == 0
+    # 65536 sequences x 256 splits x 64 KV heads = 2^30 decode items (and 2^30
+    # partial rows): accepted; 65 KV heads: rejected.
+    assert L.pa_attention_workspace_size(65536, 65536, 16384, 64, 64, 128, 16) > 0
+    assert L.pa_attention_workspace_size(65536, 65536, 16384, 65, 65, 128, 16) == 0
+
+
 FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: every call below fails before a launch
 
 
@@ -82,6 +94,11 @@ def _attn(L, **kw):
     (dict(wsb=16), _lib.PA_ERR_WORKSPACE_TOO_SMALL),
     (dict(NB=1 << 28, bs=16), _lib.PA_ERR_NOT_IMPLEMENTED),   # slots beyond int32
     (dict(MB=16385, bs=16), _lib.PA_ERR_NOT_IMPLEMENTED),     # context beyond 262144 tokens
+    (dict(hq=8192, hk=8192, MB=1, bs=1024, d=128), _lib.PA_ERR_NOT_IMPLEMENTED),  # block > 2^31 B
+    (dict(B=65536, MB=16384, hq=65, hk=65, d=128), _lib.PA_ERR_NOT_IMPLEMENTED),  # > 2^30 items
+    (dict(q=ctypes.c_void_p(0x1008), wsb=1 << 30), _lib.PA_ERR_INVALID_ARGUMENT),  # q unaligned
+    (dict(out=ctypes.c_void_p(0x1002), wsb=1 << 30), _lib.PA_ERR_INVALID_ARGUMENT),
+    (dict(vc=ctypes.c_void_p(0x1004), wsb=1 << 30), _lib.PA_ERR_INVALID_ARGUMENT),
 ])
 def test_attention_rejects_on_host(L, kw, status):
     assert _attn(L, **kw) == status
@@ -106,6 +123,8 @@ def _scatter(L, **kw):
     (dict(hk=0), _lib.PA_ERR_INVALID_ARGUMENT),
     (dict(slots=None), _lib.PA_ERR_INVALID_ARGUMENT),
     (dict(NB=1 << 30, bs=16), _lib.PA_ERR_NOT_IMPLEMENTED),
+    (dict(k=ctypes.c_void_p(0x1008)), _lib.PA_ERR_INVALID_ARGUMENT),   # unaligned K rows
+    (dict(vc=ctypes.c_void_p(0x1002)), _lib.PA_ERR_INVALID_ARGUMENT),
 ])
 def test_scatter_rejects_on_host(L, kw, status):
     assert _scatter(L, **kw) == status

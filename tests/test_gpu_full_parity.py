@@ -1,0 +1,139 @@
+"""Full-output parity on the multi-GB workloads (pure decode, chunked
+prefill, large mixed batch), in the launch configuration the benchmark
+times.
+
+* Attention: EVERY output row of every sequence is compared with the fp64
+  oracle.  The oracle runs one sequence at a time (its caches hold only that
+  sequence's blocks, filled by the oracle's own scatter of the generator's
+  values), on a pool of host threads with BLAS held to one thread each.
+* Scatter: after all KV positions are written, the WHOLE K and V caches are
+  compared bit for bit with the oracle's scatter into NaN-sentinel pools,
+  one chunk of blocks at a time (so host memory stays bounded).
+
+Bars: scatter bit-exact; attention max abs error <= 2e-3 (fp16) /
+1.6e-2 (bf16).  The worst error per workload is printed.
+"""
+import os
+import time
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from paged_kv_cache_pa_amd import workloads as W
+from gpu_util import NAN_BITS, TOL, device_inputs, run_attention
+from pa_testutil import oracle_caches_for
+
+pytestmark = pytest.mark.gpu
+
+# Host threads for the oracle: the machine's CPU share, whatever os.cpu_count() says.
+WORKERS = min(16, len(os.sched_getaffinity(0)))
+CHUNK_BLOCKS_BYTES = 1 << 30     # oracle pool chunk for the whole-cache scatter check
+
+
+def _log(msg):
+    print(msg, flush=True)
+
+
+def _bits(t):
+    return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def _decode(bits, dtype):
+    """Stored fp16/bf16 bit patterns -> float64, exactly."""
+    if dtype == "f16":
+        return bits.view(np.float16).astype(np.float64)
+    return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def _blas_one_thread():
+    try:
+        from threadpoolctl import threadpool_limits
+        return threadpool_limits(1)
+    except ImportError:          # pragma: no cover - threadpoolctl is in the image
+        import contextlib
+        return contextlib.nullcontext()
+
+
+@pytest.mark.parametrize("idx", [3, 4, 5])
+def test_every_row_full_workload(idx):
+    wl = W.by_index(idx)
+    _log(f"full parity: {wl.name}")
+    d = device_inputs(wl, backend="torch")
+    out = run_attention(wl, d)
+    assert torch.isfinite(out).all()
+    kb, vb = _bits(d["k_all"]), _bits(d["v_all"])
+    qh = d["q"].float().cpu().numpy().astype(np.float64)
+    oh = out.float().cpu().numpy().astype(np.float64)
+    del d, out
+    torch.cuda.empty_cache()
+    cu, kv_cu = wl.cu_seqlens_q, wl.kv_cu
+
+    def one(b):
+        ql = int(cu[b + 1] - cu[b])
+        if ql == 0:
+            return b, 0.0
+        lo, hi = int(kv_cu[b]), int(kv_cu[b + 1])
+        kc, vc = oracle_caches_for(wl, [b], lambda _: _decode(kb[lo:hi], wl.dtype),
+                                   lambda _: _decode(vb[lo:hi], wl.dtype))
+        ref = oracle.attention(qh[cu[b]:cu[b + 1]], np.array([0, ql], np.int32),
+                               wl.seqlens_kv[b:b + 1], wl.block_table[b:b + 1], kc, vc,
+                               wl.scale, wl.num_heads, wl.num_kv_heads, wl.block_size)
+        return b, float(np.abs(oh[cu[b]:cu[b + 1]] - ref).max())
+
+    t0 = time.perf_counter()
+    # Longest sequences first so the pool's tail is short.
+    order = sorted(range(wl.num_seqs), key=lambda b: -int(wl.q_lens[b]) * int(wl.seqlens_kv[b])
+                   - int(wl.seqlens_kv[b]))
+    errs = {}
+    last = t0
+    with _blas_one_thread(), ThreadPoolExecutor(WORKERS) as ex:
+        for b, e in ex.map(one, order):
+            errs[b] = e
+            if time.perf_counter() - last > 20.0:
+                last = time.perf_counter()
+                _log(f"  ... {len(errs)}/{wl.num_seqs} sequences, {last - t0:.0f} s")
+    worst_b = max(errs, key=errs.get)
+    worst = errs[worst_b]
+    _log(f"  {wl.num_tokens} rows x {wl.num_heads} heads of {wl.num_seqs} sequences, oracle "
+         f"{time.perf_counter() - t0:.1f} s on {WORKERS} threads; worst max abs error "
+         f"{worst:.3g} (sequence {worst_b}, q_len {int(wl.q_lens[worst_b])}, "
+         f"kv {int(wl.seqlens_kv[worst_b])}); bar {TOL[wl.dtype]}")
+    bad = {b: e for b, e in errs.items() if not e <= TOL[wl.dtype]}
+    assert not bad, f"{len(bad)} sequences over the bar, e.g. {sorted(bad.items())[:5]}"
+
+
+@pytest.mark.parametrize("idx", [3, 4, 5])
+def test_whole_cache_scatter_full_workload(idx):
+    """Every byte of both caches after the scatter of all KV positions equals
+    the oracle's scatter into a NaN-sentinel pool (unused slots and blocks
+    keep the sentinel)."""
+    wl = W.by_index(idx)
+    _log(f"whole-cache scatter: {wl.name}")
+    d = device_inputs(wl, backend="torch")
+    torch.cuda.synchronize()
+    kb, vb = _bits(d["k_all"]), _bits(d["v_all"])
+    row = wl.block_size * wl.num_kv_heads * wl.head_size          # elements per block
+    step = max(1, CHUNK_BLOCKS_BYTES // (row * 2))
+    slots = wl.kv_slots.astype(np.int64)
+    blk_of = slots // wl.block_size
+    order = np.argsort(blk_of, kind="stable")
+    sorted_blk = blk_of[order]
+    shape = (wl.block_size, wl.num_kv_heads, wl.head_size)
+    t0 = time.perf_counter()
+    for a in range(0, wl.num_blocks, step):
+        e = min(wl.num_blocks, a + step)
+        i0, i1 = np.searchsorted(sorted_blk, [a, e])
+        toks = order[i0:i1]
+        kref = np.full((e - a,) + shape, NAN_BITS, dtype=np.uint16)
+        vref = np.full((e - a,) + shape, NAN_BITS, dtype=np.uint16)
+        # The oracle's scatter into this chunk of the pool: the chunk's
+        # tokens, with slots counted from the chunk's first block.
+        oracle.scatter_kv(kb[toks], vb[toks], slots[toks] - a * wl.block_size, kref, vref,
+                          wl.block_size)
+        assert np.array_equal(_bits(d["kc"][a:e]), kref), (a, e)
+        assert np.array_equal(_bits(d["vc"][a:e]), vref), (a, e)
+    _log(f"  {wl.num_blocks} blocks x 2 caches ({2 * wl.num_blocks * row * 2 / 2**30:.1f} GiB) "
+         f"bit-exact, {len(slots)} slots written, {time.perf_counter() - t0:.1f} s")

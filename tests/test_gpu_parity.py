@@ -450,6 +450,35 @@ def test_concurrent_calls_on_two_streams():
         assert torch.equal(out, ref), wl.name
 
 
+def test_default_workspace_on_side_streams():
+    """Calls on side streams that leave out and workspace to the binding:
+    the binding allocates both on the call's stream, so allocations made on
+    the current stream right after each call (filled with zeros, which keep
+    every work-list index in range) never take the bytes of a workspace that
+    a side-stream kernel still uses.  Every output is bitwise its batch's
+    solo output."""
+    wl1 = W.custom([1, 40, 1, 3], [3000, 500, 20, 2100], 32, 8, 128, 16, seed=33)
+    wl2 = W.custom([2, 1, 17, 1], [5000, 70, 900, 1025], 32, 8, 128, 16, dtype="bf16", seed=34)
+    _log(f"default workspace on side streams: {wl1.name} | {wl2.name}")
+    runs = []
+    for wl in (wl1, wl2):
+        d = device_inputs(wl)
+        runs.append((wl, d, run_attention(wl, d).clone(), torch.cuda.Stream()))
+    torch.cuda.synchronize()
+    outs, junk = [], []
+    for _ in range(4):
+        for wl, d, _, st in runs:
+            st.wait_stream(torch.cuda.current_stream())
+            o = pa.pa_attention(d["q"], d["cu"], d["lens"], d["table"], d["kc"], d["vc"],
+                                wl.scale, wl.num_heads, wl.num_kv_heads, stream=st)
+            outs.append((wl.name, o))
+            junk.append(torch.zeros(1 << 22, dtype=torch.uint8, device="cuda"))
+    torch.cuda.synchronize()
+    refs = {wl.name: ref for wl, _, ref, _ in runs}
+    for name, o in outs:
+        assert torch.equal(o, refs[name]), name
+
+
 def test_step_under_graph_capture():
     """The scatter of new rows plus the attention, captured in one graph
     (caller-owned output and workspace; the entry points only launch
