@@ -325,6 +325,41 @@ pa_status_t pa_attention(const void* q, const int32_t* cu_seqlens_q,
                          void* stream);
 
 /*
+ * pa_attention_noalloc - pa_attention without a caller workspace and
+ * without any device allocation in the call.
+ *
+ * For callers that cannot allocate device memory around the call: code
+ * under stream/graph capture, tight serving loops, harnesses that forbid
+ * allocation.  The result is pa_attention's, from the same kernels; the plan
+ * lists, fetch counters and split-KV partials live in a fixed 256 MiB
+ * device-resident scratch array inside the library (one per GPU, held until
+ * the process ends, set up on the first call on each device).
+ *
+ * Arguments, limits, status codes and empty calls as for pa_attention,
+ * minus workspace / workspace_bytes.  Sizes whose workspace
+ * (pa_attention_workspace_size) exceeds 256 MiB return
+ * PA_ERR_WORKSPACE_TOO_SMALL before any HIP call (the decode- and
+ * prefill-shaped batches this library is measured on need 33 MiB and
+ * 3 MiB; a mixed batch of 256 sequences with 32768-token tables needs more:
+ * use pa_attention there).  The call launches kernels only (no allocation,
+ * memset or copy); the plan kernel initialises what must start at zero.
+ *
+ * All calls on one GPU share that GPU's scratch, which keeps the last
+ * call's contents: calls that overlap in time on one GPU (concurrent
+ * streams, or threads) race and must be serialised by the caller.
+ */
+pa_status_t pa_attention_noalloc(const void* q, const int32_t* cu_seqlens_q,
+                                 const int32_t* seqlens_kv,
+                                 const int32_t* block_table,
+                                 const void* k_cache, const void* v_cache,
+                                 void* out, int32_t num_seqs, int64_t num_tokens,
+                                 int32_t max_blocks_per_seq, int64_t num_blocks,
+                                 float scale, float softcap,
+                                 int32_t local_window_size, int32_t num_heads,
+                                 int32_t num_kv_heads, int32_t head_size,
+                                 int32_t block_size, int32_t dtype, void* stream);
+
+/*
  * pa_scatter_kv_fp8 - pa_scatter_kv into fp8 caches: each new K/V element is
  * quantized to an 8-bit float with a per-(KV head, channel) scale.
  *

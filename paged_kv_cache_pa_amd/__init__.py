@@ -12,7 +12,7 @@ import ctypes
 from ._lib import (PA_BF16, PA_F16, PROFILE_KINDS, PAError, check, lib)  # noqa: F401
 
 __all__ = ["pa_scatter_kv", "pa_scatter_kv_paged", "pa_scatter_kv_fp8", "pa_seqlens_from_past",
-           "pa_attention", "pa_attention_fp8", "pa_rotary_scatter_kv",
+           "pa_attention", "pa_attention_noalloc", "pa_attention_fp8", "pa_rotary_scatter_kv",
            "pa_attention_workspace_size", "pa_validate_metadata", "profile_enable",
            "profile_read", "PAError"]
 
@@ -199,6 +199,37 @@ def pa_attention(q, cu_seqlens_q, seqlens_kv, block_table, k_cache, v_cache, sca
         _dtype_code(q),
         _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
         _stream_ptr(q, stream)))
+    return out
+
+
+def pa_attention_noalloc(q, cu_seqlens_q, seqlens_kv, block_table, k_cache, v_cache, scale,
+                         num_heads, num_kv_heads, out, stream=None, softcap=0.0,
+                         local_window_size=0):
+    """pa_attention with the library's fixed device scratch instead of a
+    workspace: nothing is allocated here or in the library.  ``out`` (the
+    caller's [T, Hq, D] tensor) is required for the same reason.  Calls
+    that overlap on one GPU share that scratch and must not run
+    concurrently."""
+    import torch
+    T = q.shape[0]
+    d = k_cache.shape[-1]
+    nb, bs = k_cache.shape[0], k_cache.shape[1]
+    B = seqlens_kv.shape[0]
+    MB = block_table.shape[1]
+    if q.numel() != T * num_heads * d or cu_seqlens_q.shape != (B + 1,) \
+            or block_table.shape[0] != B or tuple(v_cache.shape) != tuple(k_cache.shape) \
+            or k_cache.shape[2] != num_kv_heads:
+        raise ValueError("inconsistent shapes")
+    if not (q.dtype == k_cache.dtype == v_cache.dtype):
+        raise ValueError("q and caches must share one dtype")
+    if out is None or out.numel() != q.numel() or out.dtype != q.dtype:
+        raise ValueError("out must be given and match q")
+    check(lib().pa_attention_noalloc(
+        _dev(q, "q"), _dev(cu_seqlens_q, "cu_seqlens_q", torch.int32),
+        _dev(seqlens_kv, "seqlens_kv", torch.int32), _dev(block_table, "block_table", torch.int32),
+        _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), _dev(out, "out"), B, T, MB, nb,
+        float(scale), float(softcap), int(local_window_size), num_heads, num_kv_heads, d, bs,
+        _dtype_code(q), _stream_ptr(q, stream)))
     return out
 
 

@@ -518,6 +518,72 @@ pa_status_t pa_attention(const void* q, const int32_t* cu_seqlens_q, const int32
                         workspace_bytes, stream, false);
 }
 
+// ------------------------------------------------ allocation-free variant
+// The fixed device scratch of pa_attention_noalloc: plan lists, counters and
+// split-KV partials live here instead of in a caller workspace.  Each GPU the
+// library runs on holds its own copy until the process ends.  In host code
+// `scratch` only names the symbol; its device address (per device) comes
+// from hipGetSymbolAddress and is the only form passed to kernels.
+constexpr size_t kScratchBytes = size_t(256) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept.
+hipError_t scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_dev[dev] = p;
+  }
+  *out = g_scratch_dev[dev];
+  return hipSuccess;
+}
+}  // namespace
+
+pa_status_t pa_attention_noalloc(const void* q, const int32_t* cu_seqlens_q,
+                                 const int32_t* seqlens_kv, const int32_t* block_table,
+                                 const void* k_cache, const void* v_cache, void* out,
+                                 int32_t num_seqs, int64_t num_tokens, int32_t max_blocks_per_seq,
+                                 int64_t num_blocks, float scale, float softcap,
+                                 int32_t local_window_size, int32_t num_heads,
+                                 int32_t num_kv_heads, int32_t head_size, int32_t block_size,
+                                 int32_t dtype, void* stream) {
+  g_err[0] = 0;
+  if (dtype != PA_F16 && dtype != PA_BF16)
+    return fail(PA_ERR_NOT_IMPLEMENTED, "dtype=%d (supported: PA_F16, PA_BF16)", dtype);
+  // Sizes first, on the host, before any HIP call: the scratch must hold the
+  // workspace pa_attention would need for these sizes.
+  const pa::Shape s{num_seqs, num_tokens, max_blocks_per_seq, num_heads, num_kv_heads, head_size,
+                    block_size};
+  pa_status_t cs = check_shape(s);
+  if (cs != PA_OK) return cs;
+  const size_t need = pa::workspace_layout(s).total;
+  if (need > kScratchBytes)
+    return fail(PA_ERR_WORKSPACE_TOO_SMALL,
+                "these sizes need %zu bytes of scratch; the fixed scratch holds %zu (use "
+                "pa_attention with a caller workspace)", need, kScratchBytes);
+  if (num_tokens == 0) return PA_OK;
+  void* ws = nullptr;
+  hipError_t e = scratch_address(&ws);
+  if (e != hipSuccess) return hip_fail(e, "scratch address");
+  return attention_impl(q, cu_seqlens_q, seqlens_kv, block_table, k_cache, v_cache, nullptr,
+                        nullptr, out, num_seqs, num_tokens, max_blocks_per_seq, num_blocks, scale,
+                        softcap, local_window_size, num_heads, num_kv_heads, head_size,
+                        block_size, dtype, ws, kScratchBytes, stream, false);
+}
+
 pa_status_t pa_attention_fp8(const void* q, const int32_t* cu_seqlens_q,
                              const int32_t* seqlens_kv, const int32_t* block_table,
                              const void* k_cache, const void* v_cache, const float* k_scale,

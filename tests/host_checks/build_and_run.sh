@@ -13,7 +13,10 @@ HIPCC="${HIPCC:-/opt/rocm/bin/hipcc}"
 INC=(-I "$ROOT/include" -I "$ROOT/paged_kv_cache_pa_amd/csrc")
 SAN=(-Xarch_host -fsanitize=address -Xarch_host -fsanitize=undefined
      -Xarch_host -fno-sanitize-recover=undefined -Xarch_host -fno-omit-frame-pointer)
-"$HIPCC" --offload-arch=gfx950 --cuda-host-only -O1 -g -std=c++17 "${SAN[@]}" "${INC[@]}" \
+# pa_api.hip with its device part (the allocation-free entry point's scratch
+# array has no kernels, but the host code registers it); sanitizers apply to
+# the host side only.
+"$HIPCC" --offload-arch=gfx950 -O1 -g -std=c++17 "${SAN[@]}" "${INC[@]}" \
   -c "$ROOT/paged_kv_cache_pa_amd/csrc/pa_api.hip" -o "$OUT/pa_api.o"
 "$HIPCC" --offload-arch=gfx950 --cuda-host-only -O1 -g -std=c++17 "${SAN[@]}" "${INC[@]}" \
   -x hip -c "$HERE/stubs.cpp" -o "$OUT/stubs.o"

@@ -131,6 +131,18 @@ int main() {
   expect(pa_scatter_kv(P, P, I, P8, P, 5, 8, 2, 64, 16, PA_F16, nullptr),
          PA_ERR_INVALID_ARGUMENT, "scatter misaligned cache");
 
+  // pa_attention_noalloc: rejections and the empty call return before any
+  // HIP call (the scratch lookup needs a GPU).
+  expect(pa_attention_noalloc(P, I, I, I, P, P, P, 256, 8432, 2048, 500224, 0.088f, 0.f, 0, 64, 8,
+                              128, 16, PA_BF16, nullptr),
+         PA_ERR_WORKSPACE_TOO_SMALL, "noalloc workspace beyond the fixed scratch");
+  expect(pa_attention_noalloc(P, I, I, I, P, P, P, 2, 5, 2, 8, 0.125f, 0.f, 0, 4, 3, 64, 16,
+                              PA_F16, nullptr),
+         PA_ERR_INVALID_ARGUMENT, "noalloc Hq % Hk");
+  expect(pa_attention_noalloc(nullptr, I, I, I, P, P, nullptr, 2, 0, 2, 8, 0.125f, 0.f, 0, 4, 2,
+                              64, 16, PA_F16, nullptr),
+         PA_OK, "noalloc empty call");
+
   // Metadata validator and profiling arguments.
   uint32_t viol = 0;
   expect(pa_validate_metadata(nullptr, I, I, nullptr, 2, 5, 2, 8, 16, &viol, nullptr),

@@ -286,3 +286,30 @@ def test_profile_kind_selection(L):
     assert L.pa_profile_select(0xFFFFFFFF) == 0
     with pytest.raises(ValueError):
         pa.profile_select(["attention", "softmax"])
+
+
+def _noalloc(L, **kw):
+    a = dict(q=FAKE, cu=FAKE, lens=FAKE, table=FAKE, kc=FAKE, vc=FAKE, out=FAKE, B=2, T=5, MB=2,
+             NB=8, scale=0.125, cap=0.0, win=0, hq=4, hk=2, d=64, bs=16, dtype=0, st=None)
+    a.update(kw)
+    return L.pa_attention_noalloc(a["q"], a["cu"], a["lens"], a["table"], a["kc"], a["vc"],
+                                  a["out"], a["B"], a["T"], a["MB"], a["NB"], a["scale"],
+                                  a["cap"], a["win"], a["hq"], a["hk"], a["d"], a["bs"],
+                                  a["dtype"], a["st"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    # The large mixed batch's sizes need 520 MiB of workspace > the 256 MiB scratch.
+    (dict(B=256, T=8432, MB=2048, NB=500224, hq=64, hk=8, d=128, bs=16, dtype=1),
+     _lib.PA_ERR_WORKSPACE_TOO_SMALL),
+    (dict(hk=3), _lib.PA_ERR_INVALID_ARGUMENT),
+    (dict(d=96), _lib.PA_ERR_NOT_IMPLEMENTED),
+    (dict(dtype=5), _lib.PA_ERR_NOT_IMPLEMENTED),
+])
+def test_attention_noalloc_rejects_on_host(L, kw, status):
+    assert _noalloc(L, **kw) == status
+    assert L.pa_last_error() != b""
+
+
+def test_attention_noalloc_empty_call_is_ok(L):
+    assert _noalloc(L, T=0, q=None, out=None) == _lib.PA_OK
