@@ -6,7 +6,10 @@ whole continuous batch, on the large mixed workload (16 prefill chunks of
 512 tokens + 240 decodes with 1k-32k contexts, 64/8 heads, D 128, block 16,
 bf16).  Inputs are resident in HBM before the timed region.  The line also
 carries the pure-decode and chunked-prefill workloads' figures, the
-roofline of the dominant kernel, and the fp64 oracle timed on host cores.
+roofline of the dominant kernel, the fp64 oracle timed on host cores on a
+sample of the headline batch (cpu_baseline), and per_config: every other
+configuration's step latency and tokens/s with the oracle's attention and
+scatter times on the host and the max abs error of the timed GPU output.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload mixed|decode|prefill]
 """
@@ -25,6 +28,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK = 8.0e12          # B/s, MI355X HBM3E
 MFMA_PEAK = 2.5e15         # FLOP/s, dense fp16/bf16 matrix cores
 ES = 2                     # bytes per fp16/bf16 element
+TOL = {"f16": 2e-3, "bf16": 1.6e-2}   # attention bars: max abs error on U(-1,1) inputs
 WORKLOADS = {"tiny": 1, "small": 2, "decode": 3, "prefill": 4, "mixed": 5}
 
 
@@ -143,7 +147,8 @@ def sub_batch(wl, st, sel, torch, pa):
     return sub
 
 
-def time_workload(wl, steps, warmup, torch, pa, W, extras=False, fp8=False, opts=None):
+def time_workload(wl, steps, warmup, torch, pa, W, extras=False, fp8=False, opts=None,
+                  keep=False):
     """Back-to-back timing of `steps` steps (the headline figure) and the
     per-kernel averages; with `extras`, also per-rep scrubbed timing of the
     step and, for a batch that mixes both kinds, its decode-only and
@@ -181,6 +186,9 @@ def time_workload(wl, steps, warmup, torch, pa, W, extras=False, fp8=False, opts
     kern = {k: (kern[k] if k == "attention" else v) for k, v in pa.profile_read().items()}
     per_kernel = {k: (v[0] / v[1] if v[1] else 0.0) for k, v in kern.items()}
     more = {}
+    if keep:   # the timed run's output and the inputs it was computed from
+        more["out"] = st["out"].clone()
+        more["vals"] = st["vals"]
     if extras:
         scrub = torch.empty(SCRUB_BYTES, dtype=torch.uint8, device="cuda")
         more["step_reps"] = per_rep_times(lambda: step(wl, st, pa), steps, torch, scrub)
@@ -404,6 +412,114 @@ def cpu_baseline(wl, W, torch, budget_s=20.0, opts=None):
                       f"({int(q_lens.sum())} query tokens)"}
 
 
+# ------------------------------------------------------------- per config
+def _host_rows(t):
+    """GPU fp16/bf16 rows -> host float32 (exact), kept as float32 to halve
+    host memory; converted to float64 per sequence."""
+    return t.float().cpu().numpy()
+
+
+def oracle_check(wl, vals, out, threads, opts=None):
+    """The fp64 oracle over every sequence of a workload, in three phases:
+    each sequence's past rows are scattered into a dict-of-blocks cache of
+    its own (untimed); the step's new rows of every sequence are scattered
+    (timed, one thread: the scatter); the attention of every sequence's new
+    rows is computed one sequence at a time on `threads` host threads with
+    BLAS held to one thread each (timed: the attention).  Returns both wall
+    times, the thread counts and the max abs error of `out` (the GPU output
+    of the timed run)."""
+    import oracle
+    from concurrent.futures import ThreadPoolExecutor
+    k_all, v_all = _host_rows(vals["k_all"]), _host_rows(vals["v_all"])
+    qh = vals["q"].float().cpu().numpy().astype(np.float64)
+    oh = out.float().cpu().numpy().astype(np.float64)
+    cu, kv_cu = wl.cu_seqlens_q, wl.kv_cu
+    shape = (wl.block_size, wl.num_kv_heads, wl.head_size)
+    seqs = [b for b in range(wl.num_seqs) if cu[b + 1] > cu[b]]
+    caches = {}
+
+    def build(b):        # float32 holds the fp16/bf16 values exactly
+        lo, nl = int(kv_cu[b]), int(kv_cu[b + 1] - wl.q_lens[b])
+        kc, vc = {}, {}
+        for x in wl.block_table[b, :-(-int(wl.seqlens_kv[b]) // wl.block_size)]:
+            kc.setdefault(int(x), np.zeros(shape, np.float32))
+            vc.setdefault(int(x), np.zeros(shape, np.float32))
+        oracle.scatter_kv(k_all[lo:nl], v_all[lo:nl], wl.kv_slots[lo:nl], kc, vc, wl.block_size)
+        caches[b] = (kc, vc)
+
+    def attend(b):
+        kc, vc = caches[b]
+        ql = int(cu[b + 1] - cu[b])
+        ref = oracle.attention(qh[cu[b]:cu[b + 1]], np.array([0, ql], np.int32),
+                               wl.seqlens_kv[b:b + 1], wl.block_table[b:b + 1], kc, vc, wl.scale,
+                               wl.num_heads, wl.num_kv_heads, wl.block_size, **(opts or {}))
+        return float(np.abs(oh[cu[b]:cu[b + 1]] - ref).max())
+
+    try:
+        from threadpoolctl import threadpool_limits
+        limit = threadpool_limits(1)
+    except ImportError:
+        import contextlib
+        limit = contextlib.nullcontext()
+    with ThreadPoolExecutor(threads) as ex:
+        list(ex.map(build, seqs))
+    t0 = time.perf_counter()
+    for b in seqs:
+        nl, hi = int(kv_cu[b + 1] - wl.q_lens[b]), int(kv_cu[b + 1])
+        oracle.scatter_kv(k_all[nl:hi].astype(np.float64), v_all[nl:hi].astype(np.float64),
+                          wl.kv_slots[nl:hi], caches[b][0], caches[b][1], wl.block_size)
+    t_scatter = time.perf_counter() - t0
+    order = sorted(seqs, key=lambda b: -int(wl.q_lens[b]) * int(wl.seqlens_kv[b])
+                   - int(wl.seqlens_kv[b]))
+    t0 = time.perf_counter()
+    with limit, ThreadPoolExecutor(threads) as ex:
+        errs = list(ex.map(attend, order))
+    t_att = time.perf_counter() - t0
+    return {"attention_s": t_att, "attention_threads": threads, "scatter_s": t_scatter,
+            "scatter_threads": 1, "max_abs_err": max(errs) if errs else 0.0}
+
+
+def per_config(steps, warmup, torch, pa, W):
+    """Every configuration apart from the headline one: GPU step latency
+    (pa_scatter_kv of the step's new tokens + pa_attention, back to back
+    after warm-up) and tokens/s, and the fp64 oracle on the host cores
+    (attention and scatter timed apart) with the max abs error of the GPU
+    output of the timed run against it.  The small configuration is the
+    84-case matrix: latency over the cases, the worst error."""
+    threads = min(16, len(os.sched_getaffinity(0)))
+    res = {}
+    for name, idx in (("tiny", 1), ("decode", 3), ("prefill", 4)):
+        wl = W.by_index(idx)
+        ms, _, pk, more = time_workload(wl, steps, warmup, torch, pa, W, keep=True)
+        r = {"workload": wl.name, "dtype": wl.dtype, "step_us": ms * 1e3,
+             "attention_us": pk.get("attention", 0.0) * 1e3,
+             "tokens_per_s": wl.num_tokens / (ms * 1e-3)}
+        r["oracle"] = oracle_check(wl, more["vals"], more["out"], threads)
+        r["oracle"]["tolerance"] = TOL[wl.dtype]
+        res[name] = r
+        del more
+        torch.cuda.empty_cache()
+    lat, toks, worst, o_att, o_sc = [], 0, 0.0, 0.0, 0.0
+    for n, (qs, ls, hq, hk) in enumerate(W.small_cases()):
+        wl = W.small(qs, ls, hq, hk, seed=2000 + n)
+        ms, _, pk, more = time_workload(wl, steps, warmup, torch, pa, W, keep=True)
+        lat.append(ms * 1e3)
+        toks += wl.num_tokens
+        o = oracle_check(wl, more["vals"], more["out"], 1)
+        worst = max(worst, o["max_abs_err"])
+        o_att += o["attention_s"]
+        o_sc += o["scatter_s"]
+    res["small"] = {"workload": f"small matrix: {len(lat)} cases (q_len {{1,4,16}}, total "
+                                f"{{32,64}}, MHA 8/8 and GQA 8/2, D 64, bs 256, fp16)",
+                    "dtype": "f16", "step_us_median": float(np.median(lat)),
+                    "step_us_min": float(min(lat)), "step_us_max": float(max(lat)),
+                    "tokens_per_s": toks / (sum(lat) * 1e-6),
+                    "oracle": {"attention_s": o_att, "attention_threads": 1,
+                               "scatter_s": o_sc, "scatter_threads": 1, "max_abs_err": worst,
+                               "tolerance": TOL["f16"], "note": "summed over the 84 cases"}}
+    return res
+
+
 # ------------------------------------------------------------- main
 def main():
     ap = argparse.ArgumentParser()
@@ -531,6 +647,8 @@ def main():
         "rotary_scatter": more.get("rotary_scatter"),
         "extra": extra,
     }
+    if not args.no_extra and args.workload == "mixed" and not opts:
+        line["per_config"] = per_config(max(5, args.steps // 2), 3, torch, pa, W)
     if opts.get("local_window_size"):
         line["note"] = ("algorithmic bytes and flops count the plain causal work; the window "
                         "reads and computes less, so the rates above overstate it")
