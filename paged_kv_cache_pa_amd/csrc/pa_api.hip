@@ -12,6 +12,7 @@
 #include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <algorithm>
@@ -97,8 +98,52 @@ int device_cus() {
   return cached[dev];
 }
 
+// Test-only overrides, read once per process from the environment and not
+// part of the ABI: PA_TEST_SPLIT_KEYS (256, 512, 1024 or 2048: the decode
+// split length) and PA_TEST_PATH=prefill (every sequence takes the prefill
+// path, including those whose q_len * G fits one decode tile).  Tests vary
+// them to demand the same results under other tile and split parameters.
+struct TestOverrides {
+  int split_keys = pa::kSplitKeys;
+  bool force_prefill = false;
+  bool valid = true;
+  char msg[160] = "";
+};
+const TestOverrides& test_overrides() {
+  static TestOverrides o;
+  static std::once_flag once;
+  std::call_once(once, [] {
+    if (const char* v = getenv("PA_TEST_SPLIT_KEYS")) {
+      const int k = atoi(v);
+      if (k == 256 || k == 512 || k == 1024 || k == 2048) {
+        o.split_keys = k;
+      } else {
+        o.valid = false;
+        snprintf(o.msg, sizeof(o.msg), "PA_TEST_SPLIT_KEYS=%s (test override): 256, 512, 1024 or 2048", v);
+      }
+    }
+    if (const char* v = getenv("PA_TEST_PATH")) {
+      if (strcmp(v, "prefill") == 0) {
+        o.force_prefill = true;
+      } else if (strcmp(v, "auto") != 0) {
+        o.valid = false;
+        snprintf(o.msg, sizeof(o.msg), "PA_TEST_PATH=%s (test override): prefill or auto", v);
+      }
+    }
+  });
+  return o;
+}
+
+pa::Shape make_shape(int32_t num_seqs, int64_t num_tokens, int32_t max_blocks_per_seq,
+                     int32_t num_heads, int32_t num_kv_heads, int32_t head_size,
+                     int32_t block_size) {
+  return pa::Shape{num_seqs, num_tokens, max_blocks_per_seq, num_heads, num_kv_heads, head_size,
+                   block_size, test_overrides().split_keys};
+}
+
 // Host-side shape checks shared by pa_attention and the workspace query.
 pa_status_t check_shape(const pa::Shape& s) {
+  if (!test_overrides().valid) return fail(PA_ERR_INVALID_ARGUMENT, "%s", test_overrides().msg);
   if (s.num_seqs < 1 || s.num_seqs > 65536)
     return fail(PA_ERR_INVALID_ARGUMENT, "num_seqs=%d outside [1, 65536]", s.num_seqs);
   if (s.num_tokens < 0 || s.num_tokens > INT32_MAX)
@@ -119,9 +164,12 @@ pa_status_t check_shape(const pa::Shape& s) {
   if (!is_pow2(s.block_size) || s.block_size < 16 || s.block_size > 1024)
     return fail(PA_ERR_NOT_IMPLEMENTED, "block_size=%d (supported: powers of two in [16, 1024])",
                 s.block_size);
-  if ((int64_t)s.max_blocks_per_seq * s.block_size > (int64_t)pa::kSplitKeys * pa::kMaxSplitsCombine)
+  if ((int64_t)s.max_blocks_per_seq * s.block_size > (int64_t)s.split_keys * pa::kMaxSplitsCombine)
     return fail(PA_ERR_NOT_IMPLEMENTED, "max_blocks_per_seq * block_size exceeds %d tokens",
-                pa::kSplitKeys * pa::kMaxSplitsCombine);
+                s.split_keys * pa::kMaxSplitsCombine);
+  if (s.split_keys > 64 * s.block_size)   // a decode split's block ids fill one register
+    return fail(PA_ERR_NOT_IMPLEMENTED, "split length %d exceeds 64 blocks of %d", s.split_keys,
+                s.block_size);
   // The kernels' 32-bit quantities: a prefill lane's byte offset inside a
   // cache block, and the work-item, queue and partial-row counts the plan
   // writes and the fetch counters run past by at most one per wave.
@@ -160,7 +208,7 @@ Layout workspace_layout(const Shape& s) {
   Layout L{};
   const int G = s.num_heads / s.num_kv_heads;
   const int64_t max_kv = (int64_t)s.max_blocks_per_seq * s.block_size;
-  const int64_t max_splits = (max_kv + kSplitKeys - 1) / kSplitKeys;
+  const int64_t max_splits = (max_kv + s.split_keys - 1) / s.split_keys;
   const int tq = prefill_tokens_per_tile(G);
   L.max_dec_pairs = (int64_t)s.num_seqs * max_splits;
   const int64_t cols = std::min<int64_t>((int64_t)kDecodeCols * s.num_seqs, (int64_t)G * s.num_tokens);
@@ -388,8 +436,8 @@ pa_status_t pa_seqlens_from_past(const int32_t* cu_seqlens_q, const int32_t* pas
 size_t pa_attention_workspace_size(int32_t num_seqs, int64_t num_tokens, int32_t max_blocks_per_seq,
                                    int32_t num_heads, int32_t num_kv_heads, int32_t head_size,
                                    int32_t block_size) {
-  pa::Shape s{num_seqs, num_tokens, max_blocks_per_seq, num_heads, num_kv_heads, head_size,
-              block_size};
+  const pa::Shape s = make_shape(num_seqs, num_tokens, max_blocks_per_seq, num_heads,
+                                 num_kv_heads, head_size, block_size);
   if (check_shape(s) != PA_OK) return 0;
   return pa::workspace_layout(s).total;
 }
@@ -408,8 +456,8 @@ static pa_status_t attention_impl(const void* q, const int32_t* cu_seqlens_q,
                                   void* stream, bool kv8) {
   if (dtype != PA_F16 && dtype != PA_BF16)
     return fail(PA_ERR_NOT_IMPLEMENTED, "dtype=%d (supported: PA_F16, PA_BF16)", dtype);
-  const pa::Shape s{num_seqs, num_tokens, max_blocks_per_seq, num_heads, num_kv_heads, head_size,
-                    block_size};
+  const pa::Shape s = make_shape(num_seqs, num_tokens, max_blocks_per_seq, num_heads,
+                                 num_kv_heads, head_size, block_size);
   pa_status_t cs = check_shape(s);
   if (cs != PA_OK) return cs;
   if (num_blocks < 1) return fail(PA_ERR_INVALID_ARGUMENT, "num_blocks < 1");
@@ -456,6 +504,9 @@ static pa_status_t attention_impl(const void* q, const int32_t* cu_seqlens_q,
   pl.tokens_per_tile = tq;
   pl.decode_only = kv8 ? 1 : 0;
   pl.window = local_window_size > 0 ? local_window_size : 0;
+  pl.split_keys = s.split_keys;
+  pl.split_shift = log2i(s.split_keys);
+  pl.force_prefill = test_overrides().force_prefill && !kv8 ? 1 : 0;
   // Persistent grid: what the device holds at once, but no more groups than
   // there are prefill items plus groups of 8 decode waves.
   const int64_t max_groups =
@@ -494,6 +545,9 @@ static pa_status_t attention_impl(const void* q, const int32_t* cu_seqlens_q,
   a.cap_k = (float)cap_k;
   a.cap_b = softcap > 0.f ? softcap * pa::kLog2e : 0.f;
   a.window = pl.window;
+  a.split_keys = pl.split_keys;
+  a.split_shift = pl.split_shift;
+  a.force_prefill = pl.force_prefill;
 
   e = timed(2, st, [&] { return pa::launch_attention(a, dtype, head_size, workers, st, kv8); });
   if (e != hipSuccess) return hip_fail(e, "attention launch");
@@ -565,8 +619,8 @@ pa_status_t pa_attention_noalloc(const void* q, const int32_t* cu_seqlens_q,
     return fail(PA_ERR_NOT_IMPLEMENTED, "dtype=%d (supported: PA_F16, PA_BF16)", dtype);
   // Sizes first, on the host, before any HIP call: the scratch must hold the
   // workspace pa_attention would need for these sizes.
-  const pa::Shape s{num_seqs, num_tokens, max_blocks_per_seq, num_heads, num_kv_heads, head_size,
-                    block_size};
+  const pa::Shape s = make_shape(num_seqs, num_tokens, max_blocks_per_seq, num_heads,
+                                 num_kv_heads, head_size, block_size);
   pa_status_t cs = check_shape(s);
   if (cs != PA_OK) return cs;
   const size_t need = pa::workspace_layout(s).total;

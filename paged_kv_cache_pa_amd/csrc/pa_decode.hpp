@@ -12,7 +12,7 @@
 //
 // Work item = (sequence b, split s, KV head kh), one wavefront each, fetched
 // from a device counter.  The wave walks 16-key chunks of keys
-// [s*S, min(L, (s+1)*S)), S = kSplitKeys, through the block table (the split's block ids
+// [s*S, min(L, (s+1)*S)), S = the split length, through the block table (the split's block ids
 // are prefetched into one VGPR and broadcast per chunk with readlane).  The
 // G query heads of kh (times q_len tokens) are the 16 columns n = i*G + g of
 // the score tile, so every K/V byte is read from HBM exactly once per call.
@@ -94,10 +94,10 @@ __device__ __forceinline__ void decode_items(const AttnArgs& a) {
     const int L = si.kv_len, ql = si.q_len;
     const int past = L - ql;
     const int ncols = ql * G;
-    const int nsplit = (L + kSplitKeys - 1) / kSplitKeys;
-    const int live = nsplit - (WIN ? first_live_split(L, ql, a.window) : 0);   // splits with items
-    const int k0 = split * kSplitKeys;
-    const int k1 = min(L, k0 + kSplitKeys);
+    const int nsplit = (L + a.split_keys - 1) >> a.split_shift;
+    const int live = nsplit - (WIN ? first_live_split(L, ql, a.window, a.split_shift) : 0);   // splits with items
+    const int k0 = split << a.split_shift;
+    const int k1 = min(L, k0 + a.split_keys);
 
     // Q^T operand: column n = r16 -> (token n / G, head kh*G + n % G).
     u32x4_t qreg[NS];
@@ -391,9 +391,9 @@ __global__ __launch_bounds__(256) void combine_kernel(AttnArgs a) {
   const SeqInfo si = a.seqinfo[b];
   const int G = a.group;
   const int ncols = si.q_len * G;
-  if (si.q_len <= 0 || ncols > kDecodeCols) return;
-  const int nsplit = (si.kv_len + kSplitKeys - 1) / kSplitKeys;
-  const int s0 = first_live_split(si.kv_len, si.q_len, a.window);   // splits s0 .. nsplit-1
+  if (si.q_len <= 0 || ncols > kDecodeCols || a.force_prefill) return;
+  const int nsplit = (si.kv_len + a.split_keys - 1) >> a.split_shift;
+  const int s0 = first_live_split(si.kv_len, si.q_len, a.window, a.split_shift);   // splits s0 .. nsplit-1
   if (nsplit - s0 <= 1) return;
   const int64_t row0 = (int64_t)si.pbase + (int64_t)kh * nsplit * ncols;
   // Column n's weights: one 16-lane group of a wave per column.

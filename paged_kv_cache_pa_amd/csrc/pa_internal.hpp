@@ -9,11 +9,13 @@
 
 namespace pa {
 
-// Split-KV length of the decode path (keys per work item).  It depends on
-// nothing but this constant, so a sequence's output never depends on its
-// batch-mates.  1024 measured faster than 512 on the large mixed batch
+// Split-KV length of the decode path (keys per work item).  A sequence's
+// split depends on nothing but this length, so its output never depends on
+// its batch-mates.  1024 measured faster than 512 on the large mixed batch
 // (half the split partials to write and combine) and the same on pure
-// decode; 256 was 7 % slower (per-item start-up).
+// decode; 256 was 7 % slower (per-item start-up).  The kernels take the
+// length as an argument (a power of two, at most 64 blocks: one lane per
+// block id), so a test-only host override can vary it.
 constexpr int kSplitKeys = 1024;
 // Largest split count per sequence (the block table row bounds the context:
 // max_blocks_per_seq * block_size <= kSplitKeys * kMaxSplitsCombine).
@@ -77,6 +79,7 @@ struct Shape {
   int64_t num_tokens;
   int32_t max_blocks_per_seq;
   int32_t num_heads, num_kv_heads, head_size, block_size;
+  int32_t split_keys;   // decode split length (kSplitKeys unless overridden for tests)
 };
 
 // Tokens per prefill tile for a GQA group size.
@@ -96,6 +99,8 @@ struct PlanArgs {
   int32_t decode_only;  // fp8 caches: only the decode path; a sequence with
                         // more than kDecodeCols columns gets no work items
   int32_t window;       // local_window_size (0: off)
+  int32_t split_keys, split_shift;   // decode split length and its log2
+  int32_t force_prefill;             // every sequence takes the prefill path (test override)
 };
 
 struct AttnArgs {
@@ -122,14 +127,17 @@ struct AttnArgs {
   // s, with cap_k = 2 (scale / c) log2(e) and cap_b = c log2(e); cap_b = 0: off.
   float cap_k, cap_b;
   int32_t window;    // local_window_size W: row sees keys (limit - W, limit]; 0: off
+  int32_t split_keys, split_shift;   // decode split length and its log2
+  int32_t force_prefill;             // no sequence took the decode path (test override)
 };
 
 // First decode split of a sequence with a sliding window: splits wholly
 // below the window start of its first new row hold no visible key.
-__host__ __device__ inline int first_live_split(int kv_len, int q_len, int window) {
+__host__ __device__ inline int first_live_split(int kv_len, int q_len, int window,
+                                                int split_shift) {
   if (window <= 0) return 0;
   const int lo = kv_len - q_len - window + 1;   // first visible key of row 0
-  return lo > 0 ? lo / kSplitKeys : 0;
+  return lo > 0 ? lo >> split_shift : 0;
 }
 
 hipError_t launch_scatter(const void* k_new, const void* v_new, const int32_t* slots, void* kc,

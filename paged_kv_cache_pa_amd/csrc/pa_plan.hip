@@ -9,7 +9,7 @@
 //
 // Per sequence b: q_len = cu[b+1] - cu[b], L = seqlens_kv[b].  A sequence
 // whose q_len * G columns fit one 16-wide tile takes the decode path and is
-// split into ceil(L / kSplitKeys) key ranges; every other non-empty sequence
+// split into ceil(L / split_keys) key ranges; every other non-empty sequence
 // takes the prefill path in tiles of tokens_per_tile tokens per KV head.
 // Prefill (sequence, KV head) pairs are dealt to 8 queues, one per XCD, so
 // all tiles that reuse one K/V stream share an L2; inside a queue the
@@ -78,9 +78,9 @@ __device__ inline SeqCounts seq_counts(const PlanArgs& a, int b) {
   if (c.q_len <= 0) return c;
   const int ncols = c.q_len * a.group;
   if (a.decode_only && ncols > kDecodeCols) return c;   // no work (precondition violated)
-  if (ncols <= kDecodeCols) {
-    c.nsplit = (c.L + kSplitKeys - 1) / kSplitKeys;
-    c.s0 = first_live_split(c.L, c.q_len, a.window);
+  if (ncols <= kDecodeCols && !a.force_prefill) {
+    c.nsplit = (c.L + a.split_keys - 1) >> a.split_shift;
+    c.s0 = first_live_split(c.L, c.q_len, a.window, a.split_shift);
     if (c.nsplit - c.s0 > 1) c.prows = a.num_kv_heads * c.nsplit * ncols;
   } else {
     c.ntiles = (c.q_len + a.tokens_per_tile - 1) / a.tokens_per_tile;
@@ -119,12 +119,12 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
       if (a.window > 0) keys = fminf(keys, (float)a.window + (float)a.tokens_per_tile);
       cost_p += (float)c.ntiles * a.num_kv_heads * (keys / kPrefillKeys + 0.5f);
     } else if (c.q_len > 0) {
-      cost_d += (float)(c.L - c.s0 * kSplitKeys) * a.num_kv_heads;
+      cost_d += (float)(c.L - (c.s0 << a.split_shift)) * a.num_kv_heads;
     }
-    // Decode pairs: every full kSplitKeys split first (pass 1), then the
+    // Decode pairs: every full split first (pass 1), then the
     // shorter last splits (pass 2), so the tail of the decode work is made
     // of short items.
-    const int has_part = (c.L % kSplitKeys) != 0 && c.nsplit > 0;
+    const int has_part = (c.L & (a.split_keys - 1)) != 0 && c.nsplit > 0;
     const int nfull = max(0, c.nsplit - has_part - c.s0);   // live full splits: s0 ..
     int v[3 + kQueues], tot[3 + kQueues];
     v[0] = nfull;
@@ -175,7 +175,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
   for (int base = 0; base < a.num_seqs; base += kPlanThreads) {
     const int b = base + tid;
     const SeqCounts c = seq_counts(a, b);
-    const int has_part = (c.L % kSplitKeys) != 0 && c.nsplit > 0;
+    const int has_part = (c.L & (a.split_keys - 1)) != 0 && c.nsplit > 0;
     int v[kQueues + 1], tot[kQueues + 1];
 #pragma unroll
     for (int x = 0; x < kQueues; ++x) v[x] = c.ntiles * heads_in_queue(b, a.num_kv_heads, x);
