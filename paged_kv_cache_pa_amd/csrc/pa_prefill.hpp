@@ -135,6 +135,30 @@ __device__ __forceinline__ void prefill_items(const AttnArgs& a) {
   auto kswz = [](int row) { return CPR == 16 ? (row & 15) : ((row >> 1) & 7); };
   auto kslot = [&](int row, int chunk) { return row * ROWB + ((chunk ^ kswz(row)) << 4); };
 
+  // Byte offsets of this wave's tile rows RPW*wave + p*RPI + ln/CPR inside
+  // their cache block, with the chunk swizzles applied: constants of the
+  // work-group, parked in this wave's own slice of the decode staging buffer
+  // (idle in the prefill phase; no other wave touches the slice, so no
+  // barrier) and read back with one LDS read per tile.  Tile t's copies add
+  // a wave-uniform part (block start, and for blocks of BN keys or more the
+  // tile's row offset in its block) to the scalar base, so they need no
+  // vector address arithmetic.  The last tile of an item, whose rows past
+  // the visible range are clamped, takes the general path.
+  static_assert(2 * LPW <= 4 && 16 * ROWB >= 2048, "copy offsets slot");
+  unsigned char* const offs_lds = decode_stage<T, D, CAP, WIN, 2>() + wave * (16 * ROWB) + 1024;
+  {
+    const int ln = lane_here();
+    uint32_t o[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int p = 0; p < LPW; ++p) {
+      const int row = RPW * wave + p * RPI + ln / CPR;
+      const int rib = bsz >= BN ? row : (row & (bsz - 1));
+      o[2 * p] = (uint32_t)((rib * (int)row_stride + ((ln % CPR) ^ kswz(row)) * 8) * 2);
+      o[2 * p + 1] = (uint32_t)((rib * (int)row_stride + ((ln % CPR) ^ swz(row)) * 8) * 2);
+    }
+    *reinterpret_cast<u32x4_t*>(offs_lds + ln * 16) = u32x4_t{o[0], o[1], o[2], o[3]};
+  }
+
   for (int qi = 0; qi < kQueues; ++qi) {
     const int x = (home + qi) % kQueues;
     // Uniform plan results: keep them in scalar registers.
@@ -190,6 +214,28 @@ __device__ __forceinline__ void prefill_items(const AttnArgs& a) {
         }
       };
 
+      // The copies of a tile that is not the item's last: lane offsets held
+      // (koff_l / voff_l), everything else wave-uniform.
+      auto issue_fast = [&](int t, int blk) {
+        const int64_t in_blk = bsz >= BN ? (int64_t)((t * BN) & (bsz - 1)) * row_stride : 0;
+        const int64_t bstart = (int64_t)blk * bsz * row_stride + (int64_t)kh * D + in_blk;
+        const uint16_t* kbase = kc + bstart;
+        const uint16_t* vbase = vc + bstart;
+        const uint32_t kdst = lds_addr + (uint32_t)((t % NB) * 2 * TB + RPW * wave * ROWB);
+        const u32x4_t o = *reinterpret_cast<const u32x4_t*>(offs_lds + lane_here() * 16);
+#pragma unroll
+        for (int p = 0; p < LPW; ++p) {
+          lds_dma16(kbase, o[2 * p], kdst + p * 1024);
+          lds_dma16(vbase, o[2 * p + 1], kdst + TB + p * 1024);
+        }
+      };
+      auto issue_tile = [&](int t, int blk) {
+        if (t + 1 < n)
+          issue_fast(t, blk);
+        else
+          issue(t, blk);
+      };
+
       // Per-lane indices taken per item (lane_here), so values derived from
       // them are not hoisted out of the item loop and held across it.
       const int lane = lane_here();
@@ -239,8 +285,8 @@ __device__ __forceinline__ void prefill_items(const AttnArgs& a) {
       u32x4_t pb[NR][NK / 2];  // rounded P of the tile between its V and next M phases
 
       // Prologue: tiles t_lo and t_lo+1 resident, block id of the next fetched.
-      issue(t_lo, block_of(t_lo));
-      if (nrel > 1) issue(t_lo + 1, block_of(t_lo + 1));
+      issue_tile(t_lo, block_of(t_lo));
+      if (nrel > 1) issue_tile(t_lo + 1, block_of(t_lo + 1));
       int blk_next = nrel > 2 ? block_of(t_lo + 2) : 0;
       wait_vmcnt<0>();
       // The wait above is opaque to the compiler, which would otherwise
@@ -453,7 +499,7 @@ __device__ __forceinline__ void prefill_items(const AttnArgs& a) {
       // once can stall the issuing waves until the address unit drains them,
       // which must not happen in a matrix-core phase.
       auto even_service = [&](int i) {
-        if (i + 2 < nrel) issue(t_lo + i + 2, blk_next);
+        if (i + 2 < nrel) issue_tile(t_lo + i + 2, blk_next);
       };
       // Block id of tile i+3 (a scalar load, first used at tick 2i+2), read
       // at the start of the wave's softmax phase: that phase has no LDS reads
