@@ -94,17 +94,50 @@ __device__ inline int heads_in_queue(int b, int hk, int x) {
   return r < hk ? (hk - 1 - r) / 8 + 1 : 0;
 }
 
+// The second-pass writes of sequence b (lane-owned values, the whole wave
+// cooperating): its partial last decode split, placed after all full splits,
+// and its prefill items, heaviest tile of each (sequence, KV head) first.
+// part_at: slot of b's partial split; qpos[x]: first slot of b's items in
+// queue x (queue start + items of earlier sequences).
+__device__ inline void emit_second_pass(const PlanArgs& a, int b, const SeqCounts& c, bool has_part,
+                                        int part_at, const int (&qpos)[kQueues]) {
+  if (has_part) a.dec_items[part_at] = make_int2(b, c.nsplit - 1);
+  // A prefill sequence's Hk x ntiles items are written by its whole wave
+  // (the owning lane's values broadcast): one lane storing them in turn
+  // held the plan at ~25 us on a few long prefill chunks.
+  unsigned long long todo = __ballot(c.ntiles > 0);
+  while (todo) {
+    const int src = __builtin_ctzll(todo);
+    todo &= todo - 1;
+    const int bb = __shfl(b, src), nt = __shfl(c.ntiles, src);
+    int vx[kQueues];
+#pragma unroll
+    for (int x = 0; x < kQueues; ++x) vx[x] = __shfl(qpos[x], src);
+    for (int i = threadIdx.x & 63; i < a.num_kv_heads * nt; i += 64) {
+      const int kh = i / nt, r = i - kh * nt;
+      const int x = (int)(((int64_t)bb * a.num_kv_heads + kh) & 7);
+      int pos = 0;   // first item of (bb, kh) in queue x
+#pragma unroll
+      for (int q = 0; q < kQueues; ++q)
+        if (q == x) pos = vx[q] + (kh >> 3) * nt;
+      a.pf_items[pos + r] = make_int4(bb, kh, nt - 1 - r, 0);
+    }
+  }
+}
+
 }  // namespace
 
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
   __shared__ int lds[(kPlanWaves + 1) * 12];
   __shared__ int qstart[kQueues];
   __shared__ int nfull_total;
-  __shared__ float cost_sh[2];
+  __shared__ float cost_sh[kPlanWaves][2];
   const int tid = threadIdx.x;
   if (tid <= kQueues) a.counters[kLine * tid] = 0;   // fetch counters: decode, then queues 0..7
-  if (tid < 2) cost_sh[tid] = 0.f;
-  __syncthreads();
+  // A batch that one sweep of the work-group covers takes both passes in
+  // that sweep: the first pass's scan already gives every total the second
+  // pass places its items by.
+  const bool one_sweep = a.num_seqs <= kPlanThreads;
 
   // Pass 1: sequence info, decode pairs, partial-row bases, queue sizes,
   // estimated prefill and decode costs.
@@ -138,6 +171,15 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
       const int off = carry[0] + v[0];
       for (int s = 0; s < nfull; ++s) a.dec_items[off + s] = make_int2(b, c.s0 + s);
     }
+    if (one_sweep) {
+      int qpos[kQueues], run = 0;
+#pragma unroll
+      for (int x = 0; x < kQueues; ++x) {
+        qpos[x] = run + v[3 + x];
+        run += tot[3 + x];
+      }
+      emit_second_pass(a, b, c, has_part, tot[0] + v[2], qpos);
+    }
 #pragma unroll
     for (int k = 0; k < 3 + kQueues; ++k) carry[k] += tot[k];
   }
@@ -147,12 +189,17 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
     cost_d += __shfl_xor(cost_d, o);
   }
   if ((tid & 63) == 0) {
-    atomicAdd(&cost_sh[0], cost_p);
-    atomicAdd(&cost_sh[1], cost_d);
+    cost_sh[tid >> 6][0] = cost_p;
+    cost_sh[tid >> 6][1] = cost_d;
   }
   __syncthreads();
   if (tid == 0) {
-    const float wp = cost_sh[0] * kPrefillStepCost, wd = cost_sh[1];
+    float sp = 0.f, sd = 0.f;
+    for (int w = 0; w < kPlanWaves; ++w) {
+      sp += cost_sh[w][0];
+      sd += cost_sh[w][1];
+    }
+    const float wp = sp * kPrefillStepCost, wd = sd;
     int first = a.num_workers;
     if (wd > 0.f) first = (int)(a.num_workers * (wp / (wp + wd)) + 0.5f);
     if (wp > 0.f && first < 1) first = 1;
@@ -167,10 +214,11 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
       run += carry[3 + x];
     }
   }
+  if (one_sweep) return;
   __syncthreads();
 
-  // Pass 2: the partial last decode splits after all full ones; prefill
-  // items, heaviest tile of each (sequence, head) first.
+  // Pass 2 (batches of more than one sweep): the partial last decode splits
+  // after all full ones; prefill items.
   int qcarry[kQueues + 1] = {0};
   for (int base = 0; base < a.num_seqs; base += kPlanThreads) {
     const int b = base + tid;
@@ -181,28 +229,10 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
     for (int x = 0; x < kQueues; ++x) v[x] = c.ntiles * heads_in_queue(b, a.num_kv_heads, x);
     v[kQueues] = has_part;
     block_scan<kQueues + 1>(v, tot, lds);
-    if (has_part) a.dec_items[nfull_total + qcarry[kQueues] + v[kQueues]] = make_int2(b, c.nsplit - 1);
-    // A prefill sequence's Hk x ntiles items are written by its whole wave
-    // (the owning lane's values broadcast): one lane storing them in turn
-    // held the plan at ~25 us on a few long prefill chunks.
-    unsigned long long todo = __ballot(c.ntiles > 0);
-    while (todo) {
-      const int src = __builtin_ctzll(todo);
-      todo &= todo - 1;
-      const int bb = __shfl(b, src), nt = __shfl(c.ntiles, src);
-      int vx[kQueues];
+    int qpos[kQueues];
 #pragma unroll
-      for (int x = 0; x < kQueues; ++x) vx[x] = __shfl(v[x], src);
-      for (int i = tid & 63; i < a.num_kv_heads * nt; i += 64) {
-        const int kh = i / nt, r = i - kh * nt;
-        const int x = (int)(((int64_t)bb * a.num_kv_heads + kh) & 7);
-        int pos = 0;   // first item of (bb, kh) in queue x
-#pragma unroll
-        for (int q = 0; q < kQueues; ++q)
-          if (q == x) pos = qstart[q] + qcarry[q] + vx[q] + (kh >> 3) * nt;
-        a.pf_items[pos + r] = make_int4(bb, kh, nt - 1 - r, 0);
-      }
-    }
+    for (int x = 0; x < kQueues; ++x) qpos[x] = qstart[x] + qcarry[x] + v[x];
+    emit_second_pass(a, b, c, has_part, nfull_total + qcarry[kQueues] + v[kQueues], qpos);
 #pragma unroll
     for (int x = 0; x <= kQueues; ++x) qcarry[x] += tot[x];
   }
