@@ -38,7 +38,10 @@
  * - Cache layout (both caches): [num_blocks, block_size, num_kv_heads,
  *   head_size], row-major; cache slot s = block * block_size + offset holds
  *   one token's num_kv_heads * head_size row.
- * - Index arrays are int32.  All address arithmetic is 64-bit.
+ * - Index arrays are int32.  Offsets into q, out, the caches and the
+ *   workspace are computed in 64 bits; offsets inside one cache block and
+ *   the work-item counts are 32-bit, which the size limits of each entry
+ *   point keep in range.
  * - Errors: argument checks happen on the host before any HIP call and
  *   return PA_ERR_INVALID_ARGUMENT / PA_ERR_NOT_IMPLEMENTED /
  *   PA_ERR_WORKSPACE_TOO_SMALL; a failed kernel launch returns PA_ERR_HIP.

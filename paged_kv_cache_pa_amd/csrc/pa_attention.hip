@@ -103,9 +103,9 @@ template <typename T>
 static hipError_t combine_dispatch(const AttnArgs& a, int head_size, hipStream_t st) {
   dim3 grid(a.num_seqs, a.num_kv_heads);
   if (head_size == 128)
-    hipLaunchKernelGGL((combine_kernel<T, 128>), grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((combine_kernel<T, 128>), grid, dim3(kCombineThreads), 0, st, a);
   else
-    hipLaunchKernelGGL((combine_kernel<T, 64>), grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((combine_kernel<T, 64>), grid, dim3(kCombineThreads), 0, st, a);
   return hipGetLastError();
 }
 

@@ -377,14 +377,20 @@ __device__ __forceinline__ void decode_items(const AttnArgs& a) {
 }
 
 // One work-group per (sequence, KV head); a no-op unless the sequence took
-// the decode path with more than one split.  The per-split weights
-// w_s = 2^(m_s - M) of each column are computed once into LDS together with
-// 1 / sum_s w_s l_s; then each thread produces 4 consecutive outputs of one
-// column from 16-byte partial loads, with the splits unrolled so several
-// loads are in flight.
+// the decode path with more than one split.  Per column: M = max_s m_s,
+// w_s = 2^(m_s - M), and the output is sum_s w_s acc_s / sum_s w_s l_s.
+// The kernel's time is its chain of dependent memory round trips, so each
+// column's (m, l) pairs are loaded once, held in registers while the max is
+// taken, and the partials follow eight splits per round trip.  All
+// work-groups of a large batch fit on the chip at once only while the kernel
+// stays near 64 registers, so nothing more is held.
+constexpr int kCombineThreads = 256;
+
 template <typename T, int D>
-__global__ __launch_bounds__(256) void combine_kernel(AttnArgs a) {
+__global__ __launch_bounds__(kCombineThreads) void combine_kernel(AttnArgs a) {
   constexpr int MAXS = kMaxSplitsCombine;
+  constexpr int MLR = 2;     // (m, l) pairs per weight lane held in registers
+  constexpr int DEPTH = 8;   // partial loads in flight per thread
   __shared__ float wts[kDecodeCols][MAXS];
   __shared__ float inv_den[kDecodeCols];
   const int b = blockIdx.x, kh = blockIdx.y;
@@ -396,45 +402,62 @@ __global__ __launch_bounds__(256) void combine_kernel(AttnArgs a) {
   const int s0 = first_live_split(si.kv_len, si.q_len, a.window, a.split_shift);   // splits s0 .. nsplit-1
   if (nsplit - s0 <= 1) return;
   const int64_t row0 = (int64_t)si.pbase + (int64_t)kh * nsplit * ncols;
-  // Column n's weights: one 16-lane group of a wave per column.
-  for (int n = threadIdx.x >> 4; n < ncols; n += blockDim.x >> 4) {
-    const int lane16 = threadIdx.x & 15;
+  const int tid = threadIdx.x;
+
+  // Column c's weights: the 16 lanes of one group; split s0 + lane16 + 16j
+  // in register j, further splits (past 16 * MLR) loaded again.
+  const int c = tid >> 4, lane16 = tid & 15;
+  if (c < ncols) {
+    auto ml_at = [&](int s) { return a.part_ml[row0 + (int64_t)s * ncols + c]; };
+    float2 ml[MLR];
+#pragma unroll
+    for (int j = 0; j < MLR; ++j) {
+      const int s = s0 + lane16 + 16 * j;
+      ml[j] = s < nsplit ? ml_at(s) : make_float2(-INFINITY, 0.f);
+    }
     float M = -INFINITY;
-    for (int s = s0 + lane16; s < nsplit; s += 16)
-      M = fmaxf(M, a.part_ml[row0 + (int64_t)s * ncols + n].x);
+    for (int s = s0 + lane16 + 16 * MLR; s < nsplit; s += 16) M = fmaxf(M, ml_at(s).x);
+#pragma unroll
+    for (int j = 0; j < MLR; ++j) M = fmaxf(M, ml[j].x);
 #pragma unroll
     for (int o = 8; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 16));
     float den = 0.f;
-    for (int s = s0 + lane16; s < nsplit; s += 16) {
-      const float2 ml = a.part_ml[row0 + (int64_t)s * ncols + n];
-      const float w = ml.x == -INFINITY ? 0.f : exp2_fast(ml.x - M);
-      if (s < MAXS) wts[n][s] = w;
-      den += w * ml.y;
+    auto weigh = [&](int s, float2 v) {
+      const float w = v.x == -INFINITY ? 0.f : exp2_fast(v.x - M);
+      wts[c][s] = w;
+      den += w * v.y;
+    };
+#pragma unroll
+    for (int j = 0; j < MLR; ++j) {
+      const int s = s0 + lane16 + 16 * j;
+      if (s < nsplit) weigh(s, ml[j]);
     }
+    for (int s = s0 + lane16 + 16 * MLR; s < nsplit; s += 16) weigh(s, ml_at(s));
 #pragma unroll
     for (int o = 8; o >= 1; o >>= 1) den += __shfl_xor(den, o, 16);
-    if (lane16 == 0) inv_den[n] = 1.f / den;
+    if (lane16 == 0) inv_den[c] = 1.f / den;
   }
   __syncthreads();
+
+  // Each thread: 4 consecutive outputs of one column from 16-byte partial
+  // loads, splits summed in order.
   uint16_t* __restrict__ op = (uint16_t*)a.out;
-  for (int idx = threadIdx.x; idx < ncols * (D / 4); idx += blockDim.x) {
-    const int n = idx / (D / 4);
-    const int d = (idx - n * (D / 4)) * 4;
+  const int64_t step = (int64_t)ncols * D;     // floats between one column's splits
+  for (int idx = tid; idx < ncols * (D / 4); idx += kCombineThreads) {
+    const int n = idx / (D / 4), d = (idx - n * (D / 4)) * 4;
     const float* src = a.part_acc + (row0 + n) * D + d;
-    const int64_t step = (int64_t)ncols * D;
-    // Four splits per step, so four independent 16-byte loads are in flight
-    // (two left the kernel waiting through one round trip per pair).
-    float4_t acc[4] = {};
-    int s = s0;
-    for (; s + 3 < nsplit; s += 4) {
-      float4_t v[4];
+    float4_t acc = {0.f, 0.f, 0.f, 0.f};
+    for (int s = s0; s < nsplit; s += DEPTH) {
+      float4_t v[DEPTH];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) v[u] = *reinterpret_cast<const float4_t*>(src + (s + u) * step);
+      for (int u = 0; u < DEPTH; ++u)
+        v[u] = s + u < nsplit ? *reinterpret_cast<const float4_t*>(src + (s + u) * step)
+                              : float4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int u = 0; u < 4; ++u) acc[u] += wts[n][s + u] * v[u];
+      for (int u = 0; u < DEPTH; ++u)
+        if (s + u < nsplit) acc += wts[n][s + u] * v[u];
     }
-    for (; s < nsplit; ++s) acc[0] += wts[n][s] * *reinterpret_cast<const float4_t*>(src + s * step);
-    const float4_t o = ((acc[0] + acc[1]) + (acc[2] + acc[3])) * inv_den[n];
+    const float4_t o = acc * inv_den[n];
     const int tok = si.cu + n / G;
     const int h = kh * G + n % G;
     *reinterpret_cast<u32x2_t*>(op + ((int64_t)tok * a.num_heads + h) * D + d) =
