@@ -109,24 +109,38 @@ def step(wl, st, pa):
                     **st["opts"])
 
 
-SCRUB_BYTES = 512 << 20     # written between separately timed reps (larger than the 256 MB MALL)
+SCRUB_BYTES = 512 << 20     # swept between separately timed reps (larger than the 256 MB MALL)
 
 
-def per_rep_times(fn, reps, torch, scrub):
-    """Each rep timed on its own with HIP events, after writing `scrub`
+def scrub_caches(scrub, i, torch, write=False):
+    """Evict every cache level: read all of `scrub` (a reduction over it), or
+    with `write`, overwrite it.  A write scrub leaves a cache's worth of
+    dirty lines whose write-back the next timed rep pays for (26 us on the
+    pure-decode step), so the default sweep only reads."""
+    if write:
+        scrub.fill_(i & 255)
+        return None
+    return scrub.view(torch.int32).amax()
+
+
+def per_rep_times(fn, reps, torch, scrub, write_scrub=False):
+    """Each rep timed on its own with HIP events, after a sweep of `scrub`
     (outside the events) so that no cache level still holds the previous
     rep's data.  Median, min and p90 over the reps."""
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(reps)]
+    sink = []
     for i, (a, b) in enumerate(ev):
-        scrub.fill_(i & 255)
+        sink.append(scrub_caches(scrub, i, torch, write_scrub))
         a.record()
         fn()
         b.record()
     torch.cuda.synchronize()
     t = sorted(a.elapsed_time(b) for a, b in ev)
-    return {"reps": reps, "scrub_MiB": scrub.numel() >> 20, "median_ms": float(np.median(t)),
-            "min_ms": float(t[0]), "p90_ms": float(np.percentile(t, 90))}
+    return {"reps": reps, "scrub_MiB": scrub.numel() >> 20,
+            "scrub": "write" if write_scrub else "read",
+            "median_ms": float(np.median(t)), "min_ms": float(t[0]),
+            "p90_ms": float(np.percentile(t, 90))}
 
 
 def sub_batch(wl, st, sel, torch, pa):
@@ -190,8 +204,10 @@ def time_workload(wl, steps, warmup, torch, pa, W, extras=False, fp8=False, opts
         more["out"] = st["out"].clone()
         more["vals"] = st["vals"]
     if extras:
-        scrub = torch.empty(SCRUB_BYTES, dtype=torch.uint8, device="cuda")
+        scrub = torch.zeros(SCRUB_BYTES, dtype=torch.uint8, device="cuda")
         more["step_reps"] = per_rep_times(lambda: step(wl, st, pa), steps, torch, scrub)
+        more["step_reps_write_scrub"] = per_rep_times(lambda: step(wl, st, pa), steps, torch,
+                                                      scrub, write_scrub=True)
         if fp8:
             del scrub, st
             torch.cuda.empty_cache()
@@ -593,6 +609,7 @@ def main():
             extra[name] = summarize(w2, m2, k2)
             extra[name]["workload"] = w2.name
             extra[name]["step_reps"] = more2.get("step_reps")
+            extra[name]["step_reps_write_scrub"] = more2.get("step_reps_write_scrub")
         # The pure-decode workload again on fp8 (e4m3) caches with per-channel
         # scales (pa_scatter_kv_fp8 + pa_attention_fp8): half the cache bytes.
         w2 = W.by_index(WORKLOADS["decode"])
@@ -601,6 +618,7 @@ def main():
         e = summarize(w2, m2, k2, kv_es=1)
         e["workload"] = w2.name + ", fp8 e4m3 caches with per-channel scales"
         e["step_reps"] = more2.get("step_reps")
+        e["step_reps_write_scrub"] = more2.get("step_reps_write_scrub")
         a16 = extra["decode"]["kernel_ms"].get("attention", 0.0)
         a8 = e["kernel_ms"].get("attention", 0.0)
         e["attention_speedup_vs_16bit_cache"] = a16 / a8 if a8 > 0 else None
@@ -642,6 +660,7 @@ def main():
         "copy_GBps": copy_gbps,
         "roofline": roof,
         "step_reps": more.get("step_reps"),
+        "step_reps_write_scrub": more.get("step_reps_write_scrub"),
         "sub_batches": more.get("sub_batches"),
         "scatter": more.get("scatter"),
         "rotary_scatter": more.get("rotary_scatter"),
