@@ -425,6 +425,37 @@ def test_maximum_sequence_count():
     assert max_err(out[torch.from_numpy(toks).cuda()], ref) <= TOL["f16"]
 
 
+def test_plan_past_one_sweep():
+    """1100 sequences, more than one sweep of the plan's 1024-thread
+    work-group, so the plan places the partial last decode splits and the
+    prefill items in a second sweep: decodes over contexts of up to four
+    1024-key splits (most with a partial last split), 20-token prefill
+    chunks and empty sequences.  Every row against the oracle; and each half
+    of the batch (550 sequences, planned in one sweep) run alone over the
+    same cache gives bitwise its rows of the whole batch."""
+    rng = np.random.default_rng(23)
+    B = 1100
+    kind = rng.choice([0, 1, 1, 1, 2], size=B)            # empty, decode x3, prefill chunk
+    q_lens = np.where(kind == 0, 0, np.where(kind == 1, 1, 20)).astype(np.int32)
+    lens = np.where(kind == 1, rng.integers(1, 4096, size=B, endpoint=True),
+                    np.where(kind == 2, 20 + rng.integers(0, 300, size=B), 0)).astype(np.int64)
+    wl = W.custom(q_lens, lens, 8, 2, 64, 16, dtype="f16", seed=23)
+    _log(f"plan past one sweep: {B} sequences, {wl.num_tokens} tokens, "
+         f"{int(((lens + 1023) // 1024 > 1).sum())} multi-split decodes")
+    d = device_inputs(wl, backend="torch")
+    out = run_attention(wl, d)
+    assert max_err(out, oracle_full(wl, d)) <= TOL["f16"]
+    cu = wl.cu_seqlens_q
+    for b0, b1 in ((0, B // 2), (B // 2, B)):
+        sub_cu = torch.from_numpy((cu[b0:b1 + 1] - cu[b0]).astype(np.int32)).cuda()
+        q = d["q"][int(cu[b0]):int(cu[b1])].contiguous()
+        part = pa.pa_attention(q, sub_cu, d["lens"][b0:b1].contiguous(),
+                               d["table"][b0:b1].contiguous(), d["kc"], d["vc"], wl.scale,
+                               wl.num_heads, wl.num_kv_heads)
+        torch.cuda.synchronize()
+        assert torch.equal(part, out[int(cu[b0]):int(cu[b1])]), (b0, b1)
+
+
 def test_concurrent_calls_on_two_streams():
     """Two batches on two streams with their own workspaces, launches
     interleaved: each output is bitwise the one its batch gets alone."""
