@@ -167,8 +167,8 @@ pa_status_t check_shape(const pa::Shape& s) {
   if ((int64_t)s.max_blocks_per_seq * s.block_size > (int64_t)s.split_keys * pa::kMaxSplitsCombine)
     return fail(PA_ERR_NOT_IMPLEMENTED, "max_blocks_per_seq * block_size exceeds %d tokens",
                 s.split_keys * pa::kMaxSplitsCombine);
-  if (s.split_keys > 64 * s.block_size)   // a decode split's block ids fill one register
-    return fail(PA_ERR_NOT_IMPLEMENTED, "split length %d exceeds 64 blocks of %d", s.split_keys,
+  if (s.split_keys > 128 * s.block_size)   // a decode split's block ids fill two registers
+    return fail(PA_ERR_NOT_IMPLEMENTED, "split length %d exceeds 128 blocks of %d", s.split_keys,
                 s.block_size);
   // The kernels' 32-bit quantities: a prefill lane's byte offset inside a
   // cache block, and the work-item, queue and partial-row counts the plan

@@ -13,7 +13,7 @@
 // Work item = (sequence b, split s, KV head kh), one wavefront each, fetched
 // from a device counter.  The wave walks 16-key chunks of keys
 // [s*S, min(L, (s+1)*S)), S = the split length, through the block table (the split's block ids
-// are prefetched into one VGPR and broadcast per chunk with readlane).  The
+// are prefetched into two VGPRs and broadcast per chunk with readlane).  The
 // G query heads of kh (times q_len tokens) are the 16 columns n = i*G + g of
 // the score tile, so every K/V byte is read from HBM exactly once per call.
 //
@@ -137,11 +137,13 @@ __device__ __forceinline__ void decode_items(const AttnArgs& a) {
     const int col_limit = past + div_small(r16, a.inv_group);
     const int col_low = col_limit - (WIN ? a.window : 0);
 
-    // Block ids of this split, one per lane.
+    // Block ids of this split: block i in lane i % 64 of register i / 64
+    // (a split spans at most 128 blocks).
     const int blk0 = k0 >> a.block_shift;
     const int nblk = ((k1 - 1) >> a.block_shift) - blk0 + 1;
     const int32_t* trow = a.block_table + (int64_t)b * a.max_blocks_per_seq + blk0;
     const int my_blk = lane < nblk ? trow[lane] : 0;
+    const int my_blk2 = lane + 64 < nblk ? trow[lane + 64] : 0;
 
     float m = -INFINITY, l = 0.f;
     float4_t acc[NT];
@@ -175,7 +177,9 @@ __device__ __forceinline__ void decode_items(const AttnArgs& a) {
       uint32_t v[4][VW];
     };
     auto load = [&](int c0, Chunk& ch) {
-      const int blk = __builtin_amdgcn_readlane(my_blk, (c0 >> a.block_shift) - blk0);
+      const int bi = (c0 >> a.block_shift) - blk0;   // uniform
+      const int blk = bi < 64 ? __builtin_amdgcn_readlane(my_blk, bi)
+                              : __builtin_amdgcn_readlane(my_blk2, bi - 64);
       const int64_t base =
           ((int64_t)blk * a.block_size + (c0 & (a.block_size - 1))) * row_stride + (int64_t)kh * D;
       // Load j: rows j * KRPI .. + KRPI - 1, chunk lane % KCPR of row

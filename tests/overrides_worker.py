@@ -41,7 +41,7 @@ def one_sequence(wl, d, b, **opts):
 def main():
     S = int(os.environ.get("PA_TEST_SPLIT_KEYS", "1024"))
     path = os.environ.get("PA_TEST_PATH", "auto")
-    bs_list = [16, 32] if S <= 1024 else [32, 64]    # a split spans at most 64 blocks
+    bs_list = [16, 32]    # a 2048-key split spans 128 blocks of 16, the most a split may
     cases = []
     for bs in bs_list:
         # Decode columns around split boundaries (q_len 1 and 2, G 8: 8 and

@@ -38,11 +38,10 @@ def test_split_override_changes_the_plan_bounds():
     # 1024 keys means more split-KV partial rows, 2048-key splits fewer
     assert s256[0] > base[0] > s2048[0] > 0
     # contexts of 262144 tokens (16384 blocks of 16): 256 splits of 1024
-    # keys; 256-key splits would need 1024, and 2048-key splits span more
-    # than 64 blocks of 16
-    assert base[1] > 0 and s256[1] == 0 and s2048[1] == 0
-    # 2048-key splits over 16-token blocks are refused at any length
-    assert s2048[2] == 0 and base[2] > 0
+    # keys or 128 of 2048; 256-key splits would need 1024
+    assert base[1] > 0 and s256[1] == 0 and s2048[1] > 0
+    # 2048-key splits span 128 blocks of 16, the most a split may
+    assert s2048[2] > 0 and base[2] > 0
 
 
 def test_bad_override_values_are_rejected():
