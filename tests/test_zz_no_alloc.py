@@ -89,3 +89,40 @@ def test_noalloc_rejects_beyond_scratch():
         pa.pa_attention_noalloc(q, cu, lens, table, kc, kc, 0.1, wl.num_heads, wl.num_kv_heads,
                                 torch.empty_like(q))
     assert e.value.status == 3   # PA_ERR_WORKSPACE_TOO_SMALL
+
+
+def test_noalloc_under_graph_capture():
+    """The entry point captured in a graph (the caller it is for): each of
+    three replays equals the eager output bitwise, with eager work between
+    replays that includes an allocation-free call on another batch, which
+    overwrites the shared scratch the graph's kernels use."""
+    wl = W.custom([1, 40, 1, 3], [3000, 500, 20, 2100], 32, 8, 128, 16, seed=54)
+    other = W.custom([2, 1, 17], [5000, 70, 900], 32, 8, 128, 16, seed=55)
+    _log(f"noalloc under graph capture: {wl.name}")
+    d, d2 = device_inputs(wl), device_inputs(other)
+    out = torch.empty_like(d["q"])
+
+    def call():
+        pa.pa_attention_noalloc(d["q"], d["cu"], d["lens"], d["table"], d["kc"], d["vc"],
+                                wl.scale, wl.num_heads, wl.num_kv_heads, out)
+
+    call()
+    torch.cuda.synchronize()
+    ref = out.clone()
+    assert torch.equal(ref, run_attention(wl, d))
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    ref2 = run_attention(other, d2)
+    for _ in range(3):
+        out.zero_()
+        assert torch.equal(_noalloc(other, d2), ref2)
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref)
