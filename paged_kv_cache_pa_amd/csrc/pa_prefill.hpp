@@ -47,9 +47,11 @@ constexpr int kSchedDsRead = 0x100;
 // copies the 16 bytes at base + voff (base wave-uniform, voff a 32-bit
 // per-lane byte offset) to LDS byte lds_base + 16 * l.  The compiler emits
 // the SGPR-base form and sets M0 (the LDS destination) itself.  The kernel
-// orders these copies with explicit vmcnt waits and barriers; the compiler
-// adds no waits of its own in the tile loops (the instruction listing has
-// the same waits as a hand-written form).
+// orders these copies with explicit vmcnt waits and barriers.  Each tick's
+// __syncthreads() also waits for all of the wave's copies in flight (the
+// copies write LDS); barriers that leave the newest tile's copies in flight
+// measured slower, since copies landing during the matrix-core phase compete
+// with its LDS operand reads.
 __device__ inline void lds_dma16(const void* base, uint32_t voff, uint32_t lds_base) {
   __builtin_amdgcn_global_load_lds((const unsigned char*)base + voff,
                                    (__attribute__((address_space(3))) void*)(uintptr_t)lds_base,
