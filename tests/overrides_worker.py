@@ -4,7 +4,8 @@ environment (the library reads them once per process).
 
 For a set of batches built around the split length in force, it checks
 through the C ABI:
-* every output within the fp16 / bf16 bar of the fp64 oracle;
+* every output within the fp16 / bf16 bar of the fp64 oracle (also over
+  fp8 caches, for decode-shaped batches);
 * batch invariance: each sequence's rows computed in a call of its own
   (same cache, same table row) equal its rows in the whole batch bitwise.
 Prints one JSON line and exits 0 when everything holds, 1 otherwise.
@@ -22,7 +23,8 @@ import torch  # noqa: E402
 
 import paged_kv_cache_pa_amd as pa  # noqa: E402
 from paged_kv_cache_pa_amd import workloads as W  # noqa: E402
-from gpu_util import TOL, device_inputs, max_err, oracle_full  # noqa: E402
+from gpu_util import (TOL, device_inputs, device_inputs_fp8, max_err, oracle_full,  # noqa: E402
+                      oracle_full_fp8, run_attention_fp8)
 
 
 def one_sequence(wl, d, b, **opts):
@@ -72,6 +74,18 @@ def main():
             if not torch.equal(alone, out[cu[b]:cu[b + 1]]):
                 invariant = False
                 print(json.dumps({"not invariant": wl.name, "seq": b}), flush=True)
+        n += 1
+    # fp8 caches (decode-shaped batches; the forced prefill path does not
+    # apply to them): the same split boundaries through the fp8 decode items.
+    for bs in bs_list:
+        wl = W.custom([1, 2, 1, 1], [S - 1, 2 * S + 5, S + 1, 3 * S + 7], 32, 8, 128, bs,
+                      seed=65)
+        d = device_inputs_fp8(wl)
+        err = max_err(run_attention_fp8(wl, d), oracle_full_fp8(wl, d))
+        worst = max(worst, err)
+        if not err <= TOL[wl.dtype]:
+            print(json.dumps({"fail": "fp8 " + wl.name, "err": err}), flush=True)
+            return 1
         n += 1
     print(json.dumps({"split_keys": S, "path": path, "batches": n, "worst_err": worst,
                       "batch_invariant": invariant}), flush=True)
