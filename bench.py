@@ -315,16 +315,44 @@ def summarize(wl, ms, per_kernel, kv_es=ES):
     return r
 
 
-def kernel_source_hash():
-    """Hash of the sources the kernels are compiled from: every file under
-    csrc/ except pa_api.hip, the C-ABI host code, which holds no kernel."""
+def strip_comments(src):
+    """C++ source without its // and /* */ comments (string and character
+    literals kept as they are)."""
+    out, i, n = [], 0, len(src)
+    while i < n:
+        c = src[i]
+        if c in "\"'":
+            j = i + 1
+            while j < n and src[j] != c:
+                j += 2 if src[j] == "\\" else 1
+            out.append(src[i:j + 1])
+            i = j + 1
+        elif src.startswith("//", i):
+            j = src.find("\n", i)
+            i = n if j < 0 else j
+        elif src.startswith("/*", i):
+            j = src.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+        else:
+            out.append(c)
+            i += 1
+    return "".join(out)
+
+
+def kernel_source_hash(sources=None):
+    """Hash of the code the kernels are compiled from: every file under
+    csrc/ except pa_api.hip (the C-ABI host code, which holds no kernel),
+    with comments removed and runs of white space made one space, so that
+    only a change of code marks recorded counters as stale.  ``sources``: {file name: text} in place of the
+    files on disk."""
+    if sources is None:
+        csrc = os.path.join(ROOT, "paged_kv_cache_pa_amd", "csrc")
+        sources = {f: open(os.path.join(csrc, f)).read() for f in os.listdir(csrc)}
     h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "paged_kv_cache_pa_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
+    for f in sorted(sources):
         if f == "pa_api.hip":
             continue
-        with open(os.path.join(csrc, f), "rb") as fh:
-            h.update(fh.read())
+        h.update(f.encode() + b"\0" + " ".join(strip_comments(sources[f]).split()).encode())
     return h.hexdigest()[:16]
 
 

@@ -13,9 +13,11 @@ namespace pa {
 // split depends on nothing but this length, so its output never depends on
 // its batch-mates.  1024 measured faster than 512 on the large mixed batch
 // (half the split partials to write and combine) and the same on pure
-// decode; 256 was 7 % slower (per-item start-up).  The kernels take the
-// length as an argument (a power of two, at most 64 blocks: one lane per
-// block id), so a test-only host override can vary it.
+// decode; 256 was 7 % slower (per-item start-up), and 2048 no faster on
+// the mixed batch (a cheaper combine, longer decode items).  The kernels
+// take the length as an argument (a power of two, at most 128 blocks: two
+// registers of block ids, one per lane each), so a test-only host override
+// can vary it.
 constexpr int kSplitKeys = 1024;
 // Largest split count per sequence (the block table row bounds the context:
 // max_blocks_per_seq * block_size <= kSplitKeys * kMaxSplitsCombine).
