@@ -23,7 +23,8 @@ import torch
 
 import oracle
 from paged_kv_cache_pa_amd import workloads as W
-from gpu_util import NAN_BITS, TOL, device_inputs, run_attention
+from gpu_util import (FP8_NAN, NAN_BITS, TOL, device_inputs, device_inputs_fp8, run_attention,
+                      run_attention_fp8)
 from pa_testutil import oracle_caches_for
 
 pytestmark = pytest.mark.gpu
@@ -137,3 +138,58 @@ def test_whole_cache_scatter_full_workload(idx):
         assert np.array_equal(_bits(d["vc"][a:e]), vref), (a, e)
     _log(f"  {wl.num_blocks} blocks x 2 caches ({2 * wl.num_blocks * row * 2 / 2**30:.1f} GiB) "
          f"bit-exact, {len(slots)} slots written, {time.perf_counter() - t0:.1f} s")
+
+
+def test_every_row_fp8_pure_decode():
+    """The pure-decode workload over fp8 (e4m3) caches: every output row
+    against the oracle's attention over its own quantization of the
+    generator's values (one sequence at a time, on the host threads)."""
+    from oracle import kv_fp8
+    wl = W.by_index(3)
+    _log(f"full parity over fp8 caches: {wl.name}")
+    d = device_inputs_fp8(wl, backend="torch")
+    out = run_attention_fp8(wl, d)
+    assert torch.isfinite(out).all()
+    kb, vb = _bits(d["k_all"]), _bits(d["v_all"])
+    qh = d["q"].float().cpu().numpy().astype(np.float64)
+    oh = out.float().cpu().numpy().astype(np.float64)
+    ks, vs = d["ks_np"], d["vs_np"]
+    del d, out
+    torch.cuda.empty_cache()
+    cu, kv_cu, bs = wl.cu_seqlens_q, wl.kv_cu, wl.block_size
+    shape = (bs, wl.num_kv_heads, wl.head_size)
+
+    def one(b):
+        lo, hi = int(kv_cu[b]), int(kv_cu[b + 1])
+        kq = kv_fp8.quantize(_decode(kb[lo:hi], wl.dtype), ks)
+        vq = kv_fp8.quantize(_decode(vb[lo:hi], wl.dtype), vs)
+        kc, vc = {}, {}
+        for r, slot in enumerate(wl.kv_slots[lo:hi]):
+            blk, off = divmod(int(slot), bs)
+            if blk not in kc:
+                kc[blk] = np.full(shape, FP8_NAN, np.uint8)
+                vc[blk] = np.full(shape, FP8_NAN, np.uint8)
+            kc[blk][off] = kq[r]
+            vc[blk][off] = vq[r]
+        ql = int(cu[b + 1] - cu[b])
+        ref = kv_fp8.attention_fp8(qh[cu[b]:cu[b + 1]], np.array([0, ql], np.int32),
+                                   wl.seqlens_kv[b:b + 1], wl.block_table[b:b + 1], kc, vc, ks, vs,
+                                   wl.scale, wl.num_heads, wl.num_kv_heads, bs)
+        return b, float(np.abs(oh[cu[b]:cu[b + 1]] - ref).max())
+
+    t0 = time.perf_counter()
+    order = sorted(range(wl.num_seqs), key=lambda b: -int(wl.seqlens_kv[b]))
+    errs = {}
+    last = t0
+    with _blas_one_thread(), ThreadPoolExecutor(WORKERS) as ex:
+        for b, e in ex.map(one, order):
+            errs[b] = e
+            if time.perf_counter() - last > 20.0:
+                last = time.perf_counter()
+                _log(f"  ... {len(errs)}/{wl.num_seqs} sequences, {last - t0:.0f} s")
+    worst_b = max(errs, key=errs.get)
+    _log(f"  {wl.num_tokens} rows x {wl.num_heads} heads, oracle {time.perf_counter() - t0:.1f} s "
+         f"on {WORKERS} threads; worst max abs error {errs[worst_b]:.3g} (sequence {worst_b}, "
+         f"kv {int(wl.seqlens_kv[worst_b])}); bar {TOL[wl.dtype]}")
+    bad = {b: e for b, e in errs.items() if not e <= TOL[wl.dtype]}
+    assert not bad, f"{len(bad)} sequences over the bar, e.g. {sorted(bad.items())[:5]}"
