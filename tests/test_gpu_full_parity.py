@@ -58,12 +58,14 @@ def _blas_one_thread():
         return contextlib.nullcontext()
 
 
-@pytest.mark.parametrize("idx", [3, 4, 5])
-def test_every_row_full_workload(idx):
+@pytest.mark.parametrize("idx,opts", [(3, {}), (4, {}), (5, {}),
+                                      (5, {"softcap": 50.0, "local_window_size": 4096})],
+                         ids=["decode", "prefill", "mixed", "mixed-cap50-window4096"])
+def test_every_row_full_workload(idx, opts):
     wl = W.by_index(idx)
-    _log(f"full parity: {wl.name}")
+    _log(f"full parity: {wl.name} {opts or ''}")
     d = device_inputs(wl, backend="torch")
-    out = run_attention(wl, d)
+    out = run_attention(wl, d, **opts)
     assert torch.isfinite(out).all()
     kb, vb = _bits(d["k_all"]), _bits(d["v_all"])
     qh = d["q"].float().cpu().numpy().astype(np.float64)
@@ -81,7 +83,7 @@ def test_every_row_full_workload(idx):
                                    lambda _: _decode(vb[lo:hi], wl.dtype))
         ref = oracle.attention(qh[cu[b]:cu[b + 1]], np.array([0, ql], np.int32),
                                wl.seqlens_kv[b:b + 1], wl.block_table[b:b + 1], kc, vc,
-                               wl.scale, wl.num_heads, wl.num_kv_heads, wl.block_size)
+                               wl.scale, wl.num_heads, wl.num_kv_heads, wl.block_size, **opts)
         return b, float(np.abs(oh[cu[b]:cu[b + 1]] - ref).max())
 
     t0 = time.perf_counter()
