@@ -9,8 +9,11 @@
 //
 // Per sequence b: q_len = cu[b+1] - cu[b], L = seqlens_kv[b].  A sequence
 // whose q_len * G columns fit one 16-wide tile takes the decode path and is
-// split into ceil(L / split_keys) key ranges; every other non-empty sequence
-// takes the prefill path in tiles of tokens_per_tile tokens per KV head.
+// split into ceil(L / split_keys) key ranges: the decode work list holds
+// every full split, then the partial last splits, longest first (by length
+// class), so the work ends on the shortest items; every other non-empty
+// sequence takes the prefill path in tiles of tokens_per_tile tokens per KV
+// head.
 // Prefill (sequence, KV head) pairs are dealt to 8 queues, one per XCD, so
 // all tiles that reuse one K/V stream share an L2; inside a queue the
 // heaviest (last) tile of each pair comes first.  The plan also splits the
@@ -88,6 +91,12 @@ __device__ inline SeqCounts seq_counts(const PlanArgs& a, int b) {
   return c;
 }
 
+// Length class of a sequence's partial last split (its L mod split keys):
+// 0 for the shortest quarter of split lengths, up to 3 for the longest.
+__device__ inline int part_class(int L, int split_shift) {
+  return ((L & ((1 << split_shift) - 1)) << 2) >> split_shift;
+}
+
 // Number of KV heads kh in [0, Hk) with (b * Hk + kh) % 8 == x.
 __device__ inline int heads_in_queue(int b, int hk, int x) {
   const int r = ((x - (int)(((int64_t)b * hk) & 7)) % 8 + 8) % 8;
@@ -127,10 +136,14 @@ __device__ inline void emit_second_pass(const PlanArgs& a, int b, const SeqCount
 
 }  // namespace
 
+// Partial last splits are placed longest first, in kPartClasses classes of
+// their key count, so the decode work ends on the shortest items.
+constexpr int kPartClasses = 4;
+
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
-  __shared__ int lds[(kPlanWaves + 1) * 12];
+  __shared__ int lds[(kPlanWaves + 1) * 16];
   __shared__ int qstart[kQueues];
-  __shared__ int nfull_total;
+  __shared__ int part_start[kPartClasses];
   __shared__ float cost_sh[kPlanWaves][2];
   const int tid = threadIdx.x;
   if (tid <= kQueues) a.counters[kLine * tid] = 0;   // fetch counters: decode, then queues 0..7
@@ -141,7 +154,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
 
   // Pass 1: sequence info, decode pairs, partial-row bases, queue sizes,
   // estimated prefill and decode costs.
-  int carry[3 + kQueues] = {0};
+  int carry[2 + kPartClasses + kQueues] = {0};
   float cost_p = 0.f, cost_d = 0.f;
   for (int base = 0; base < a.num_seqs; base += kPlanThreads) {
     const int b = base + tid;
@@ -155,17 +168,21 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
       cost_d += (float)(c.L - (c.s0 << a.split_shift)) * a.num_kv_heads;
     }
     // Decode pairs: every full split first (pass 1), then the
-    // shorter last splits (pass 2), so the tail of the decode work is made
-    // of short items.
+    // shorter last splits (pass 2), longest first, so the tail of the
+    // decode work is made of the shortest items.
     const int has_part = (c.L & (a.split_keys - 1)) != 0 && c.nsplit > 0;
+    const int pcls = part_class(c.L, a.split_shift);
     const int nfull = max(0, c.nsplit - has_part - c.s0);   // live full splits: s0 ..
-    int v[3 + kQueues], tot[3 + kQueues];
+    constexpr int NV = 2 + kPartClasses + kQueues;
+    int v[NV], tot[NV];
     v[0] = nfull;
     v[1] = c.prows;
-    v[2] = has_part;
 #pragma unroll
-    for (int x = 0; x < kQueues; ++x) v[3 + x] = c.ntiles * heads_in_queue(b, a.num_kv_heads, x);
-    block_scan<3 + kQueues>(v, tot, lds);
+    for (int k = 0; k < kPartClasses; ++k) v[2 + k] = has_part && pcls == k;
+#pragma unroll
+    for (int x = 0; x < kQueues; ++x)
+      v[2 + kPartClasses + x] = c.ntiles * heads_in_queue(b, a.num_kv_heads, x);
+    block_scan<NV>(v, tot, lds);
     if (b < a.num_seqs) {
       a.seqinfo[b] = SeqInfo{c.cu0, c.q_len, c.L, carry[1] + v[1]};
       const int off = carry[0] + v[0];
@@ -175,13 +192,20 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
       int qpos[kQueues], run = 0;
 #pragma unroll
       for (int x = 0; x < kQueues; ++x) {
-        qpos[x] = run + v[3 + x];
-        run += tot[3 + x];
+        qpos[x] = run + v[2 + kPartClasses + x];
+        run += tot[2 + kPartClasses + x];
       }
-      emit_second_pass(a, b, c, has_part, tot[0] + v[2], qpos);
+      int part_at = tot[0];   // after every full split: longer classes first
+#pragma unroll
+      for (int k = kPartClasses - 1; k >= 0; --k)
+        if (k > pcls) part_at += tot[2 + k];
+#pragma unroll
+      for (int k = 0; k < kPartClasses; ++k)
+        if (k == pcls) part_at += v[2 + k];
+      emit_second_pass(a, b, c, has_part, part_at, qpos);
     }
 #pragma unroll
-    for (int k = 0; k < 3 + kQueues; ++k) carry[k] += tot[k];
+    for (int k = 0; k < NV; ++k) carry[k] += tot[k];
   }
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
@@ -204,14 +228,18 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
     if (wd > 0.f) first = (int)(a.num_workers * (wp / (wp + wd)) + 0.5f);
     if (wp > 0.f && first < 1) first = 1;
     a.counters[kPrefillFirst] = min(first, a.num_workers);
-    a.counters[kNumDecPairs] = carry[0] + carry[2];
-    nfull_total = carry[0];
+    int pairs = carry[0];
+    for (int k = kPartClasses - 1; k >= 0; --k) {
+      part_start[k] = pairs;
+      pairs += carry[2 + k];
+    }
+    a.counters[kNumDecPairs] = pairs;
     int run = 0;
     for (int x = 0; x < kQueues; ++x) {
-      a.counters[kQueueLen + x] = carry[3 + x];
+      a.counters[kQueueLen + x] = carry[2 + kPartClasses + x];
       a.counters[kQueueStart + x] = run;
       qstart[x] = run;
-      run += carry[3 + x];
+      run += carry[2 + kPartClasses + x];
     }
   }
   if (one_sweep) return;
@@ -219,22 +247,29 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
 
   // Pass 2 (batches of more than one sweep): the partial last decode splits
   // after all full ones; prefill items.
-  int qcarry[kQueues + 1] = {0};
+  constexpr int NV2 = kQueues + kPartClasses;
+  int qcarry[NV2] = {0};
   for (int base = 0; base < a.num_seqs; base += kPlanThreads) {
     const int b = base + tid;
     const SeqCounts c = seq_counts(a, b);
     const int has_part = (c.L & (a.split_keys - 1)) != 0 && c.nsplit > 0;
-    int v[kQueues + 1], tot[kQueues + 1];
+    const int pcls = part_class(c.L, a.split_shift);
+    int v[NV2], tot[NV2];
 #pragma unroll
     for (int x = 0; x < kQueues; ++x) v[x] = c.ntiles * heads_in_queue(b, a.num_kv_heads, x);
-    v[kQueues] = has_part;
-    block_scan<kQueues + 1>(v, tot, lds);
+#pragma unroll
+    for (int k = 0; k < kPartClasses; ++k) v[kQueues + k] = has_part && pcls == k;
+    block_scan<NV2>(v, tot, lds);
     int qpos[kQueues];
 #pragma unroll
     for (int x = 0; x < kQueues; ++x) qpos[x] = qstart[x] + qcarry[x] + v[x];
-    emit_second_pass(a, b, c, has_part, nfull_total + qcarry[kQueues] + v[kQueues], qpos);
+    int part_at = 0;
 #pragma unroll
-    for (int x = 0; x <= kQueues; ++x) qcarry[x] += tot[x];
+    for (int k = 0; k < kPartClasses; ++k)
+      if (k == pcls) part_at = part_start[k] + qcarry[kQueues + k] + v[kQueues + k];
+    emit_second_pass(a, b, c, has_part, part_at, qpos);
+#pragma unroll
+    for (int x = 0; x < NV2; ++x) qcarry[x] += tot[x];
   }
 }
 
