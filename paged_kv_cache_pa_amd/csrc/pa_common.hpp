@@ -117,11 +117,20 @@ __device__ inline uint32_t pair_elem(uint32_t xw, uint32_t yw, bool hi) {
 constexpr float kMaxSlack = 8.f;
 
 // xor-16 / xor-32 lane exchanges as VALU permutes (no LDS round trip).
+// max of two floats as one v_max_f32.  fmaxf on values that come out of a
+// lane permute makes the compiler quiet possible signalling NaNs first (a
+// v_max_f32 x, x per operand); the values here are arithmetic results or
+// -inf, never signalling NaNs, so that step is dropped.
+__device__ inline float max_raw(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
 __device__ inline float max_xor16_32(float v) {
   auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  v = max_raw(__uint_as_float(a[0]), __uint_as_float(a[1]));
   auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+  return max_raw(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 __device__ inline float sum_xor16_32(float v) {
   auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);

@@ -242,6 +242,23 @@ __device__ __forceinline__ void prefill_items(const AttnArgs& a) {
       // them are not hoisted out of the item loop and held across it.
       const int lane = lane_here();
       const int r16 = lane & 15, kq = lane >> 4;
+      // Operand-read offsets.  Both swizzles XOR the chunk index with row
+      // bits that are fixed per lane, so every operand read is one XOR-add on
+      // two values held per lane plus an immediate offset:
+      //  K, chunk 4s + kq of row 16 kap + r16 (kslot):
+      //    16 kap ROWB + k_lane + (k_x ^ 64 s);
+      //  V^T, d-tile t, key row 32u + 16e + vrow (vread):
+      //    32u ROWB + 16e ROWB + v_lane + (v_x ^ 32 t).
+      // (kswz(r16) = 4 k_x/64 + its low two bits; swz(vrow) = 2 v_x/32 + its
+      // low bit; u, e and kap only move rows by multiples of 16.)
+      const int ksw = kswz(r16);
+      const uint32_t k_lane = (uint32_t)(r16 * ROWB + 16 * (kq ^ (ksw & 3)));
+      uint32_t k_x = (uint32_t)(64 * (ksw >> 2));
+      const int vrow = 4 * kq + (r16 >> 2);
+      const int vsw = swz(vrow);
+      const uint32_t v_lane =
+          (uint32_t)(vrow * ROWB + 16 * (((lane & 3) >> 1) ^ (vsw & 1)) + ((lane & 1) << 3));
+      uint32_t v_x = (uint32_t)(32 * (vsw >> 1));
 
       // Q^T operands and causal limits of this lane's row groups.
       u32x4_t qreg[NR][NS];
@@ -303,7 +320,6 @@ __device__ __forceinline__ void prefill_items(const AttnArgs& a) {
 
       // acc += P_t V_t with V of tile t (buffer t % 4).
       auto pv = [&](int t) {
-        const unsigned char* vb = lds + (t % NB) * 2 * TB;
           // O^T tile t covers d = 16t .. 16t+15.  ds_read_b64_tr_b16: within
           // each 16-lane group, result lane i gets element i % 4 of the
           // 8 bytes read by source lanes 4r + i / 4 (r = 0..3).  Source lane
@@ -311,19 +327,19 @@ __device__ __forceinline__ void prefill_items(const AttnArgs& a) {
           // i receives d = 16t + i of keys 4kq .. 4kq+3: the V^T operand,
           // with contraction element e <-> key 32u + 4kq + e (e < 4) or
           // 32u + 16 + 4kq + (e - 4), the same keys pb holds.
-          const int r4 = (lane & 15) >> 2, q4 = lane & 3, vk = kq;
           // Operands in groups of VG (u, t .. t+VG-1); group g+1 is read while
           // group g feeds its MFMAs (two register sets, fenced as in qk).
           constexpr int VG = 4;
           constexpr int NG = (NK / 2) * NT / VG;
-          auto vread = [&](int u, int t) {
-            const int R0 = 32 * u + 4 * vk + r4;
-            const int chunk = 2 * t + (q4 >> 1);
-            const int boff = (q4 & 1) << 3;
-            const short4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (lds_s4_t)(vb + TB + slot(R0, chunk) + boff));
-            const short4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (lds_s4_t)(vb + TB + slot(R0 + 16, chunk) + boff));
+          // v_x passes through an empty asm each tile, so the XOR stays one
+          // v_xad_u32 per read instead of a table of per-lane offsets held
+          // across the tile loop.
+          asm volatile("" : "+v"(v_x));
+          const uint32_t vb = (uint32_t)((t % NB) * 2 * TB + TB) + v_lane;
+          auto vread = [&](int u, int dt) {
+            const unsigned char* p = lds + ((v_x ^ (uint32_t)(32 * dt)) + vb) + 32 * u * ROWB;
+            const short4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4_t)p);
+            const short4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4_t)(p + 16 * ROWB));
             const u32x2_t l2 = __builtin_bit_cast(u32x2_t, lo);
             const u32x2_t h2 = __builtin_bit_cast(u32x2_t, hi);
             return u32x4_t{l2[0], l2[1], h2[0], h2[1]};
@@ -356,29 +372,27 @@ __device__ __forceinline__ void prefill_items(const AttnArgs& a) {
       // fences keep each group's reads a group ahead of their use, so the
       // LDS latency hides under the previous group's 8 MFMAs).  Group 0's
       // operands are read by qk_first, which the matrix-core phase issues
-      // before its P.V, so their latency hides under the P.V MFMAs.
+      // before its P.V, so their latency hides under the P.V MFMAs; qk()
+      // then reads the tile whose offsets qk_first(t) left in koff.
       u32x4_t ka[2][NS];
+      uint32_t koff[NS];   // this tile's K read offsets for kap = 0 (qk_first)
       auto qk_first = [&](int t) {
-        const unsigned char* kb = lds + (t % NB) * 2 * TB;
-        const int ln = lane_here();
-        const int kr = ln & 15, kk = ln >> 4;
+        asm volatile("" : "+v"(k_x));   // one v_xad_u32 per offset, as v_x in pv
+        const uint32_t kb = (uint32_t)((t % NB) * 2 * TB) + k_lane;
 #pragma unroll
-        for (int s = 0; s < NS; ++s)
-          ka[0][s] = *reinterpret_cast<const u32x4_t*>(kb + kslot(kr, 4 * s + kk));
+        for (int s = 0; s < NS; ++s) {
+          koff[s] = (k_x ^ (uint32_t)(64 * s)) + kb;
+          ka[0][s] = *reinterpret_cast<const u32x4_t*>(lds + koff[s]);
+        }
       };
-      auto qk = [&](int t) {
-        const unsigned char* kb = lds + (t % NB) * 2 * TB;
-        // Per-lane K read offsets recomputed here (a few VALU ops per tile)
-        // rather than held across the tile loop.
-        const int ln = lane_here();
-        const int kr = ln & 15, kk = ln >> 4;
+      auto qk = [&]() {
 #pragma unroll
         for (int kap = 0; kap < NK; ++kap) {
           if (kap + 1 < NK) {
 #pragma unroll
             for (int s = 0; s < NS; ++s)
               ka[(kap + 1) & 1][s] =
-                  *reinterpret_cast<const u32x4_t*>(kb + kslot(16 * (kap + 1) + kr, 4 * s + kk));
+                  *reinterpret_cast<const u32x4_t*>(lds + koff[s] + 16 * (kap + 1) * ROWB);
           }
           __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -538,7 +552,7 @@ __device__ __forceinline__ void prefill_items(const AttnArgs& a) {
           __builtin_amdgcn_sched_barrier(0);
           if (i > a0) pv(t_lo + i - 1);
           __builtin_amdgcn_sched_barrier(0);
-          qk(t_lo + i);
+          qk();
           __syncthreads();
           even_service(i);
           fetch_service(i);
@@ -567,7 +581,7 @@ __device__ __forceinline__ void prefill_items(const AttnArgs& a) {
         __syncthreads();
         if (a3 > a0) {
           qk_first(t_lo + i);
-          qk(t_lo + i);
+          qk();
         }
         odd_service(i);
         __syncthreads();
@@ -581,7 +595,7 @@ __device__ __forceinline__ void prefill_items(const AttnArgs& a) {
           __builtin_amdgcn_sched_barrier(0);
           pv(t_lo + i - 1);
           __builtin_amdgcn_sched_barrier(0);
-          qk(t_lo + i);
+          qk();
           odd_service(i);
           __syncthreads();
         };
