@@ -443,18 +443,22 @@ __device__ __forceinline__ void prefill_items(const AttnArgs& a) {
             mt = CAP ? capf(mt) : mt * c;   // the cap is increasing: max commutes
           }
           mt = max_xor16_32(mt);
-          const bool raise = mt > m[rho] + kMaxSlack || m[rho] == -INFINITY;
-          float alpha = 1.f;
+          // (While m is -inf, m + kMaxSlack is too, so any finite tile max
+          // raises it.)
+          const bool raise = mt > m[rho] + kMaxSlack;
           if (__any(raise)) {   // rare after the first tile
             const float m_new = raise ? fmaxf(m[rho], mt) : m[rho];
             const float base_old = m[rho] == -INFINITY ? 0.f : m[rho];
             const float base_new = m_new == -INFINITY ? 0.f : m_new;
-            alpha = m[rho] == -INFINITY ? 0.f : exp2_fast(base_old - base_new);
+            const float alpha = m[rho] == -INFINITY ? 0.f : exp2_fast(base_old - base_new);
             m[rho] = m_new;
+            l[rho] *= alpha;
 #pragma unroll
             for (int t = 0; t < NT; ++t) scale_in_place(acc[rho][t], alpha);
           }
-          const float base_m = m[rho] == -INFINITY ? 0.f : m[rho];
+          // An unmasked tile shows every row of the wave all 64 of its keys,
+          // so m is finite here; a masked row can still have m = -inf.
+          const float base_m = !kMasked ? m[rho] : m[rho] == -INFINITY ? 0.f : m[rho];
           float sv[NK][4];
 #pragma unroll
           for (int kap = 0; kap < NK; ++kap)
@@ -464,8 +468,7 @@ __device__ __forceinline__ void prefill_items(const AttnArgs& a) {
                            : CAP   ? exp2_fast(capf(sacc[kap][rho][i]) - base_m)
                                    : exp2_fast(fmaf(sacc[kap][rho][i], c, -base_m));
           // P rounded to the input dtype feeds P.V; the denominator sums
-          // the same rounded values.
-          float psum = 0.f;
+          // the same rounded values, straight into l.
 #pragma unroll
           for (int u = 0; u < NK / 2; ++u) {
             pb[rho][u] = u32x4_t{Elt<T>::pack2(sv[2 * u][0], sv[2 * u][1]),
@@ -473,9 +476,8 @@ __device__ __forceinline__ void prefill_items(const AttnArgs& a) {
                                  Elt<T>::pack2(sv[2 * u + 1][0], sv[2 * u + 1][1]),
                                  Elt<T>::pack2(sv[2 * u + 1][2], sv[2 * u + 1][3])};
 #pragma unroll
-            for (int w = 0; w < 4; ++w) psum = Elt<T>::sum2(pb[rho][u][w], psum);
+            for (int w = 0; w < 4; ++w) l[rho] = Elt<T>::sum2(pb[rho][u][w], l[rho]);
           }
-          l[rho] = l[rho] * alpha + psum;
           __builtin_amdgcn_sched_barrier(0);   // one row group at a time (registers)
         }
       };
