@@ -274,7 +274,29 @@ def time_workload(wl, steps, warmup, torch, pa, W, extras=False, fp8=False, opts
         r.update({"bytes": nbytes, "GBps": nbytes / (r["median_ms"] * 1e-3) / 1e9,
                   "rotary_dim": wl.head_size, "pairing": "split", "input": "packed QKV"})
         more["rotary_scatter"] = r
-        del packed, q_rot
+        # The whole rotary step: that scatter writing the rotated Q and
+        # pa_attention reading it back, against the scatter leaving Q alone
+        # and pa_attention_rope rotating Q from the packed rows as it loads
+        # it (same output bits).
+        qv = packed.view(T, -1, wl.head_size)
+        two = lambda: (fn(), pa.pa_attention(  # noqa: E731
+            q_rot, st["cu"], st["lens"], st["table"], st["kc"], st["vc"], wl.scale, wl.num_heads,
+            wl.num_kv_heads, out=st["out"], workspace=st["ws"], **st["opts"]))
+        fused = lambda: (pa.pa_rotary_scatter_kv(  # noqa: E731
+            packed, st["cu"], st["lens"], st["table"], st["kc"], st["vc"], wl.num_heads,
+            wl.num_kv_heads, cos_cache=cos, sin_cache=sin, write_q=False), pa.pa_attention_rope(
+            qv, st["cu"], st["lens"], st["table"], st["kc"], st["vc"], wl.scale, wl.num_heads,
+            wl.num_kv_heads, cos_cache=cos, sin_cache=sin, out=st["out"], workspace=st["ws"],
+            **st["opts"]))
+        rs = {}
+        for name, f in (("two_step", two), ("fused", fused)):
+            f()
+            rs[name] = per_rep_times(f, steps, torch, scrub)
+        rs["note"] = ("pa_rotary_scatter_kv + pa_attention on its rotated Q, against the scatter "
+                      "without Q + pa_attention_rope on the packed rows (Q rotated on load)")
+        rs["fused_vs_two_step"] = rs["fused"]["median_ms"] / rs["two_step"]["median_ms"]
+        more["rope_step"] = rs
+        del packed, q_rot, qv
         del scrub
     del st
     torch.cuda.empty_cache()
@@ -692,6 +714,7 @@ def main():
         "sub_batches": more.get("sub_batches"),
         "scatter": more.get("scatter"),
         "rotary_scatter": more.get("rotary_scatter"),
+        "rope_step": more.get("rope_step"),
         "extra": extra,
     }
     if not args.no_extra and args.workload == "mixed" and not opts:

@@ -199,7 +199,9 @@ pa_status_t pa_seqlens_from_past(const int32_t* cu_seqlens_q,
  * query        [num_tokens, num_heads, head_size] dtype, or, when key and
  *              value are NULL, packed rows [num_tokens, num_heads +
  *              2 num_kv_heads, head_size]: each token's Q heads, then its K
- *              heads, then its V heads.
+ *              heads, then its V heads.  NULL with key, value given and
+ *              q_out NULL (a K/V-only rotated scatter, such as filling the
+ *              cache with history keys).
  * key, value   [num_tokens, num_kv_heads, head_size] dtype, or both NULL.
  * cos_cache,
  * sin_cache    [max_position, rotary_dim / 2] dtype, or both NULL (no
@@ -211,7 +213,9 @@ pa_status_t pa_seqlens_from_past(const int32_t* cu_seqlens_q,
  *              as for pa_attention.  A negative table entry gives the token
  *              no cache slot (its K/V are not written; its Q is).
  * q_out        [num_tokens, num_heads, head_size] dtype, written (the Q
- *              pa_attention then reads); must not overlap the inputs.
+ *              pa_attention then reads); must not overlap the inputs.  NULL:
+ *              the Q rows are not written (pa_attention_rope then reads Q
+ *              from the packed rows and rotates it as it loads it).
  * k_cache,
  * v_cache      paged caches, updated in place.
  * All tensor pointers 16-byte aligned (else PA_ERR_INVALID_ARGUMENT).
@@ -326,6 +330,53 @@ pa_status_t pa_attention(const void* q, const int32_t* cu_seqlens_q,
                          int32_t head_size, int32_t block_size, int32_t dtype,
                          void* workspace, size_t workspace_bytes,
                          void* stream);
+
+/*
+ * pa_attention_rope - pa_attention with the rotary embedding of Q fused into
+ * the attention's Q load, reading Q from rows of any stride (such as the
+ * packed QKV rows that pa_rotary_scatter_kv splits).
+ *
+ * Defines: "[WebGPU] Initial PagedAttention implementation (1/n)": the file
+ * summaries put a packed-QKV split program and a rotary program ahead of the
+ * attention, each a round trip through memory.  Here pa_rotary_scatter_kv
+ * (q_out NULL) rotates and scatters K and V, and this call reads the
+ * unrotated Q straight from the packed rows and rotates it on load, so Q is
+ * neither written nor read back.  The rotation is pa_rotary_scatter_kv's
+ * (same pairing, position p = past_b + i, tables, fp32 arithmetic rounded
+ * once to dtype): the result is bitwise that of pa_rotary_scatter_kv with a
+ * q_out followed by pa_attention on q_out.
+ *
+ * q            element (t, h, d) of Q at q[t * q_row_stride + h * head_size
+ *              + d], dtype; for packed [num_tokens, num_heads + 2
+ *              num_kv_heads, head_size] rows, q is the packed buffer and
+ *              q_row_stride = (num_heads + 2 num_kv_heads) * head_size.
+ * q_row_stride >= num_heads * head_size and a multiple of 8 (16-byte rows);
+ *              else PA_ERR_INVALID_ARGUMENT.
+ * cos_cache,
+ * sin_cache    [max_position, rotary_dim / 2] dtype, 16-byte aligned, or
+ *              both NULL (no rotation: pa_attention on strided Q rows).
+ * rotary_dim   multiple of 16 in [16, head_size] (others: NOT_IMPLEMENTED;
+ *              outside [1, head_size]: INVALID_ARGUMENT); dimensions >=
+ *              rotary_dim are used as given.  Ignored without tables.
+ * interleaved  nonzero: pairs (2k, 2k+1); 0: pairs (k, k + rotary_dim / 2).
+ * max_position >= 1 with tables.  A row whose position is >= max_position
+ *              breaks a precondition and is used unrotated.
+ * Every other argument, limit, status code and the empty call as for
+ * pa_attention; q and out must not overlap.
+ */
+pa_status_t pa_attention_rope(const void* q, int64_t q_row_stride,
+                              const void* cos_cache, const void* sin_cache,
+                              int32_t max_position, int32_t rotary_dim,
+                              int32_t interleaved, const int32_t* cu_seqlens_q,
+                              const int32_t* seqlens_kv,
+                              const int32_t* block_table, const void* k_cache,
+                              const void* v_cache, void* out, int32_t num_seqs,
+                              int64_t num_tokens, int32_t max_blocks_per_seq,
+                              int64_t num_blocks, float scale, float softcap,
+                              int32_t local_window_size, int32_t num_heads,
+                              int32_t num_kv_heads, int32_t head_size,
+                              int32_t block_size, int32_t dtype, void* workspace,
+                              size_t workspace_bytes, void* stream);
 
 /*
  * pa_attention_noalloc - pa_attention without a caller workspace and

@@ -12,7 +12,8 @@ import ctypes
 from ._lib import (PA_BF16, PA_F16, PROFILE_KINDS, PAError, check, lib)  # noqa: F401
 
 __all__ = ["pa_scatter_kv", "pa_scatter_kv_paged", "pa_scatter_kv_fp8", "pa_seqlens_from_past",
-           "pa_attention", "pa_attention_noalloc", "pa_attention_fp8", "pa_rotary_scatter_kv",
+           "pa_attention", "pa_attention_rope", "pa_attention_noalloc", "pa_attention_fp8",
+           "pa_rotary_scatter_kv",
            "pa_attention_workspace_size", "pa_validate_metadata", "profile_enable",
            "profile_read", "PAError"]
 
@@ -109,14 +110,20 @@ def pa_seqlens_from_past(cu_seqlens_q, past_seqlens, out=None, stream=None):
 
 def pa_rotary_scatter_kv(query, cu_seqlens_q, seqlens_kv, block_table, k_cache, v_cache,
                          num_heads, num_kv_heads, key=None, value=None, cos_cache=None,
-                         sin_cache=None, interleaved=False, q_out=None, stream=None):
+                         sin_cache=None, interleaved=False, q_out=None, stream=None,
+                         write_q=True):
     """Split packed QKV (``key``/``value`` None: ``query`` is [T, Hq + 2 Hk, D]
     or [T, (Hq + 2 Hk) * D]), rotate Q and K at each token's KV position
     with ``cos_cache``/``sin_cache`` [max_position, rotary_dim / 2] (None: no
     rotation), write K/V into the caches at the block table's slots and
-    return the (rotated) Q [T, Hq, D]."""
+    return the (rotated) Q [T, Hq, D].  ``write_q=False``: Q is not written
+    (returns None); pa_attention_rope rotates it as it loads it.  ``query``
+    may then be None when ``key``/``value`` are given (K/V only)."""
     import torch
-    T = query.shape[0]
+    if query is None and (write_q or key is None):
+        raise ValueError("query may be None only with key/value given and write_q=False")
+    ref = query if query is not None else key
+    T = ref.shape[0]
     nb, bs, hk, d = k_cache.shape
     B = seqlens_kv.shape[0]
     MB = block_table.shape[1]
@@ -126,11 +133,11 @@ def pa_rotary_scatter_kv(query, cu_seqlens_q, seqlens_kv, block_table, k_cache, 
     if key is None:
         if value is not None or query.numel() != T * (num_heads + 2 * num_kv_heads) * d:
             raise ValueError("packed QKV rows must hold Hq + 2 Hk heads")
-    elif query.numel() != T * num_heads * d or key.numel() != T * hk * d \
+    elif (query is not None and query.numel() != T * num_heads * d) or key.numel() != T * hk * d \
             or value is None or value.numel() != T * hk * d:
         raise ValueError("inconsistent Q/K/V shapes")
     for t in (key, value, k_cache, v_cache, cos_cache, sin_cache):
-        if t is not None and t.dtype != query.dtype:
+        if t is not None and t.dtype != ref.dtype:
             raise ValueError("all tensors share the query's dtype")
     if (cos_cache is None) != (sin_cache is None):
         raise ValueError("cos_cache and sin_cache go together")
@@ -138,18 +145,20 @@ def pa_rotary_scatter_kv(query, cu_seqlens_q, seqlens_kv, block_table, k_cache, 
                                                        2 * cos_cache.shape[1])
     if sin_cache is not None and tuple(sin_cache.shape) != tuple(cos_cache.shape):
         raise ValueError("cos_cache and sin_cache shapes differ")
-    if q_out is None:
+    if not write_q:
+        q_out = None
+    elif q_out is None:
         q_out = _alloc_on(stream, query, (T, num_heads, d), query.dtype)
     elif q_out.numel() != T * num_heads * d or q_out.dtype != query.dtype:
         raise ValueError("q_out must be [T, Hq, D] of the query's dtype")
     opt = lambda t, n: None if t is None else _dev(t, n)  # noqa: E731
     check(lib().pa_rotary_scatter_kv(
-        _dev(query, "query"), opt(key, "key"), opt(value, "value"), opt(cos_cache, "cos_cache"),
+        opt(query, "query"), opt(key, "key"), opt(value, "value"), opt(cos_cache, "cos_cache"),
         opt(sin_cache, "sin_cache"), max_pos, rdim, 1 if interleaved else 0,
         _dev(cu_seqlens_q, "cu_seqlens_q", torch.int32), _dev(seqlens_kv, "seqlens_kv", torch.int32),
-        _dev(block_table, "block_table", torch.int32), _dev(q_out, "q_out"),
+        _dev(block_table, "block_table", torch.int32), opt(q_out, "q_out"),
         _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), B, T, MB, nb, num_heads, hk, d, bs,
-        _dtype_code(query), _stream_ptr(query, stream)))
+        _dtype_code(ref), _stream_ptr(ref, stream)))
     return q_out
 
 
@@ -199,6 +208,53 @@ def pa_attention(q, cu_seqlens_q, seqlens_kv, block_table, k_cache, v_cache, sca
         _dtype_code(q),
         _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
         _stream_ptr(q, stream)))
+    return out
+
+
+def pa_attention_rope(q, cu_seqlens_q, seqlens_kv, block_table, k_cache, v_cache, scale,
+                      num_heads, num_kv_heads, cos_cache=None, sin_cache=None, interleaved=False,
+                      out=None, workspace=None, stream=None, softcap=0.0, local_window_size=0):
+    """pa_attention with Q read from rows of [T, H', D] (H' >= Hq; packed QKV
+    rows [T, Hq + 2 Hk, D] as given to pa_rotary_scatter_kv) and rotated as
+    it is loaded with ``cos_cache``/``sin_cache`` [max_position,
+    rotary_dim / 2] at each token's position (None: no rotation).  Returns
+    out [T, Hq, D], bitwise pa_attention on pa_rotary_scatter_kv's Q."""
+    import torch
+    T = q.shape[0]
+    d = k_cache.shape[-1]
+    nb, bs = k_cache.shape[0], k_cache.shape[1]
+    B = seqlens_kv.shape[0]
+    MB = block_table.shape[1]
+    if q.numel() % (T * d) != 0 or q.numel() // (T * d) < num_heads \
+            or cu_seqlens_q.shape != (B + 1,) or block_table.shape[0] != B \
+            or tuple(v_cache.shape) != tuple(k_cache.shape) or k_cache.shape[2] != num_kv_heads:
+        raise ValueError("inconsistent shapes")
+    row = q.numel() // T   # elements per token row
+    for t in (k_cache, v_cache, cos_cache, sin_cache):
+        if t is not None and t.dtype != q.dtype:
+            raise ValueError("all tensors share q's dtype")
+    if (cos_cache is None) != (sin_cache is None):
+        raise ValueError("cos_cache and sin_cache go together")
+    if sin_cache is not None and tuple(sin_cache.shape) != tuple(cos_cache.shape):
+        raise ValueError("cos_cache and sin_cache shapes differ")
+    max_pos, rdim = (0, 0) if cos_cache is None else (cos_cache.shape[0],
+                                                       2 * cos_cache.shape[1])
+    if out is None:
+        out = _alloc_on(stream, q, (T, num_heads, d), q.dtype)
+    elif out.numel() != T * num_heads * d or out.dtype != q.dtype:
+        raise ValueError("out must be [T, Hq, D] of q's dtype")
+    need = pa_attention_workspace_size(B, T, MB, num_heads, num_kv_heads, d, bs)
+    if workspace is None:
+        workspace = _alloc_on(stream, q, (max(need, 256),), torch.uint8)
+    opt = lambda t, n: None if t is None else _dev(t, n)  # noqa: E731
+    check(lib().pa_attention_rope(
+        _dev(q, "q"), row, opt(cos_cache, "cos_cache"), opt(sin_cache, "sin_cache"), max_pos,
+        rdim, 1 if interleaved else 0, _dev(cu_seqlens_q, "cu_seqlens_q", torch.int32),
+        _dev(seqlens_kv, "seqlens_kv", torch.int32), _dev(block_table, "block_table", torch.int32),
+        _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), _dev(out, "out"), B, T, MB, nb,
+        float(scale), float(softcap), int(local_window_size), num_heads, num_kv_heads, d, bs,
+        _dtype_code(q), _dev(workspace, "workspace"),
+        workspace.numel() * workspace.element_size(), _stream_ptr(q, stream)))
     return out
 
 

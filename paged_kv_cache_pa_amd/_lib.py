@@ -23,7 +23,8 @@ PROFILE_KINDS = ("scatter", "plan", "attention", "combine", "rotary")
 
 EXPORTS = ("pa_scatter_kv", "pa_scatter_kv_paged", "pa_scatter_kv_fp8", "pa_rotary_scatter_kv",
            "pa_seqlens_from_past",
-           "pa_attention_workspace_size", "pa_attention", "pa_attention_noalloc",
+           "pa_attention_workspace_size", "pa_attention", "pa_attention_rope",
+           "pa_attention_noalloc",
            "pa_attention_fp8",
            "pa_validate_metadata", "pa_status_string", "pa_last_error",
            "pa_profile_enable", "pa_profile_select", "pa_profile_read")
@@ -66,6 +67,10 @@ def lib():
     L.pa_attention.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i64, f32, f32, i32,
                                i32, i32, i32, i32, i32, vp, sz, vp]
     L.pa_attention.restype = i32
+    L.pa_attention_rope.argtypes = [vp, i64, vp, vp, i32, i32, i32, vp, vp, vp, vp, vp, vp, i32,
+                                    i64, i32, i64, f32, f32, i32, i32, i32, i32, i32, i32, vp, sz,
+                                    vp]
+    L.pa_attention_rope.restype = i32
     L.pa_attention_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i64, f32, f32,
                                        i32, i32, i32, i32, i32, i32, vp]
     L.pa_attention_noalloc.restype = i32

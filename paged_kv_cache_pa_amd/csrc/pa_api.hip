@@ -385,8 +385,11 @@ pa_status_t pa_rotary_scatter_kv(const void* query, const void* key, const void*
     if (max_position < 1) return fail(PA_ERR_INVALID_ARGUMENT, "max_position < 1");
   }
   if (num_tokens == 0) return PA_OK;
-  if (!query || !cu_seqlens_q || !seqlens_kv || !block_table || !q_out || !k_cache || !v_cache)
+  if (!cu_seqlens_q || !seqlens_kv || !block_table || !k_cache || !v_cache)
     return fail(PA_ERR_INVALID_ARGUMENT, "null pointer argument");
+  // Q is neither read nor written when q_out is null and K, V come apart.
+  if (!query && (q_out || !key))
+    return fail(PA_ERR_INVALID_ARGUMENT, "null query (allowed only with separate key/value and no q_out)");
   for (const void* ptr : {query, key, value, cos_cache, sin_cache, (const void*)q_out,
                           (const void*)k_cache, (const void*)v_cache})
     if (((uintptr_t)ptr & 15) != 0)
@@ -444,6 +447,15 @@ size_t pa_attention_workspace_size(int32_t num_seqs, int64_t num_tokens, int32_t
 
 // Shared by pa_attention (16-bit caches) and pa_attention_fp8 (kv8: e4m3
 // caches with per-channel scales, decode path only).
+// Where the attention reads Q: the row stride (elements between tokens) and
+// the rotary tables Q is rotated with as it is loaded (cos == nullptr: none).
+struct QSource {
+  int64_t row_stride;
+  const void* cos;
+  const void* sin;
+  int32_t max_position, rotary_dim, interleaved;
+};
+
 static pa_status_t attention_impl(const void* q, const int32_t* cu_seqlens_q,
                                   const int32_t* seqlens_kv, const int32_t* block_table,
                                   const void* k_cache, const void* v_cache, const float* k_scale,
@@ -453,7 +465,7 @@ static pa_status_t attention_impl(const void* q, const int32_t* cu_seqlens_q,
                                   int32_t local_window_size, int32_t num_heads,
                                   int32_t num_kv_heads, int32_t head_size, int32_t block_size,
                                   int32_t dtype, void* workspace, size_t workspace_bytes,
-                                  void* stream, bool kv8) {
+                                  void* stream, bool kv8, const QSource* qsrc = nullptr) {
   if (dtype != PA_F16 && dtype != PA_BF16)
     return fail(PA_ERR_NOT_IMPLEMENTED, "dtype=%d (supported: PA_F16, PA_BF16)", dtype);
   const pa::Shape s = make_shape(num_seqs, num_tokens, max_blocks_per_seq, num_heads,
@@ -548,6 +560,14 @@ static pa_status_t attention_impl(const void* q, const int32_t* cu_seqlens_q,
   a.split_keys = pl.split_keys;
   a.split_shift = pl.split_shift;
   a.force_prefill = pl.force_prefill;
+  a.q_stride = qsrc ? qsrc->row_stride : (int64_t)num_heads * head_size;
+  if (qsrc && qsrc->cos) {
+    a.rope_cos = qsrc->cos;
+    a.rope_sin = qsrc->sin;
+    a.rope_dim = qsrc->rotary_dim;
+    a.rope_inter = qsrc->interleaved ? 1 : 0;
+    a.rope_max_pos = qsrc->max_position;
+  }
 
   e = timed(2, st, [&] { return pa::launch_attention(a, dtype, head_size, workers, st, kv8); });
   if (e != hipSuccess) return hip_fail(e, "attention launch");
@@ -570,6 +590,41 @@ pa_status_t pa_attention(const void* q, const int32_t* cu_seqlens_q, const int32
                         nullptr, out, num_seqs, num_tokens, max_blocks_per_seq, num_blocks, scale,
                         softcap, local_window_size, num_heads, num_kv_heads, head_size, block_size, dtype, workspace,
                         workspace_bytes, stream, false);
+}
+
+pa_status_t pa_attention_rope(const void* q, int64_t q_row_stride, const void* cos_cache,
+                              const void* sin_cache, int32_t max_position, int32_t rotary_dim,
+                              int32_t interleaved, const int32_t* cu_seqlens_q,
+                              const int32_t* seqlens_kv, const int32_t* block_table,
+                              const void* k_cache, const void* v_cache, void* out,
+                              int32_t num_seqs, int64_t num_tokens, int32_t max_blocks_per_seq,
+                              int64_t num_blocks, float scale, float softcap,
+                              int32_t local_window_size, int32_t num_heads, int32_t num_kv_heads,
+                              int32_t head_size, int32_t block_size, int32_t dtype,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+  g_err[0] = 0;
+  if (num_heads >= 1 && head_size >= 1 && q_row_stride < (int64_t)num_heads * head_size)
+    return fail(PA_ERR_INVALID_ARGUMENT, "q_row_stride=%lld < num_heads * head_size",
+                (long long)q_row_stride);
+  if (q_row_stride % 8 != 0)
+    return fail(PA_ERR_INVALID_ARGUMENT, "q_row_stride=%lld is not a multiple of 8 (16-byte rows)",
+                (long long)q_row_stride);
+  if ((cos_cache == nullptr) != (sin_cache == nullptr))
+    return fail(PA_ERR_INVALID_ARGUMENT, "cos_cache and sin_cache must both be given or both be null");
+  if (cos_cache) {
+    if (rotary_dim < 1 || rotary_dim > head_size)
+      return fail(PA_ERR_INVALID_ARGUMENT, "rotary_dim=%d outside [1, head_size]", rotary_dim);
+    if (rotary_dim % 16 != 0)
+      return fail(PA_ERR_NOT_IMPLEMENTED, "rotary_dim=%d is not a multiple of 16", rotary_dim);
+    if (max_position < 1) return fail(PA_ERR_INVALID_ARGUMENT, "max_position < 1");
+    if (!aligned16({cos_cache, sin_cache}))
+      return fail(PA_ERR_INVALID_ARGUMENT, "tensor pointers must be 16-byte aligned");
+  }
+  const QSource qs{q_row_stride, cos_cache, sin_cache, max_position, rotary_dim, interleaved};
+  return attention_impl(q, cu_seqlens_q, seqlens_kv, block_table, k_cache, v_cache, nullptr,
+                        nullptr, out, num_seqs, num_tokens, max_blocks_per_seq, num_blocks, scale,
+                        softcap, local_window_size, num_heads, num_kv_heads, head_size,
+                        block_size, dtype, workspace, workspace_bytes, stream, false, &qs);
 }
 
 // ------------------------------------------------ allocation-free variant

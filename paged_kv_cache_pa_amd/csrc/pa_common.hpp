@@ -169,4 +169,61 @@ __device__ inline int div_small(int x, float inv_g) { return (int)(((float)x + 0
 __device__ inline u32x4_t ld16(const void* p) { return *reinterpret_cast<const u32x4_t*>(p); }
 __device__ inline u32x2_t ld8(const void* p) { return *reinterpret_cast<const u32x2_t*>(p); }
 
+// Rotary position embedding of one 16-byte chunk (8 elements), in fp32 with
+// one rounding into the element type: the rotary-scatter kernel and the
+// attention's rotated Q load use these same two functions, so both produce
+// the same bits.  Source: "[WebGPU] Initial PagedAttention implementation
+// (1/n)", the review's summary (interleaved and split pairing, the sign of
+// the rotation); the rotation is RoFormer's (Su et al., section 3.2).
+// Interleaved pairing: 4 pairs per chunk (word j holds pair j); cos / sin of
+// those 4 pairs in cw / sw.
+template <typename T>
+__device__ inline u32x4_t rope_interleaved(u32x4_t x, u32x2_t cw, u32x2_t sw) {
+  u32x4_t o;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const float2 p = Elt<T>::unpack2(x[j]);
+    const float2 c2 = Elt<T>::unpack2(cw[j >> 1]);
+    const float2 s2 = Elt<T>::unpack2(sw[j >> 1]);
+    const float c = (j & 1) ? c2.y : c2.x;
+    const float s = (j & 1) ? s2.y : s2.x;
+    o[j] = Elt<T>::pack2(p.x * c - p.y * s, p.y * c + p.x * s);
+  }
+  return o;
+}
+// Split pairing: this chunk x, its partner chunk y (rotary_dim / 2 elements
+// on or back), cos / sin of the 8 pairs; first half: x c - y s, second half:
+// x c + y s.
+template <typename T>
+__device__ inline u32x4_t rope_split(u32x4_t x, u32x4_t y, u32x4_t cw, u32x4_t sw,
+                                     bool first_half) {
+  const float sg = first_half ? -1.f : 1.f;
+  u32x4_t o;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const float2 a = Elt<T>::unpack2(x[j]);
+    const float2 b = Elt<T>::unpack2(y[j]);
+    const float2 c = Elt<T>::unpack2(cw[j]);
+    const float2 s = Elt<T>::unpack2(sw[j]);
+    o[j] = Elt<T>::pack2(a.x * c.x + sg * (b.x * s.x), a.y * c.y + sg * (b.y * s.y));
+  }
+  return o;
+}
+// Chunk x = row[e .. e+8) of a head row (16-bit elements, e a multiple of 8
+// below rdim, rdim a multiple of 16) rotated at position pos, the cos / sin
+// tables being [*, rdim / 2] rows of the element type.
+template <typename T>
+__device__ inline u32x4_t rope_chunk(u32x4_t x, const uint16_t* row, int e, int pos,
+                                     const uint16_t* cos_t, const uint16_t* sin_t, int rdim,
+                                     bool interleaved) {
+  const int half = rdim >> 1;
+  const uint16_t* crow = cos_t + (int64_t)pos * half;
+  const uint16_t* srow = sin_t + (int64_t)pos * half;
+  if (interleaved) return rope_interleaved<T>(x, ld8(crow + e / 2), ld8(srow + e / 2));
+  const bool first = e < half;
+  const int k = first ? e : e - half;
+  return rope_split<T>(x, ld16(row + (first ? e + half : e - half)), ld16(crow + k), ld16(srow + k),
+                       first);
+}
+
 }  // namespace pa

@@ -107,11 +107,22 @@ __device__ __forceinline__ void decode_items(const AttnArgs& a) {
       const int ng = div_small(n, a.inv_group);
       const int tok = si.cu + (valid ? ng : 0);
       const int h = kh * G + (valid ? n - ng * G : 0);
-      const uint16_t* qrow = qp + ((int64_t)tok * hq + h) * D;
+      const uint16_t* qrow = qp + (int64_t)tok * a.q_stride + (int64_t)h * D;
       if constexpr (!KV8) {
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
           qreg[s] = valid ? ld16(qrow + (4 * s + kq) * 8) : u32x4_t{0, 0, 0, 0};
+        }
+        // Q rotated as loaded (pa_attention_rope), at the token's position.
+        const int pos = past + ng;
+        if (a.rope_dim > 0 && valid && pos < a.rope_max_pos) {
+#pragma unroll
+          for (int s = 0; s < NS; ++s) {
+            const int e = (4 * s + kq) * 8;
+            if (e < a.rope_dim)
+              qreg[s] = rope_chunk<T>(qreg[s], qrow, e, pos, (const uint16_t*)a.rope_cos,
+                                      (const uint16_t*)a.rope_sin, a.rope_dim, a.rope_inter != 0);
+          }
         }
       } else {
         const float* ks = a.k_scale + (int64_t)kh * D;

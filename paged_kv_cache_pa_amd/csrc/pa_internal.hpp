@@ -131,6 +131,14 @@ struct AttnArgs {
   int32_t window;    // local_window_size W: row sees keys (limit - W, limit]; 0: off
   int32_t split_keys, split_shift;   // decode split length and its log2
   int32_t force_prefill;             // no sequence took the decode path (test override)
+  // Q rows: element (t, h, d) at q[t * q_stride + h * head_size + d]
+  // (q_stride = num_heads * head_size, or the packed QKV row).  rope_dim > 0:
+  // Q is rotated as it is loaded (rope_chunk) at its token's position, which
+  // must be below rope_max_pos (other rows are used unrotated).
+  int64_t q_stride;
+  const void* rope_cos;   // [rope_max_pos, rope_dim / 2] dtype
+  const void* rope_sin;
+  int32_t rope_dim, rope_inter, rope_max_pos;
 };
 
 // First decode split of a sequence with a sliding window: splits wholly

@@ -271,10 +271,20 @@ __device__ __forceinline__ void prefill_items(const AttnArgs& a) {
         const bool valid = row < TQ * G && ti < ql;
         const int head = kh * G + row - rg * G;
         limit[rho] = valid ? past + ti : -1;
-        const uint16_t* qrow = qp + ((int64_t)(valid ? si.cu + ti : 0) * hq + head) * D;
+        const uint16_t* qrow = qp + (int64_t)(valid ? si.cu + ti : 0) * a.q_stride + (int64_t)head * D;
 #pragma unroll
         for (int s = 0; s < NS; ++s)
           qreg[rho][s] = valid ? ld16(qrow + (4 * s + kq) * 8) : u32x4_t{0, 0, 0, 0};
+        // Q rotated as loaded (pa_attention_rope), at the token's position.
+        if (a.rope_dim > 0 && valid && past + ti < a.rope_max_pos) {
+#pragma unroll
+          for (int s = 0; s < NS; ++s) {
+            const int e = (4 * s + kq) * 8;
+            if (e < a.rope_dim)
+              qreg[rho][s] = rope_chunk<T>(qreg[rho][s], qrow, e, past + ti, (const uint16_t*)a.rope_cos,
+                                           (const uint16_t*)a.rope_sin, a.rope_dim, a.rope_inter != 0);
+          }
+        }
       }
       // Largest and smallest causal limit over this wave's rows
       // 32*wave .. 32*wave+31 (a padding row counts as -1), in closed form

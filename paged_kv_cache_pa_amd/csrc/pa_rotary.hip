@@ -1,7 +1,8 @@
 // The steps ahead of the attention for one batch of new tokens, in one pass:
 // split packed QKV rows, rotate Q and K by the rotary position embedding at
 // each token's KV position, write the rotated Q for the attention and the
-// rotated K and plain V into the paged caches.
+// rotated K and plain V into the paged caches (without a Q output, the Q
+// rows are skipped: pa_attention_rope rotates Q as it loads it).
 //
 // Sources: "[WebGPU] Initial PagedAttention implementation (1/n)", the file
 // summaries (a packed-QKV split program and a rotary program ahead of the
@@ -36,41 +37,6 @@ __device__ inline u32x4_t ld16_once(const uint16_t* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
 }
 __device__ inline u32x2_t ld8(const uint16_t* p) { return *reinterpret_cast<const u32x2_t*>(p); }
-
-// x rotated by the pairs' angles: interleaved pairing, 4 pairs per chunk
-// (word j holds pair j), cos / sin of those 4 pairs in cw / sw.
-template <typename T>
-__device__ inline u32x4_t rotate_interleaved(u32x4_t x, u32x2_t cw, u32x2_t sw) {
-  u32x4_t o;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const float2 p = Elt<T>::unpack2(x[j]);
-    const float2 c2 = Elt<T>::unpack2(cw[j >> 1]);
-    const float2 s2 = Elt<T>::unpack2(sw[j >> 1]);
-    const float c = (j & 1) ? c2.y : c2.x;
-    const float s = (j & 1) ? s2.y : s2.x;
-    o[j] = Elt<T>::pack2(p.x * c - p.y * s, p.y * c + p.x * s);
-  }
-  return o;
-}
-
-// Split pairing: this chunk x, its partner chunk y, cos / sin of the 8 pairs;
-// first half: x c - y s, second half: x c + y s.
-template <typename T>
-__device__ inline u32x4_t rotate_split(u32x4_t x, u32x4_t y, u32x4_t cw, u32x4_t sw,
-                                       bool first_half) {
-  const float sg = first_half ? -1.f : 1.f;
-  u32x4_t o;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const float2 a = Elt<T>::unpack2(x[j]);
-    const float2 b = Elt<T>::unpack2(y[j]);
-    const float2 c = Elt<T>::unpack2(cw[j]);
-    const float2 s = Elt<T>::unpack2(sw[j]);
-    o[j] = Elt<T>::pack2(a.x * c.x + sg * (b.x * s.x), a.y * c.y + sg * (b.y * s.y));
-  }
-  return o;
-}
 
 }  // namespace
 
@@ -115,7 +81,8 @@ __global__ __launch_bounds__(256) void rotary_scatter_kernel(RotaryArgs a) {
     const uint16_t* crow = cosp + (int64_t)pos * half;
     const uint16_t* srow = sinp + (int64_t)pos * half;
 
-    for (int c = lane; c < nchunks; c += 64) {
+    // Without q_out the Q rows are left to the attention's rotated Q load.
+    for (int c = lane + (qo == nullptr ? hq * cpr : 0); c < nchunks; c += 64) {
       const int r = c / cpr;                      // row: Q heads, K heads, V heads
       const int e = (c - r * cpr) * 8;            // first element of the chunk
       const uint16_t* src;
@@ -135,12 +102,12 @@ __global__ __launch_bounds__(256) void rotary_scatter_kernel(RotaryArgs a) {
       u32x4_t x = ld16_once(src + e);
       if (ROT && r < hq + hk && e < a.rotary_dim) {
         if constexpr (INTER) {
-          x = rotate_interleaved<T>(x, ld8(crow + e / 2), ld8(srow + e / 2));
+          x = rope_interleaved<T>(x, ld8(crow + e / 2), ld8(srow + e / 2));
         } else {
           const bool first = e < half;
           const int k = first ? e : e - half;      // pair index of the chunk's first element
           const u32x4_t y = ld16_once(src + (first ? e + half : e - half));
-          x = rotate_split<T>(x, y, ld16(crow + k), ld16(srow + k), first);
+          x = rope_split<T>(x, y, ld16(crow + k), ld16(srow + k), first);
         }
       }
       *reinterpret_cast<u32x4_t*>(dst + e) = x;

@@ -189,7 +189,7 @@ def _rot(L, **kw):
     (dict(rdim=80), _lib.PA_ERR_INVALID_ARGUMENT),        # beyond head_size
     (dict(maxpos=0), _lib.PA_ERR_INVALID_ARGUMENT),
     (dict(q=None), _lib.PA_ERR_INVALID_ARGUMENT),
-    (dict(qo=None), _lib.PA_ERR_INVALID_ARGUMENT),
+    (dict(kc=None), _lib.PA_ERR_INVALID_ARGUMENT),        # (q_out may be null: Q not written)
     (dict(table=None), _lib.PA_ERR_INVALID_ARGUMENT),
     (dict(qo=ctypes.c_void_p(0x1008)), _lib.PA_ERR_INVALID_ARGUMENT),   # unaligned
     (dict(cos=ctypes.c_void_p(0x1004)), _lib.PA_ERR_INVALID_ARGUMENT),  # unaligned
@@ -197,6 +197,43 @@ def _rot(L, **kw):
 def test_rotary_scatter_rejects_on_host(L, kw, status):
     assert _rot(L, **kw) == status
     assert L.pa_last_error() != b""
+
+
+def _attn_rope(L, **kw):
+    a = dict(q=FAKE, stride=8 * 64, cos=FAKE, sin=FAKE, maxpos=64, rdim=64, inter=0, cu=FAKE,
+             lens=FAKE, table=FAKE, kc=FAKE, vc=FAKE, out=FAKE, B=2, T=5, MB=2, NB=8,
+             scale=0.125, cap=0.0, win=0, hq=4, hk=2, d=64, bs=16, dtype=0, ws=FAKE, wsb=1 << 30)
+    a.update(kw)
+    return L.pa_attention_rope(a["q"], a["stride"], a["cos"], a["sin"], a["maxpos"], a["rdim"],
+                               a["inter"], a["cu"], a["lens"], a["table"], a["kc"], a["vc"],
+                               a["out"], a["B"], a["T"], a["MB"], a["NB"], a["scale"], a["cap"],
+                               a["win"], a["hq"], a["hk"], a["d"], a["bs"], a["dtype"], a["ws"],
+                               a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(stride=4 * 64 - 8), _lib.PA_ERR_INVALID_ARGUMENT),   # below num_heads * head_size
+    (dict(stride=4 * 64 + 4), _lib.PA_ERR_INVALID_ARGUMENT),   # rows not 16-byte aligned
+    (dict(sin=None), _lib.PA_ERR_INVALID_ARGUMENT),            # cos without sin
+    (dict(rdim=0), _lib.PA_ERR_INVALID_ARGUMENT),
+    (dict(rdim=80), _lib.PA_ERR_INVALID_ARGUMENT),             # beyond head_size
+    (dict(rdim=24), _lib.PA_ERR_NOT_IMPLEMENTED),              # not a multiple of 16
+    (dict(maxpos=0), _lib.PA_ERR_INVALID_ARGUMENT),
+    (dict(cos=ctypes.c_void_p(0x1004)), _lib.PA_ERR_INVALID_ARGUMENT),   # unaligned table
+    (dict(q=ctypes.c_void_p(0x1008)), _lib.PA_ERR_INVALID_ARGUMENT),     # unaligned q
+    (dict(d=96, stride=8 * 96), _lib.PA_ERR_NOT_IMPLEMENTED),  # pa_attention's own limits
+    (dict(wsb=16), _lib.PA_ERR_WORKSPACE_TOO_SMALL),
+    (dict(cap=-1.0), _lib.PA_ERR_INVALID_ARGUMENT),
+])
+def test_attention_rope_rejects_on_host(L, kw, status):
+    assert _attn_rope(L, **kw) == status
+    assert L.pa_last_error() != b""
+
+
+def test_attention_rope_empty_call_is_ok(L):
+    assert _attn_rope(L, T=0, q=None, out=None, ws=None) == _lib.PA_OK
+    # no tables: rotary_dim and max_position are not looked at
+    assert _attn_rope(L, T=0, cos=None, sin=None, rdim=0, maxpos=0) == _lib.PA_OK
 
 
 def test_rotary_scatter_empty_call_is_ok(L):
