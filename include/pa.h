@@ -317,8 +317,9 @@ size_t pa_attention_workspace_size(int32_t num_seqs, int64_t num_tokens,
  * and the split-KV partial rows each <= 2^30.  Other shapes return
  * PA_ERR_NOT_IMPLEMENTED (pa_attention_workspace_size returns 0 for them).
  * q, out and the caches must be 16-byte aligned (else
- * PA_ERR_INVALID_ARGUMENT).  num_tokens == 0 returns PA_OK without
- * launching.
+ * PA_ERR_INVALID_ARGUMENT), and out must not overlap q (else
+ * PA_ERR_INVALID_ARGUMENT: other work-groups still read q while out is
+ * written).  num_tokens == 0 returns PA_OK without launching.
  */
 pa_status_t pa_attention(const void* q, const int32_t* cu_seqlens_q,
                          const int32_t* seqlens_kv, const int32_t* block_table,
@@ -362,7 +363,7 @@ pa_status_t pa_attention(const void* q, const int32_t* cu_seqlens_q,
  * max_position >= 1 with tables.  A row whose position is >= max_position
  *              breaks a precondition and is used unrotated.
  * Every other argument, limit, status code and the empty call as for
- * pa_attention; q and out must not overlap.
+ * pa_attention; out must not overlap q's rows (else INVALID_ARGUMENT).
  */
 pa_status_t pa_attention_rope(const void* q, int64_t q_row_stride,
                               const void* cos_cache, const void* sin_cache,

@@ -489,6 +489,15 @@ static pa_status_t attention_impl(const void* q, const int32_t* cu_seqlens_q,
   if (kv8 && (!k_scale || !v_scale)) return fail(PA_ERR_INVALID_ARGUMENT, "null scale pointer");
   if (!aligned16({q, out, k_cache, v_cache}) || (kv8 && !aligned16({k_scale, v_scale})))
     return fail(PA_ERR_INVALID_ARGUMENT, "tensor pointers must be 16-byte aligned");
+  {
+    // out is written while other work-groups still read q: the two must not
+    // overlap (byte ranges of the rows each touches).
+    const int64_t row = qsrc ? qsrc->row_stride : (int64_t)num_heads * head_size;
+    const uintptr_t q0 = (uintptr_t)q, o0 = (uintptr_t)out;
+    const uintptr_t q1 = q0 + (uintptr_t)(((num_tokens - 1) * row + (int64_t)num_heads * head_size) * 2);
+    const uintptr_t o1 = o0 + (uintptr_t)(num_tokens * num_heads * head_size * 2);
+    if (q0 < o1 && o0 < q1) return fail(PA_ERR_INVALID_ARGUMENT, "q and out overlap");
+  }
   const pa::Layout L = pa::workspace_layout(s);
   if (!workspace) return fail(PA_ERR_INVALID_ARGUMENT, "null workspace");
   if (((uintptr_t)workspace & 255) != 0)

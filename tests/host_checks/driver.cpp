@@ -23,6 +23,7 @@ static void expect(pa_status_t got, pa_status_t want, const char* what) {
 static void* const P = (void*)(uintptr_t)0x1000;
 static const int32_t* const I = (const int32_t*)(uintptr_t)0x1000;
 static const float* const F = (const float*)(uintptr_t)0x1000;
+static void* const O = (void*)(uintptr_t)0x10000000;   // outputs, apart from every input range
 
 int main() {
   // Status strings and the error buffer.
@@ -94,38 +95,52 @@ int main() {
 
   // pa_attention: rejections, then the whole host path with a sized workspace.
   const size_t ws = pa_attention_workspace_size(2, 5, 2, 4, 2, 64, 16);
-  expect(pa_attention(P, I, I, I, P, P, P, 2, 5, 2, 8, 0.125f, -1.f, 0, 4, 2, 64, 16, PA_F16, P,
+  expect(pa_attention(P, I, I, I, P, P, O, 2, 5, 2, 8, 0.125f, -1.f, 0, 4, 2, 64, 16, PA_F16, P,
                       ws, nullptr),
          PA_ERR_INVALID_ARGUMENT, "attention negative softcap");
-  expect(pa_attention(P, I, I, I, P, P, P, 2, 5, 2, 8, 1e30f, 1e-40f, 0, 4, 2, 64, 16, PA_F16, P,
+  expect(pa_attention(P, I, I, I, P, P, O, 2, 5, 2, 8, 1e30f, 1e-40f, 0, 4, 2, 64, 16, PA_F16, P,
                       ws, nullptr),
          PA_ERR_INVALID_ARGUMENT, "attention scale/softcap overflow");
-  expect(pa_attention(P, I, I, I, P, P, P, 2, 5, 2, 8, 0.125f, 0.f, 0, 4, 3, 64, 16, PA_F16, P,
+  expect(pa_attention(P, I, I, I, P, P, O, 2, 5, 2, 8, 0.125f, 0.f, 0, 4, 3, 64, 16, PA_F16, P,
                       ws, nullptr),
          PA_ERR_INVALID_ARGUMENT, "attention Hq % Hk");
-  expect(pa_attention(P, I, I, I, P, P, P, 2, 5, 2, 8, 0.125f, 0.f, 0, 4, 2, 64, 16, PA_F16, P, 16,
+  expect(pa_attention(P, I, I, I, P, P, O, 2, 5, 2, 8, 0.125f, 0.f, 0, 4, 2, 64, 16, PA_F16, P, 16,
                       nullptr),
          PA_ERR_WORKSPACE_TOO_SMALL, "attention small workspace");
-  expect(pa_attention(P, I, I, I, P, P, P, 2, 5, 2, 8, 0.125f, 30.f, 128, 4, 2, 64, 16, PA_BF16,
+  expect(pa_attention(P, I, I, I, P, P, O, 2, 5, 2, 8, 0.125f, 30.f, 128, 4, 2, 64, 16, PA_BF16,
                       P, ws, nullptr),
          PA_ERR_HIP, "attention valid (stubbed launch)");
-  expect(pa_attention_fp8(P, I, I, I, P, P, F, F, P, 2, 5, 9, 2, 8, 0.125f, 0.f, 0, 4, 2, 64, 16,
+  expect(pa_attention_fp8(P, I, I, I, P, P, F, F, O, 2, 5, 9, 2, 8, 0.125f, 0.f, 0, 4, 2, 64, 16,
                           PA_F16, P, ws, nullptr),
          PA_ERR_NOT_IMPLEMENTED, "fp8 attention q_len * G > 16");
-  expect(pa_attention_fp8(P, I, I, I, P, P, F, F, P, 2, 5, 4, 2, 8, 0.125f, 0.f, 0, 4, 2, 64, 16,
+  expect(pa_attention_fp8(P, I, I, I, P, P, F, F, O, 2, 5, 4, 2, 8, 0.125f, 0.f, 0, 4, 2, 64, 16,
                           PA_F16, P, ws, nullptr),
          PA_ERR_HIP, "fp8 attention valid (stubbed launch)");
+
+  // pa_attention_rope: Q rows of the packed QKV stride, rotated on load.
+  expect(pa_attention_rope(P, 4 * 64 - 8, P, P, 64, 64, 0, I, I, I, P, P, O, 2, 5, 2, 8, 0.125f,
+                           0.f, 0, 4, 2, 64, 16, PA_F16, P, ws, nullptr),
+         PA_ERR_INVALID_ARGUMENT, "rope attention row stride below Hq * D");
+  expect(pa_attention_rope(P, 8 * 64, P, P, 64, 24, 0, I, I, I, P, P, O, 2, 5, 2, 8, 0.125f,
+                           0.f, 0, 4, 2, 64, 16, PA_F16, P, ws, nullptr),
+         PA_ERR_NOT_IMPLEMENTED, "rope attention rotary_dim 24");
+  expect(pa_attention_rope(P, 8 * 64, P, P, 64, 64, 0, I, I, I, P, P, P, 2, 5, 2, 8, 0.125f,
+                           0.f, 0, 4, 2, 64, 16, PA_F16, P, ws, nullptr),
+         PA_ERR_INVALID_ARGUMENT, "rope attention out overlapping q");
+  expect(pa_attention_rope(P, 8 * 64, P, P, 64, 64, 1, I, I, I, P, P, O, 2, 5, 2, 8, 0.125f,
+                           0.f, 0, 4, 2, 64, 16, PA_BF16, P, ws, nullptr),
+         PA_ERR_HIP, "rope attention valid (stubbed launch)");
 
   // Shapes at the kernels' 32-bit limits, and misaligned tensors.
   if (pa_attention_workspace_size(1, 8, 1, 8191, 8191, 128, 1024) == 0) ++g_failures;
   if (pa_attention_workspace_size(1, 8, 1, 8192, 8192, 128, 1024) != 0) ++g_failures;
   if (pa_attention_workspace_size(65536, 65536, 16384, 64, 64, 128, 16) == 0) ++g_failures;
   if (pa_attention_workspace_size(65536, 65536, 16384, 65, 65, 128, 16) != 0) ++g_failures;
-  expect(pa_attention(P, I, I, I, P, P, P, 65536, 5, 16384, 8, 0.125f, 0.f, 0, 65, 65, 128, 16,
+  expect(pa_attention(P, I, I, I, P, P, O, 65536, 5, 16384, 8, 0.125f, 0.f, 0, 65, 65, 128, 16,
                       PA_F16, P, ws, nullptr),
          PA_ERR_NOT_IMPLEMENTED, "attention decode items beyond 2^30");
   void* const P8 = (void*)(uintptr_t)0x1008;
-  expect(pa_attention(P8, I, I, I, P, P, P, 2, 5, 2, 8, 0.125f, 0.f, 0, 4, 2, 64, 16, PA_F16, P,
+  expect(pa_attention(P8, I, I, I, P, P, O, 2, 5, 2, 8, 0.125f, 0.f, 0, 4, 2, 64, 16, PA_F16, P,
                       ws, nullptr),
          PA_ERR_INVALID_ARGUMENT, "attention misaligned q");
   expect(pa_scatter_kv(P, P, I, P8, P, 5, 8, 2, 64, 16, PA_F16, nullptr),
@@ -133,10 +148,10 @@ int main() {
 
   // pa_attention_noalloc: rejections and the empty call return before any
   // HIP call (the scratch lookup needs a GPU).
-  expect(pa_attention_noalloc(P, I, I, I, P, P, P, 256, 8432, 2048, 500224, 0.088f, 0.f, 0, 64, 8,
+  expect(pa_attention_noalloc(P, I, I, I, P, P, O, 256, 8432, 2048, 500224, 0.088f, 0.f, 0, 64, 8,
                               128, 16, PA_BF16, nullptr),
          PA_ERR_WORKSPACE_TOO_SMALL, "noalloc workspace beyond the fixed scratch");
-  expect(pa_attention_noalloc(P, I, I, I, P, P, P, 2, 5, 2, 8, 0.125f, 0.f, 0, 4, 3, 64, 16,
+  expect(pa_attention_noalloc(P, I, I, I, P, P, O, 2, 5, 2, 8, 0.125f, 0.f, 0, 4, 3, 64, 16,
                               PA_F16, nullptr),
          PA_ERR_INVALID_ARGUMENT, "noalloc Hq % Hk");
   expect(pa_attention_noalloc(nullptr, I, I, I, P, P, nullptr, 2, 0, 2, 8, 0.125f, 0.f, 0, 4, 2,

@@ -58,10 +58,11 @@ def test_workspace_size_at_device_arithmetic_limits(L):
 
 
 FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: every call below fails before a launch
+FAKE_OUT = ctypes.c_void_p(0x10000000)   # an output range apart from every FAKE input
 
 
 def _attn(L, **kw):
-    a = dict(q=FAKE, cu=FAKE, lens=FAKE, table=FAKE, kc=FAKE, vc=FAKE, out=FAKE, B=2, T=5, MB=2,
+    a = dict(q=FAKE, cu=FAKE, lens=FAKE, table=FAKE, kc=FAKE, vc=FAKE, out=FAKE_OUT, B=2, T=5, MB=2,
              NB=8, scale=0.125, cap=0.0, win=0, hq=4, hk=2, d=64, bs=16, dtype=0, ws=FAKE, wsb=0,
              st=None)
     a.update(kw)
@@ -99,6 +100,8 @@ def _attn(L, **kw):
     (dict(q=ctypes.c_void_p(0x1008), wsb=1 << 30), _lib.PA_ERR_INVALID_ARGUMENT),  # q unaligned
     (dict(out=ctypes.c_void_p(0x1002), wsb=1 << 30), _lib.PA_ERR_INVALID_ARGUMENT),
     (dict(vc=ctypes.c_void_p(0x1004), wsb=1 << 30), _lib.PA_ERR_INVALID_ARGUMENT),
+    (dict(out=ctypes.c_void_p(0x1000 + 4 * 64 * 2), wsb=1 << 30),
+     _lib.PA_ERR_INVALID_ARGUMENT),   # out overlaps q (from q's second row)
 ])
 def test_attention_rejects_on_host(L, kw, status):
     assert _attn(L, **kw) == status
@@ -201,7 +204,7 @@ def test_rotary_scatter_rejects_on_host(L, kw, status):
 
 def _attn_rope(L, **kw):
     a = dict(q=FAKE, stride=8 * 64, cos=FAKE, sin=FAKE, maxpos=64, rdim=64, inter=0, cu=FAKE,
-             lens=FAKE, table=FAKE, kc=FAKE, vc=FAKE, out=FAKE, B=2, T=5, MB=2, NB=8,
+             lens=FAKE, table=FAKE, kc=FAKE, vc=FAKE, out=FAKE_OUT, B=2, T=5, MB=2, NB=8,
              scale=0.125, cap=0.0, win=0, hq=4, hk=2, d=64, bs=16, dtype=0, ws=FAKE, wsb=1 << 30)
     a.update(kw)
     return L.pa_attention_rope(a["q"], a["stride"], a["cos"], a["sin"], a["maxpos"], a["rdim"],
@@ -224,6 +227,7 @@ def _attn_rope(L, **kw):
     (dict(d=96, stride=8 * 96), _lib.PA_ERR_NOT_IMPLEMENTED),  # pa_attention's own limits
     (dict(wsb=16), _lib.PA_ERR_WORKSPACE_TOO_SMALL),
     (dict(cap=-1.0), _lib.PA_ERR_INVALID_ARGUMENT),
+    (dict(out=ctypes.c_void_p(0x1000 + 4 * 8 * 64 * 2)), _lib.PA_ERR_INVALID_ARGUMENT),  # in q's rows
 ])
 def test_attention_rope_rejects_on_host(L, kw, status):
     assert _attn_rope(L, **kw) == status
@@ -278,7 +282,7 @@ def test_scatter_fp8_empty_call_is_ok(L):
 
 
 def _attn8(L, **kw):
-    a = dict(q=FAKE, cu=FAKE, lens=FAKE, table=FAKE, kc=FAKE, vc=FAKE, ks=FAKE, vs=FAKE, out=FAKE,
+    a = dict(q=FAKE, cu=FAKE, lens=FAKE, table=FAKE, kc=FAKE, vc=FAKE, ks=FAKE, vs=FAKE, out=FAKE_OUT,
              B=2, T=5, mq=4, MB=2, NB=8, scale=0.125, cap=0.0, win=0, hq=4, hk=2, d=64, bs=16,
              dtype=0, ws=FAKE, wsb=0, st=None)
     a.update(kw)
@@ -326,7 +330,7 @@ def test_profile_kind_selection(L):
 
 
 def _noalloc(L, **kw):
-    a = dict(q=FAKE, cu=FAKE, lens=FAKE, table=FAKE, kc=FAKE, vc=FAKE, out=FAKE, B=2, T=5, MB=2,
+    a = dict(q=FAKE, cu=FAKE, lens=FAKE, table=FAKE, kc=FAKE, vc=FAKE, out=FAKE_OUT, B=2, T=5, MB=2,
              NB=8, scale=0.125, cap=0.0, win=0, hq=4, hk=2, d=64, bs=16, dtype=0, st=None)
     a.update(kw)
     return L.pa_attention_noalloc(a["q"], a["cu"], a["lens"], a["table"], a["kc"], a["vc"],
