@@ -351,8 +351,9 @@ pa_status_t pa_attention(const void* q, const int32_t* cu_seqlens_q,
  *              + d], dtype; for packed [num_tokens, num_heads + 2
  *              num_kv_heads, head_size] rows, q is the packed buffer and
  *              q_row_stride = (num_heads + 2 num_kv_heads) * head_size.
- * q_row_stride >= num_heads * head_size and a multiple of 8 (16-byte rows);
- *              else PA_ERR_INVALID_ARGUMENT.
+ * q_row_stride >= num_heads * head_size, a multiple of 8 (16-byte rows), and
+ *              num_tokens * q_row_stride <= 2^60; else
+ *              PA_ERR_INVALID_ARGUMENT.
  * cos_cache,
  * sin_cache    [max_position, rotary_dim / 2] dtype, 16-byte aligned, or
  *              both NULL (no rotation: pa_attention on strided Q rows).

@@ -618,6 +618,10 @@ pa_status_t pa_attention_rope(const void* q, int64_t q_row_stride, const void* c
   if (q_row_stride % 8 != 0)
     return fail(PA_ERR_INVALID_ARGUMENT, "q_row_stride=%lld is not a multiple of 8 (16-byte rows)",
                 (long long)q_row_stride);
+  // The byte range of q's rows must fit 62 bits (64-bit offsets, with room).
+  if (num_tokens > 0 && q_row_stride > ((int64_t)1 << 60) / num_tokens)
+    return fail(PA_ERR_INVALID_ARGUMENT, "q_row_stride=%lld: q's rows exceed the address range",
+                (long long)q_row_stride);
   if ((cos_cache == nullptr) != (sin_cache == nullptr))
     return fail(PA_ERR_INVALID_ARGUMENT, "cos_cache and sin_cache must both be given or both be null");
   if (cos_cache) {

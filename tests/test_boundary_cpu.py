@@ -217,6 +217,7 @@ def _attn_rope(L, **kw):
 @pytest.mark.parametrize("kw,status", [
     (dict(stride=4 * 64 - 8), _lib.PA_ERR_INVALID_ARGUMENT),   # below num_heads * head_size
     (dict(stride=4 * 64 + 4), _lib.PA_ERR_INVALID_ARGUMENT),   # rows not 16-byte aligned
+    (dict(stride=1 << 60), _lib.PA_ERR_INVALID_ARGUMENT),      # q's rows beyond 2^60 elements
     (dict(sin=None), _lib.PA_ERR_INVALID_ARGUMENT),            # cos without sin
     (dict(rdim=0), _lib.PA_ERR_INVALID_ARGUMENT),
     (dict(rdim=80), _lib.PA_ERR_INVALID_ARGUMENT),             # beyond head_size
