@@ -239,6 +239,44 @@ pa_status_t pa_rotary_scatter_kv(const void* query, const void* key,
                                  int32_t num_kv_heads, int32_t head_size,
                                  int32_t block_size, int32_t dtype, void* stream);
 
+
+/*
+ * pa_rotary_scatter_kv_fp8 - pa_rotary_scatter_kv into fp8 (e4m3) caches
+ * with per-channel scales (pa_scatter_kv_fp8's format).
+ *
+ * Defines: the rotary step of pa_rotary_scatter_kv (same pages and
+ * sections) ahead of the quantized KV cache of "[WebGPU] Initial
+ * PagedAttention implementation (1/n)", "Roadmap", phase 3.  Each K row is
+ * rotated and rounded to dtype exactly as pa_rotary_scatter_kv does, then it
+ * and each V row are quantized as pa_scatter_kv_fp8 quantizes: the cache
+ * codes are bitwise those of pa_rotary_scatter_kv into 16-bit caches
+ * followed by pa_scatter_kv_fp8 of the rotated rows.  Q (q_out) is written
+ * in dtype as by pa_rotary_scatter_kv, or skipped when q_out is NULL.
+ *
+ * k_scale,
+ * v_scale      [num_kv_heads, head_size] float32, 16-byte aligned.
+ * k_cache,
+ * v_cache      [num_blocks, block_size, num_kv_heads, head_size] uint8 e4m3
+ *              codes, updated in place.
+ * Every other argument, limit and status code as for pa_rotary_scatter_kv;
+ * a null scale pointer returns PA_ERR_INVALID_ARGUMENT.
+ */
+pa_status_t pa_rotary_scatter_kv_fp8(const void* query, const void* key,
+                                     const void* value, const void* cos_cache,
+                                     const void* sin_cache, int32_t max_position,
+                                     int32_t rotary_dim, int32_t interleaved,
+                                     const int32_t* cu_seqlens_q,
+                                     const int32_t* seqlens_kv,
+                                     const int32_t* block_table,
+                                     const float* k_scale, const float* v_scale,
+                                     void* q_out, void* k_cache, void* v_cache,
+                                     int32_t num_seqs, int64_t num_tokens,
+                                     int32_t max_blocks_per_seq,
+                                     int64_t num_blocks, int32_t num_heads,
+                                     int32_t num_kv_heads, int32_t head_size,
+                                     int32_t block_size, int32_t dtype,
+                                     void* stream);
+
 /*
  * pa_attention_workspace_size - bytes of device workspace pa_attention
  * needs for these host-known sizes (an upper bound over every metadata the

@@ -13,7 +13,7 @@ from ._lib import (PA_BF16, PA_F16, PROFILE_KINDS, PAError, check, lib)  # noqa:
 
 __all__ = ["pa_scatter_kv", "pa_scatter_kv_paged", "pa_scatter_kv_fp8", "pa_seqlens_from_past",
            "pa_attention", "pa_attention_rope", "pa_attention_noalloc", "pa_attention_fp8",
-           "pa_rotary_scatter_kv",
+           "pa_rotary_scatter_kv", "pa_rotary_scatter_kv_fp8",
            "pa_attention_workspace_size", "pa_validate_metadata", "profile_enable",
            "profile_read", "PAError"]
 
@@ -108,18 +108,11 @@ def pa_seqlens_from_past(cu_seqlens_q, past_seqlens, out=None, stream=None):
     return out
 
 
-def pa_rotary_scatter_kv(query, cu_seqlens_q, seqlens_kv, block_table, k_cache, v_cache,
-                         num_heads, num_kv_heads, key=None, value=None, cos_cache=None,
-                         sin_cache=None, interleaved=False, q_out=None, stream=None,
-                         write_q=True):
-    """Split packed QKV (``key``/``value`` None: ``query`` is [T, Hq + 2 Hk, D]
-    or [T, (Hq + 2 Hk) * D]), rotate Q and K at each token's KV position
-    with ``cos_cache``/``sin_cache`` [max_position, rotary_dim / 2] (None: no
-    rotation), write K/V into the caches at the block table's slots and
-    return the (rotated) Q [T, Hq, D].  ``write_q=False``: Q is not written
-    (returns None); pa_attention_rope rotates it as it loads it.  ``query``
-    may then be None when ``key``/``value`` are given (K/V only)."""
+def _rotary(query, cu_seqlens_q, seqlens_kv, block_table, k_cache, v_cache, num_heads,
+            num_kv_heads, key, value, cos_cache, sin_cache, interleaved, q_out, stream, write_q,
+            k_scale=None, v_scale=None):
     import torch
+    kv8 = k_scale is not None or v_scale is not None
     if query is None and (write_q or key is None):
         raise ValueError("query may be None only with key/value given and write_q=False")
     ref = query if query is not None else key
@@ -136,9 +129,18 @@ def pa_rotary_scatter_kv(query, cu_seqlens_q, seqlens_kv, block_table, k_cache, 
     elif (query is not None and query.numel() != T * num_heads * d) or key.numel() != T * hk * d \
             or value is None or value.numel() != T * hk * d:
         raise ValueError("inconsistent Q/K/V shapes")
-    for t in (key, value, k_cache, v_cache, cos_cache, sin_cache):
+    caches = () if kv8 else (k_cache, v_cache)
+    for t in (key, value, cos_cache, sin_cache) + caches:
         if t is not None and t.dtype != ref.dtype:
             raise ValueError("all tensors share the query's dtype")
+    if kv8:
+        if k_scale is None or v_scale is None:
+            raise ValueError("k_scale and v_scale go together")
+        if k_cache.dtype != torch.uint8 or v_cache.dtype != torch.uint8:
+            raise ValueError("fp8 caches hold uint8 e4m3 codes")
+        for t in (k_scale, v_scale):
+            if t.dtype != torch.float32 or t.numel() != hk * d:
+                raise ValueError("scales are float32 [Hk, D]")
     if (cos_cache is None) != (sin_cache is None):
         raise ValueError("cos_cache and sin_cache go together")
     max_pos, rdim = (0, 0) if cos_cache is None else (cos_cache.shape[0],
@@ -152,14 +154,47 @@ def pa_rotary_scatter_kv(query, cu_seqlens_q, seqlens_kv, block_table, k_cache, 
     elif q_out.numel() != T * num_heads * d or q_out.dtype != query.dtype:
         raise ValueError("q_out must be [T, Hq, D] of the query's dtype")
     opt = lambda t, n: None if t is None else _dev(t, n)  # noqa: E731
-    check(lib().pa_rotary_scatter_kv(
-        opt(query, "query"), opt(key, "key"), opt(value, "value"), opt(cos_cache, "cos_cache"),
-        opt(sin_cache, "sin_cache"), max_pos, rdim, 1 if interleaved else 0,
-        _dev(cu_seqlens_q, "cu_seqlens_q", torch.int32), _dev(seqlens_kv, "seqlens_kv", torch.int32),
-        _dev(block_table, "block_table", torch.int32), opt(q_out, "q_out"),
-        _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), B, T, MB, nb, num_heads, hk, d, bs,
-        _dtype_code(ref), _stream_ptr(ref, stream)))
+    common = (opt(query, "query"), opt(key, "key"), opt(value, "value"),
+              opt(cos_cache, "cos_cache"), opt(sin_cache, "sin_cache"), max_pos, rdim,
+              1 if interleaved else 0, _dev(cu_seqlens_q, "cu_seqlens_q", torch.int32),
+              _dev(seqlens_kv, "seqlens_kv", torch.int32),
+              _dev(block_table, "block_table", torch.int32))
+    tail = (opt(q_out, "q_out"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), B, T, MB, nb,
+            num_heads, hk, d, bs, _dtype_code(ref), _stream_ptr(ref, stream))
+    if kv8:
+        check(lib().pa_rotary_scatter_kv_fp8(*common, _dev(k_scale, "k_scale"),
+                                             _dev(v_scale, "v_scale"), *tail))
+    else:
+        check(lib().pa_rotary_scatter_kv(*common, *tail))
     return q_out
+
+
+def pa_rotary_scatter_kv(query, cu_seqlens_q, seqlens_kv, block_table, k_cache, v_cache,
+                         num_heads, num_kv_heads, key=None, value=None, cos_cache=None,
+                         sin_cache=None, interleaved=False, q_out=None, stream=None,
+                         write_q=True):
+    """Split packed QKV (``key``/``value`` None: ``query`` is [T, Hq + 2 Hk, D]
+    or [T, (Hq + 2 Hk) * D]), rotate Q and K at each token's KV position
+    with ``cos_cache``/``sin_cache`` [max_position, rotary_dim / 2] (None: no
+    rotation), write K/V into the caches at the block table's slots and
+    return the (rotated) Q [T, Hq, D].  ``write_q=False``: Q is not written
+    (returns None); pa_attention_rope rotates it as it loads it.  ``query``
+    may then be None when ``key``/``value`` are given (K/V only)."""
+    return _rotary(query, cu_seqlens_q, seqlens_kv, block_table, k_cache, v_cache, num_heads,
+                   num_kv_heads, key, value, cos_cache, sin_cache, interleaved, q_out, stream,
+                   write_q)
+
+
+def pa_rotary_scatter_kv_fp8(query, cu_seqlens_q, seqlens_kv, block_table, k_scale, v_scale,
+                             k_cache, v_cache, num_heads, num_kv_heads, key=None, value=None,
+                             cos_cache=None, sin_cache=None, interleaved=False, q_out=None,
+                             stream=None, write_q=True):
+    """pa_rotary_scatter_kv into fp8 (uint8 e4m3) caches with float32
+    per-channel scales [Hk, D]: the codes pa_scatter_kv_fp8 writes for the
+    rotated rows."""
+    return _rotary(query, cu_seqlens_q, seqlens_kv, block_table, k_cache, v_cache, num_heads,
+                   num_kv_heads, key, value, cos_cache, sin_cache, interleaved, q_out, stream,
+                   write_q, k_scale=k_scale, v_scale=v_scale)
 
 
 def pa_attention_workspace_size(num_seqs, num_tokens, max_blocks_per_seq, num_heads,

@@ -22,6 +22,7 @@ PA_BF16 = 1
 PROFILE_KINDS = ("scatter", "plan", "attention", "combine", "rotary")
 
 EXPORTS = ("pa_scatter_kv", "pa_scatter_kv_paged", "pa_scatter_kv_fp8", "pa_rotary_scatter_kv",
+           "pa_rotary_scatter_kv_fp8",
            "pa_seqlens_from_past",
            "pa_attention_workspace_size", "pa_attention", "pa_attention_rope",
            "pa_attention_noalloc",
@@ -60,6 +61,10 @@ def lib():
     L.pa_rotary_scatter_kv.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, vp, vp, vp, vp, vp, vp,
                                        i32, i64, i32, i64, i32, i32, i32, i32, i32, vp]
     L.pa_rotary_scatter_kv.restype = i32
+    L.pa_rotary_scatter_kv_fp8.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, vp, vp, vp, vp, vp,
+                                           vp, vp, vp, i32, i64, i32, i64, i32, i32, i32, i32,
+                                           i32, vp]
+    L.pa_rotary_scatter_kv_fp8.restype = i32
     L.pa_seqlens_from_past.argtypes = [vp, vp, vp, i32, vp]
     L.pa_seqlens_from_past.restype = i32
     L.pa_attention_workspace_size.argtypes = [i32, i64, i32, i32, i32, i32, i32]

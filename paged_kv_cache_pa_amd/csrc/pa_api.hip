@@ -348,16 +348,16 @@ pa_status_t pa_scatter_kv_paged(const void* k_new, const void* v_new, const int3
   return PA_OK;
 }
 
-pa_status_t pa_rotary_scatter_kv(const void* query, const void* key, const void* value,
-                                const void* cos_cache, const void* sin_cache,
-                                int32_t max_position, int32_t rotary_dim, int32_t interleaved,
-                                const int32_t* cu_seqlens_q, const int32_t* seqlens_kv,
-                                const int32_t* block_table, void* q_out, void* k_cache,
-                                void* v_cache, int32_t num_seqs, int64_t num_tokens,
-                                int32_t max_blocks_per_seq, int64_t num_blocks, int32_t num_heads,
-                                int32_t num_kv_heads, int32_t head_size, int32_t block_size,
-                                int32_t dtype, void* stream) {
-  g_err[0] = 0;
+static pa_status_t rotary_impl(const void* query, const void* key, const void* value,
+                               const void* cos_cache, const void* sin_cache, int32_t max_position,
+                               int32_t rotary_dim, int32_t interleaved,
+                               const int32_t* cu_seqlens_q, const int32_t* seqlens_kv,
+                               const int32_t* block_table, const float* k_scale,
+                               const float* v_scale, void* q_out, void* k_cache, void* v_cache,
+                               int32_t num_seqs, int64_t num_tokens, int32_t max_blocks_per_seq,
+                               int64_t num_blocks, int32_t num_heads, int32_t num_kv_heads,
+                               int32_t head_size, int32_t block_size, int32_t dtype, void* stream,
+                               bool kv8) {
   if (dtype != PA_F16 && dtype != PA_BF16)
     return fail(PA_ERR_NOT_IMPLEMENTED, "dtype=%d (supported: PA_F16, PA_BF16)", dtype);
   if (num_tokens < 0 || num_tokens > INT32_MAX)
@@ -387,11 +387,13 @@ pa_status_t pa_rotary_scatter_kv(const void* query, const void* key, const void*
   if (num_tokens == 0) return PA_OK;
   if (!cu_seqlens_q || !seqlens_kv || !block_table || !k_cache || !v_cache)
     return fail(PA_ERR_INVALID_ARGUMENT, "null pointer argument");
+  if (kv8 && (!k_scale || !v_scale)) return fail(PA_ERR_INVALID_ARGUMENT, "null scale pointer");
   // Q is neither read nor written when q_out is null and K, V come apart.
   if (!query && (q_out || !key))
     return fail(PA_ERR_INVALID_ARGUMENT, "null query (allowed only with separate key/value and no q_out)");
   for (const void* ptr : {query, key, value, cos_cache, sin_cache, (const void*)q_out,
-                          (const void*)k_cache, (const void*)v_cache})
+                          (const void*)k_cache, (const void*)v_cache, (const void*)k_scale,
+                          (const void*)v_scale})
     if (((uintptr_t)ptr & 15) != 0)
       return fail(PA_ERR_INVALID_ARGUMENT, "tensor pointers must be 16-byte aligned");
   pa::RotaryArgs a{};
@@ -406,6 +408,8 @@ pa_status_t pa_rotary_scatter_kv(const void* query, const void* key, const void*
   a.q_out = q_out;
   a.k_cache = k_cache;
   a.v_cache = v_cache;
+  a.k_scale = kv8 ? k_scale : nullptr;
+  a.v_scale = kv8 ? v_scale : nullptr;
   a.num_tokens = num_tokens;
   a.num_seqs = num_seqs;
   a.max_blocks = max_blocks_per_seq;
@@ -420,6 +424,40 @@ pa_status_t pa_rotary_scatter_kv(const void* query, const void* key, const void*
   hipError_t e = timed(4, st, [&] { return pa::launch_rotary_scatter(a, dtype, st); });
   if (e != hipSuccess) return hip_fail(e, "rotary scatter launch");
   return PA_OK;
+}
+
+pa_status_t pa_rotary_scatter_kv(const void* query, const void* key, const void* value,
+                                const void* cos_cache, const void* sin_cache,
+                                int32_t max_position, int32_t rotary_dim, int32_t interleaved,
+                                const int32_t* cu_seqlens_q, const int32_t* seqlens_kv,
+                                const int32_t* block_table, void* q_out, void* k_cache,
+                                void* v_cache, int32_t num_seqs, int64_t num_tokens,
+                                int32_t max_blocks_per_seq, int64_t num_blocks, int32_t num_heads,
+                                int32_t num_kv_heads, int32_t head_size, int32_t block_size,
+                                int32_t dtype, void* stream) {
+  g_err[0] = 0;
+  return rotary_impl(query, key, value, cos_cache, sin_cache, max_position, rotary_dim,
+                     interleaved, cu_seqlens_q, seqlens_kv, block_table, nullptr, nullptr, q_out,
+                     k_cache, v_cache, num_seqs, num_tokens, max_blocks_per_seq, num_blocks,
+                     num_heads, num_kv_heads, head_size, block_size, dtype, stream, false);
+}
+
+pa_status_t pa_rotary_scatter_kv_fp8(const void* query, const void* key, const void* value,
+                                    const void* cos_cache, const void* sin_cache,
+                                    int32_t max_position, int32_t rotary_dim,
+                                    int32_t interleaved, const int32_t* cu_seqlens_q,
+                                    const int32_t* seqlens_kv, const int32_t* block_table,
+                                    const float* k_scale, const float* v_scale, void* q_out,
+                                    void* k_cache, void* v_cache, int32_t num_seqs,
+                                    int64_t num_tokens, int32_t max_blocks_per_seq,
+                                    int64_t num_blocks, int32_t num_heads, int32_t num_kv_heads,
+                                    int32_t head_size, int32_t block_size, int32_t dtype,
+                                    void* stream) {
+  g_err[0] = 0;
+  return rotary_impl(query, key, value, cos_cache, sin_cache, max_position, rotary_dim,
+                     interleaved, cu_seqlens_q, seqlens_kv, block_table, k_scale, v_scale, q_out,
+                     k_cache, v_cache, num_seqs, num_tokens, max_blocks_per_seq, num_blocks,
+                     num_heads, num_kv_heads, head_size, block_size, dtype, stream, true);
 }
 
 pa_status_t pa_seqlens_from_past(const int32_t* cu_seqlens_q, const int32_t* past_seqlens,

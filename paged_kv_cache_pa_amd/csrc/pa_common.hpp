@@ -169,6 +169,33 @@ __device__ inline int div_small(int x, float inv_g) { return (int)(((float)x + 0
 __device__ inline u32x4_t ld16(const void* p) { return *reinterpret_cast<const u32x4_t*>(p); }
 __device__ inline u32x2_t ld8(const void* p) { return *reinterpret_cast<const u32x2_t*>(p); }
 
+// fp8 (OCP e4m3) code of one 16-byte chunk of 8 elements with per-channel
+// scales s0 (channels 0-3) and s1 (4-7): y = x * (1 / scale) in fp32, |y| >
+// 448 (infinities too) saturated to 448, NaN kept, rounded to nearest even by
+// v_cvt_pk_fp8_f32 (which alone would turn magnitudes above 464 into NaN).
+// The quantized KV cache of "[WebGPU] Initial PagedAttention implementation
+// (1/n)", "Roadmap", phase 3; the format is this library's reading.
+__device__ inline float sat_e4m3(float y) { return fabsf(y) > 448.f ? copysignf(448.f, y) : y; }
+
+template <typename T>
+__device__ inline u32x2_t quantize8(const u32x4_t x, const float4_t s0, const float4_t s1) {
+  float y[8];
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const float2 f = Elt<T>::unpack2(x[w]);
+    const float sa = w < 2 ? s0[2 * w] : s1[2 * w - 4];
+    const float sb = w < 2 ? s0[2 * w + 1] : s1[2 * w - 3];
+    y[2 * w] = sat_e4m3(f.x * (1.0f / sa));
+    y[2 * w + 1] = sat_e4m3(f.y * (1.0f / sb));
+  }
+  int lo = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
+  lo = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], lo, true);
+  int hi = __builtin_amdgcn_cvt_pk_fp8_f32(y[4], y[5], 0, false);
+  hi = __builtin_amdgcn_cvt_pk_fp8_f32(y[6], y[7], hi, true);
+  return u32x2_t{(uint32_t)lo, (uint32_t)hi};
+}
+
+
 // Rotary position embedding of one 16-byte chunk (8 elements), in fp32 with
 // one rounding into the element type: the rotary-scatter kernel and the
 // attention's rotated Q load use these same two functions, so both produce

@@ -170,9 +170,11 @@ struct RotaryArgs {
   const int32_t* cu;
   const int32_t* lens;
   const int32_t* table;
-  void* q_out;            // [T, Hq, D]
-  void* k_cache;
+  void* q_out;            // [T, Hq, D], or null (Q rows skipped)
+  void* k_cache;          // [NB, bs, Hk, D] dtype, or uint8 e4m3 codes with k_scale
   void* v_cache;
+  const float* k_scale;   // fp8 caches: [Hk, D] float32 per-channel scales; else null
+  const float* v_scale;
   int64_t num_tokens;
   int32_t num_seqs, max_blocks, block_size;
   int32_t num_heads, num_kv_heads, head_size;

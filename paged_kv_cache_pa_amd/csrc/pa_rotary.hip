@@ -1,8 +1,9 @@
 // The steps ahead of the attention for one batch of new tokens, in one pass:
 // split packed QKV rows, rotate Q and K by the rotary position embedding at
 // each token's KV position, write the rotated Q for the attention and the
-// rotated K and plain V into the paged caches (without a Q output, the Q
-// rows are skipped: pa_attention_rope rotates Q as it loads it).
+// rotated K and plain V into the paged caches (16-bit, or fp8 with
+// per-channel scales; without a Q output, the Q rows are skipped:
+// pa_attention_rope rotates Q as it loads it).
 //
 // Sources: "[WebGPU] Initial PagedAttention implementation (1/n)", the file
 // summaries (a packed-QKV split program and a rotary program ahead of the
@@ -40,7 +41,11 @@ __device__ inline u32x2_t ld8(const uint16_t* p) { return *reinterpret_cast<cons
 
 }  // namespace
 
-template <typename T, bool ROT, bool INTER>
+// KV8: fp8 (e4m3) caches with per-channel scales: each K chunk, rotated and
+// rounded to T as for 16-bit caches, and each V chunk are quantized by the
+// fp8 scatter's quantize8, so the codes are those pa_scatter_kv_fp8 writes
+// for the rotated rows.
+template <typename T, bool ROT, bool INTER, bool KV8>
 __global__ __launch_bounds__(256) void rotary_scatter_kernel(RotaryArgs a) {
   const int lane = threadIdx.x & 63;
   const int hq = a.num_heads, hk = a.num_kv_heads, hd = a.head_size;
@@ -54,8 +59,6 @@ __global__ __launch_bounds__(256) void rotary_scatter_kernel(RotaryArgs a) {
   const uint16_t* __restrict__ cosp = (const uint16_t*)a.cos_cache;
   const uint16_t* __restrict__ sinp = (const uint16_t*)a.sin_cache;
   uint16_t* __restrict__ qo = (uint16_t*)a.q_out;
-  uint16_t* __restrict__ kc = (uint16_t*)a.k_cache;
-  uint16_t* __restrict__ vc = (uint16_t*)a.v_cache;
   const bool packed = ksrc == nullptr;
   const int64_t nwaves = (int64_t)gridDim.x * (blockDim.x >> 6);
   for (int64_t t = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
@@ -86,18 +89,25 @@ __global__ __launch_bounds__(256) void rotary_scatter_kernel(RotaryArgs a) {
       const int r = c / cpr;                      // row: Q heads, K heads, V heads
       const int e = (c - r * cpr) * 8;            // first element of the chunk
       const uint16_t* src;
-      uint16_t* dst;
+      uint16_t* dst = nullptr;   // a Q row
+      void* cache = nullptr;     // or element cel of a cache
+      int64_t cel = 0;
+      const float* scale = nullptr;
       if (r < hq) {
         src = packed ? qsrc + (t * nrows + r) * hd : qsrc + (t * hq + r) * hd;
         dst = qo + (t * hq + r) * hd;
       } else if (r < hq + hk) {
         if (!write_kv) continue;
         src = packed ? qsrc + (t * nrows + r) * hd : ksrc + (t * hk + r - hq) * hd;
-        dst = kc + (slot * hk + r - hq) * hd;
+        cache = a.k_cache;
+        cel = (slot * hk + r - hq) * hd;
+        scale = a.k_scale + (int64_t)(r - hq) * hd;
       } else {
         if (!write_kv) continue;
         src = packed ? qsrc + (t * nrows + r) * hd : vsrc + (t * hk + r - hq - hk) * hd;
-        dst = vc + (slot * hk + r - hq - hk) * hd;
+        cache = a.v_cache;
+        cel = (slot * hk + r - hq - hk) * hd;
+        scale = a.v_scale + (int64_t)(r - hq - hk) * hd;
       }
       u32x4_t x = ld16_once(src + e);
       if (ROT && r < hq + hk && e < a.rotary_dim) {
@@ -110,30 +120,38 @@ __global__ __launch_bounds__(256) void rotary_scatter_kernel(RotaryArgs a) {
           x = rope_split<T>(x, y, ld16(crow + k), ld16(srow + k), first);
         }
       }
-      *reinterpret_cast<u32x4_t*>(dst + e) = x;
+      if (r < hq) {
+        *reinterpret_cast<u32x4_t*>(dst + e) = x;
+      } else if constexpr (KV8) {
+        const float4_t* sc = reinterpret_cast<const float4_t*>(scale + e);
+        *reinterpret_cast<u32x2_t*>((uint8_t*)cache + cel + e) = quantize8<T>(x, sc[0], sc[1]);
+      } else {
+        *reinterpret_cast<u32x4_t*>((uint16_t*)cache + cel + e) = x;
+      }
     }
   }
 }
 
-template <typename T>
+template <typename T, bool KV8>
 static void rotary_dispatch(const RotaryArgs& a, dim3 g, hipStream_t st) {
   const dim3 blk(256);
   if (a.cos_cache == nullptr)
-    hipLaunchKernelGGL((rotary_scatter_kernel<T, false, false>), g, blk, 0, st, a);
+    hipLaunchKernelGGL((rotary_scatter_kernel<T, false, false, KV8>), g, blk, 0, st, a);
   else if (a.interleaved)
-    hipLaunchKernelGGL((rotary_scatter_kernel<T, true, true>), g, blk, 0, st, a);
+    hipLaunchKernelGGL((rotary_scatter_kernel<T, true, true, KV8>), g, blk, 0, st, a);
   else
-    hipLaunchKernelGGL((rotary_scatter_kernel<T, true, false>), g, blk, 0, st, a);
+    hipLaunchKernelGGL((rotary_scatter_kernel<T, true, false, KV8>), g, blk, 0, st, a);
 }
 
 hipError_t launch_rotary_scatter(const RotaryArgs& a, int dtype, hipStream_t st) {
   int64_t blocks = (a.num_tokens + 3) / 4;   // 4 waves (tokens) per work-group
   if (blocks > 16384) blocks = 16384;
   const dim3 g((unsigned)blocks);
+  const bool kv8 = a.k_scale != nullptr;
   if (dtype == 0)
-    rotary_dispatch<F16>(a, g, st);
+    kv8 ? rotary_dispatch<F16, true>(a, g, st) : rotary_dispatch<F16, false>(a, g, st);
   else
-    rotary_dispatch<BF16>(a, g, st);
+    kv8 ? rotary_dispatch<BF16, true>(a, g, st) : rotary_dispatch<BF16, false>(a, g, st);
   return hipGetLastError();
 }
 

@@ -53,27 +53,8 @@ hipError_t launch_scatter(const void* k_new, const void* v_new, const int32_t* s
 // kept, then rounded to nearest even by v_cvt_pk_fp8_f32 (which alone would
 // turn magnitudes above 464 into NaN).  Each thread quantizes one chunk of
 // 8 elements: a 16-byte load of K and of V, two 16-byte scale loads each, and
-// an 8-byte store of codes per cache.
-__device__ inline float sat_e4m3(float y) { return fabsf(y) > 448.f ? copysignf(448.f, y) : y; }
-
-template <typename T>
-__device__ inline u32x2_t quantize8(const u32x4_t x, const float4_t s0, const float4_t s1) {
-  float y[8];
-#pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    const float2 f = Elt<T>::unpack2(x[w]);
-    const float sa = w < 2 ? s0[2 * w] : s1[2 * w - 4];
-    const float sb = w < 2 ? s0[2 * w + 1] : s1[2 * w - 3];
-    y[2 * w] = sat_e4m3(f.x * (1.0f / sa));
-    y[2 * w + 1] = sat_e4m3(f.y * (1.0f / sb));
-  }
-  int lo = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
-  lo = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], lo, true);
-  int hi = __builtin_amdgcn_cvt_pk_fp8_f32(y[4], y[5], 0, false);
-  hi = __builtin_amdgcn_cvt_pk_fp8_f32(y[6], y[7], hi, true);
-  return u32x2_t{(uint32_t)lo, (uint32_t)hi};
-}
-
+// an 8-byte store of codes per cache (quantize8, shared with the rotary
+// scatter into fp8 caches).
 template <typename T>
 __global__ __launch_bounds__(256) void scatter_fp8_kernel(
     const u32x4_t* __restrict__ k_new, const u32x4_t* __restrict__ v_new,

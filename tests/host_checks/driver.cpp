@@ -117,6 +117,14 @@ int main() {
                           PA_F16, P, ws, nullptr),
          PA_ERR_HIP, "fp8 attention valid (stubbed launch)");
 
+  // pa_rotary_scatter_kv_fp8: the rotary step into fp8 caches.
+  expect(pa_rotary_scatter_kv_fp8(P, P, P, P, P, 64, 64, 0, I, I, I, nullptr, F, O, P, P, 2, 5, 2,
+                                  8, 4, 2, 64, 16, PA_F16, nullptr),
+         PA_ERR_INVALID_ARGUMENT, "rotary fp8 null k_scale");
+  expect(pa_rotary_scatter_kv_fp8(P, P, P, P, P, 64, 64, 1, I, I, I, F, F, O, P, P, 2, 5, 2, 8, 4,
+                                  2, 64, 16, PA_BF16, nullptr),
+         PA_ERR_HIP, "rotary fp8 valid (stubbed launch)");
+
   // pa_attention_rope: Q rows of the packed QKV stride, rotated on load.
   expect(pa_attention_rope(P, 4 * 64 - 8, P, P, 64, 64, 0, I, I, I, P, P, O, 2, 5, 2, 8, 0.125f,
                            0.f, 0, 4, 2, 64, 16, PA_F16, P, ws, nullptr),

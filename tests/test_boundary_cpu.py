@@ -241,6 +241,35 @@ def test_attention_rope_empty_call_is_ok(L):
     assert _attn_rope(L, T=0, cos=None, sin=None, rdim=0, maxpos=0) == _lib.PA_OK
 
 
+def _rot8(L, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, cos=FAKE, sin=FAKE, maxpos=64, rdim=64, inter=0, cu=FAKE,
+             lens=FAKE, table=FAKE, ks=FAKE, vs=FAKE, qo=FAKE_OUT, kc=FAKE, vc=FAKE, B=2, T=5, MB=2,
+             NB=8, hq=4, hk=2, d=64, bs=16, dtype=0)
+    a.update(kw)
+    return L.pa_rotary_scatter_kv_fp8(a["q"], a["k"], a["v"], a["cos"], a["sin"], a["maxpos"],
+                                      a["rdim"], a["inter"], a["cu"], a["lens"], a["table"],
+                                      a["ks"], a["vs"], a["qo"], a["kc"], a["vc"], a["B"], a["T"],
+                                      a["MB"], a["NB"], a["hq"], a["hk"], a["d"], a["bs"],
+                                      a["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(ks=None), _lib.PA_ERR_INVALID_ARGUMENT),
+    (dict(vs=None), _lib.PA_ERR_INVALID_ARGUMENT),
+    (dict(vs=ctypes.c_void_p(0x1004)), _lib.PA_ERR_INVALID_ARGUMENT),   # unaligned scales
+    (dict(rdim=24), _lib.PA_ERR_NOT_IMPLEMENTED),
+    (dict(d=60), _lib.PA_ERR_NOT_IMPLEMENTED),
+    (dict(q=None), _lib.PA_ERR_INVALID_ARGUMENT),        # Q needed: q_out given
+])
+def test_rotary_scatter_fp8_rejects_on_host(L, kw, status):
+    assert _rot8(L, **kw) == status
+    assert L.pa_last_error() != b""
+
+
+def test_rotary_scatter_fp8_empty_call_is_ok(L):
+    assert _rot8(L, T=0, q=None, qo=None) == _lib.PA_OK
+
+
 def test_rotary_scatter_empty_call_is_ok(L):
     assert _rot(L, T=0, q=None, qo=None) == _lib.PA_OK
     # no tables: rotary_dim and max_position are not looked at
