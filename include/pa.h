@@ -487,6 +487,42 @@ pa_status_t pa_scatter_kv_fp8(const void* k_new, const void* v_new,
                               int32_t block_size, int32_t dtype, void* stream);
 
 /*
+ * pa_scatter_kv_paged_fp8 - pa_scatter_kv_fp8 with each new token's slot
+ * computed on the device from the batch metadata, as pa_scatter_kv_paged
+ * computes it.
+ *
+ * Defines: the slot derivation of "[WebGPU] Initial PagedAttention
+ * implementation (1/n)", section "Description" (slots from the cumulative
+ * query lengths, the past lengths and the block table), into the quantized
+ * cache of section "Roadmap" (phase 3).  For new token t the slot s is
+ * pa_scatter_kv_paged's; the codes written at s are pa_scatter_kv_fp8's
+ * (same quantization, same per-channel scales).  A negative table entry
+ * skips the token.
+ *
+ * k_new, v_new, cu_seqlens_q, seqlens_kv, block_table
+ *                as for pa_scatter_kv_paged.
+ * k_scale,
+ * v_scale        as for pa_scatter_kv_fp8 (16-byte aligned).
+ * k_cache,
+ * v_cache        [num_blocks, block_size, num_kv_heads, head_size] uint8
+ *                e4m3 codes, updated in place.
+ * Limits, status codes and empty calls as for pa_scatter_kv_paged; null or
+ * misaligned scales are PA_ERR_INVALID_ARGUMENT.  Bit-exact: the caches
+ * equal pa_scatter_kv_fp8's with the slots pa_scatter_kv_paged derives.
+ */
+pa_status_t pa_scatter_kv_paged_fp8(const void* k_new, const void* v_new,
+                                    const int32_t* cu_seqlens_q,
+                                    const int32_t* seqlens_kv,
+                                    const int32_t* block_table,
+                                    const float* k_scale, const float* v_scale,
+                                    void* k_cache, void* v_cache,
+                                    int32_t num_seqs, int64_t num_tokens,
+                                    int32_t max_blocks_per_seq,
+                                    int64_t num_blocks, int32_t num_kv_heads,
+                                    int32_t head_size, int32_t block_size,
+                                    int32_t dtype, void* stream);
+
+/*
  * pa_attention_fp8 - pa_attention over fp8 caches written by
  * pa_scatter_kv_fp8, for decode-shaped batches.
  *
@@ -521,6 +557,47 @@ pa_status_t pa_attention_fp8(const void* q, const int32_t* cu_seqlens_q,
                              int32_t num_heads, int32_t num_kv_heads,
                              int32_t head_size, int32_t block_size, int32_t dtype,
                              void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * pa_attention_rope_fp8 - pa_attention_fp8 with Q read from strided (for
+ * example packed QKV) rows and rotated as it is loaded, as
+ * pa_attention_rope does over 16-bit caches.
+ *
+ * Defines: the rotary program that runs just ahead of the attention in
+ * "[WebGPU] Initial PagedAttention implementation (1/n)" (the file
+ * summaries: a packed-QKV split and a rotary program ahead of the scatter;
+ * the review's summary: interleaved or split pairing, pass-through of
+ * dimensions >= rotary_dim), fused into the Q load of the quantized-cache
+ * attention of section "Roadmap" (phase 3).  The rotation is
+ * pa_attention_rope's (position p = past_b + i, fp32 arithmetic rounded
+ * once to dtype), applied before the K scale is folded into Q, so the
+ * result is bitwise that of pa_rotary_scatter_kv_fp8 with a q_out followed
+ * by pa_attention_fp8 on q_out.
+ *
+ * q, q_row_stride, cos_cache, sin_cache, rotary_dim, interleaved,
+ * max_position   as for pa_attention_rope.
+ * Every other argument (k_scale, v_scale, max_q_len included), limit,
+ * status code and the empty call as for pa_attention_fp8; out must not
+ * overlap q's rows (else PA_ERR_INVALID_ARGUMENT).
+ */
+pa_status_t pa_attention_rope_fp8(const void* q, int64_t q_row_stride,
+                                  const void* cos_cache, const void* sin_cache,
+                                  int32_t max_position, int32_t rotary_dim,
+                                  int32_t interleaved,
+                                  const int32_t* cu_seqlens_q,
+                                  const int32_t* seqlens_kv,
+                                  const int32_t* block_table,
+                                  const void* k_cache, const void* v_cache,
+                                  const float* k_scale, const float* v_scale,
+                                  void* out, int32_t num_seqs,
+                                  int64_t num_tokens, int32_t max_q_len,
+                                  int32_t max_blocks_per_seq,
+                                  int64_t num_blocks, float scale,
+                                  float softcap, int32_t local_window_size,
+                                  int32_t num_heads, int32_t num_kv_heads,
+                                  int32_t head_size, int32_t block_size,
+                                  int32_t dtype, void* workspace,
+                                  size_t workspace_bytes, void* stream);
 
 /*
  * pa_validate_metadata - debug/test check of the device metadata that

@@ -11,8 +11,9 @@ import ctypes
 
 from ._lib import (PA_BF16, PA_F16, PROFILE_KINDS, PAError, check, lib)  # noqa: F401
 
-__all__ = ["pa_scatter_kv", "pa_scatter_kv_paged", "pa_scatter_kv_fp8", "pa_seqlens_from_past",
-           "pa_attention", "pa_attention_rope", "pa_attention_noalloc", "pa_attention_fp8",
+__all__ = ["pa_scatter_kv", "pa_scatter_kv_paged", "pa_scatter_kv_fp8", "pa_scatter_kv_paged_fp8",
+           "pa_seqlens_from_past", "pa_attention", "pa_attention_rope", "pa_attention_noalloc",
+           "pa_attention_fp8", "pa_attention_rope_fp8",
            "pa_rotary_scatter_kv", "pa_rotary_scatter_kv_fp8",
            "pa_attention_workspace_size", "pa_validate_metadata", "profile_enable",
            "profile_read", "PAError"]
@@ -345,6 +346,30 @@ def pa_scatter_kv_fp8(k_new, v_new, slot_mapping, k_scale, v_scale, k_cache, v_c
         _dtype_code(k_new), _stream_ptr(k_cache, stream)))
 
 
+def pa_scatter_kv_paged_fp8(k_new, v_new, cu_seqlens_q, seqlens_kv, block_table, k_scale,
+                            v_scale, k_cache, v_cache, stream=None):
+    """pa_scatter_kv_fp8 with the slots derived on the GPU as
+    pa_scatter_kv_paged derives them: token t of sequence b is quantized
+    into KV position past_b + (t - cu[b]) of b's block-table row."""
+    import torch
+    T, hk, d = k_new.shape
+    nb, bs = k_cache.shape[0], k_cache.shape[1]
+    B = cu_seqlens_q.shape[0] - 1
+    if tuple(v_new.shape) != (T, hk, d) or tuple(k_cache.shape) != (nb, bs, hk, d) \
+            or tuple(v_cache.shape) != (nb, bs, hk, d) or seqlens_kv.shape != (B,) \
+            or block_table.dim() != 2 or block_table.shape[0] != B \
+            or tuple(k_scale.shape) != (hk, d) or tuple(v_scale.shape) != (hk, d):
+        raise ValueError("inconsistent shapes")
+    if k_new.dtype != v_new.dtype or k_cache.dtype != torch.uint8 or v_cache.dtype != torch.uint8:
+        raise ValueError("K/V share one 16-bit dtype; the caches hold uint8 codes")
+    check(lib().pa_scatter_kv_paged_fp8(
+        _dev(k_new, "k_new"), _dev(v_new, "v_new"), _dev(cu_seqlens_q, "cu_seqlens_q", torch.int32),
+        _dev(seqlens_kv, "seqlens_kv", torch.int32), _dev(block_table, "block_table", torch.int32),
+        _dev(k_scale, "k_scale", torch.float32), _dev(v_scale, "v_scale", torch.float32),
+        _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), B, T, block_table.shape[1], nb, hk, d,
+        bs, _dtype_code(k_new), _stream_ptr(k_cache, stream)))
+
+
 def pa_attention_fp8(q, cu_seqlens_q, seqlens_kv, block_table, k_cache, v_cache, k_scale,
                      v_scale, scale, num_heads, num_kv_heads, max_q_len, out=None,
                      workspace=None, stream=None, softcap=0.0, local_window_size=0):
@@ -380,6 +405,59 @@ def pa_attention_fp8(q, cu_seqlens_q, seqlens_kv, block_table, k_cache, v_cache,
         _dev(out, "out"), B, T, int(max_q_len), MB, nb, float(scale), float(softcap),
         int(local_window_size), num_heads, num_kv_heads, d, bs, _dtype_code(q), _dev(workspace, "workspace"),
         workspace.numel() * workspace.element_size(), _stream_ptr(q, stream)))
+    return out
+
+
+def pa_attention_rope_fp8(q, cu_seqlens_q, seqlens_kv, block_table, k_cache, v_cache, k_scale,
+                          v_scale, scale, num_heads, num_kv_heads, max_q_len, cos_cache=None,
+                          sin_cache=None, interleaved=False, out=None, workspace=None,
+                          stream=None, softcap=0.0, local_window_size=0):
+    """pa_attention_fp8 with Q read from rows of [T, H', D] (H' >= Hq; packed
+    QKV rows [T, Hq + 2 Hk, D]) and rotated as it is loaded, as in
+    pa_attention_rope.  Returns out [T, Hq, D], bitwise pa_attention_fp8 on
+    pa_rotary_scatter_kv_fp8's Q."""
+    import torch
+    T = q.shape[0]
+    d = k_cache.shape[-1]
+    nb, bs = k_cache.shape[0], k_cache.shape[1]
+    B = seqlens_kv.shape[0]
+    MB = block_table.shape[1]
+    if q.numel() % (T * d) != 0 or q.numel() // (T * d) < num_heads \
+            or cu_seqlens_q.shape != (B + 1,) or block_table.shape[0] != B \
+            or tuple(v_cache.shape) != tuple(k_cache.shape) or k_cache.shape[2] != num_kv_heads \
+            or tuple(k_scale.shape) != (num_kv_heads, d) \
+            or tuple(v_scale.shape) != (num_kv_heads, d):
+        raise ValueError("inconsistent shapes")
+    if k_cache.dtype != torch.uint8 or v_cache.dtype != torch.uint8:
+        raise ValueError("fp8 caches hold uint8 codes")
+    row = q.numel() // T   # elements per token row
+    for t in (cos_cache, sin_cache):
+        if t is not None and t.dtype != q.dtype:
+            raise ValueError("the rotary tables share q's dtype")
+    if (cos_cache is None) != (sin_cache is None):
+        raise ValueError("cos_cache and sin_cache go together")
+    if sin_cache is not None and tuple(sin_cache.shape) != tuple(cos_cache.shape):
+        raise ValueError("cos_cache and sin_cache shapes differ")
+    max_pos, rdim = (0, 0) if cos_cache is None else (cos_cache.shape[0],
+                                                       2 * cos_cache.shape[1])
+    if out is None:
+        out = _alloc_on(stream, q, (T, num_heads, d), q.dtype)
+    elif out.numel() != T * num_heads * d or out.dtype != q.dtype:
+        raise ValueError("out must be [T, Hq, D] of q's dtype")
+    need = pa_attention_workspace_size(B, T, MB, num_heads, num_kv_heads, d, bs)
+    if workspace is None:
+        workspace = _alloc_on(stream, q, (max(need, 256),), torch.uint8)
+    opt = lambda t, n: None if t is None else _dev(t, n)  # noqa: E731
+    check(lib().pa_attention_rope_fp8(
+        _dev(q, "q"), row, opt(cos_cache, "cos_cache"), opt(sin_cache, "sin_cache"), max_pos,
+        rdim, 1 if interleaved else 0, _dev(cu_seqlens_q, "cu_seqlens_q", torch.int32),
+        _dev(seqlens_kv, "seqlens_kv", torch.int32), _dev(block_table, "block_table", torch.int32),
+        _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+        _dev(k_scale, "k_scale", torch.float32), _dev(v_scale, "v_scale", torch.float32),
+        _dev(out, "out"), B, T, int(max_q_len), MB, nb, float(scale), float(softcap),
+        int(local_window_size), num_heads, num_kv_heads, d, bs, _dtype_code(q),
+        _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+        _stream_ptr(q, stream)))
     return out
 
 

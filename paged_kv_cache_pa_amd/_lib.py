@@ -21,12 +21,13 @@ PA_F16 = 0
 PA_BF16 = 1
 PROFILE_KINDS = ("scatter", "plan", "attention", "combine", "rotary")
 
-EXPORTS = ("pa_scatter_kv", "pa_scatter_kv_paged", "pa_scatter_kv_fp8", "pa_rotary_scatter_kv",
+EXPORTS = ("pa_scatter_kv", "pa_scatter_kv_paged", "pa_scatter_kv_fp8", "pa_scatter_kv_paged_fp8",
+           "pa_rotary_scatter_kv",
            "pa_rotary_scatter_kv_fp8",
            "pa_seqlens_from_past",
            "pa_attention_workspace_size", "pa_attention", "pa_attention_rope",
            "pa_attention_noalloc",
-           "pa_attention_fp8",
+           "pa_attention_fp8", "pa_attention_rope_fp8",
            "pa_validate_metadata", "pa_status_string", "pa_last_error",
            "pa_profile_enable", "pa_profile_select", "pa_profile_read")
 
@@ -56,6 +57,9 @@ def lib():
     L.pa_scatter_kv_paged.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i64, i32, i32,
                                       i32, i32, vp]
     L.pa_scatter_kv_paged.restype = i32
+    L.pa_scatter_kv_paged_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i64,
+                                          i32, i32, i32, i32, vp]
+    L.pa_scatter_kv_paged_fp8.restype = i32
     L.pa_scatter_kv_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i32, i32, i32, i32, vp]
     L.pa_scatter_kv_fp8.restype = i32
     L.pa_rotary_scatter_kv.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, vp, vp, vp, vp, vp, vp,
@@ -82,6 +86,10 @@ def lib():
     L.pa_attention_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i64,
                                    f32, f32, i32, i32, i32, i32, i32, i32, vp, sz, vp]
     L.pa_attention_fp8.restype = i32
+    L.pa_attention_rope_fp8.argtypes = [vp, i64, vp, vp, i32, i32, i32, vp, vp, vp, vp, vp, vp,
+                                        vp, vp, i32, i64, i32, i32, i64, f32, f32, i32, i32, i32,
+                                        i32, i32, i32, vp, sz, vp]
+    L.pa_attention_rope_fp8.restype = i32
     L.pa_validate_metadata.argtypes = [vp, vp, vp, vp, i32, i64, i32, i64, i32,
                                        ctypes.POINTER(ctypes.c_uint32), vp]
     L.pa_validate_metadata.restype = i32

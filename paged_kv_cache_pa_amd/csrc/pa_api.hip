@@ -310,13 +310,14 @@ pa_status_t pa_scatter_kv_fp8(const void* k_new, const void* v_new, const int32_
   return PA_OK;
 }
 
-pa_status_t pa_scatter_kv_paged(const void* k_new, const void* v_new, const int32_t* cu_seqlens_q,
-                                const int32_t* seqlens_kv, const int32_t* block_table,
-                                void* k_cache, void* v_cache, int32_t num_seqs,
-                                int64_t num_tokens, int32_t max_blocks_per_seq, int64_t num_blocks,
-                                int32_t num_kv_heads, int32_t head_size, int32_t block_size,
-                                int32_t dtype, void* stream) {
-  g_err[0] = 0;
+static pa_status_t scatter_paged_impl(const void* k_new, const void* v_new,
+                                      const int32_t* cu_seqlens_q, const int32_t* seqlens_kv,
+                                      const int32_t* block_table, const float* k_scale,
+                                      const float* v_scale, void* k_cache, void* v_cache,
+                                      int32_t num_seqs, int64_t num_tokens,
+                                      int32_t max_blocks_per_seq, int64_t num_blocks,
+                                      int32_t num_kv_heads, int32_t head_size,
+                                      int32_t block_size, int32_t dtype, void* stream, bool kv8) {
   if (dtype != PA_F16 && dtype != PA_BF16)
     return fail(PA_ERR_NOT_IMPLEMENTED, "dtype=%d (supported: PA_F16, PA_BF16)", dtype);
   if (num_tokens < 0 || num_tokens > INT32_MAX)
@@ -331,21 +332,49 @@ pa_status_t pa_scatter_kv_paged(const void* k_new, const void* v_new, const int3
     return fail(PA_ERR_NOT_IMPLEMENTED, "num_blocks * block_size exceeds INT32_MAX");
   if ((int64_t)max_blocks_per_seq * block_size > INT32_MAX)
     return fail(PA_ERR_NOT_IMPLEMENTED, "max_blocks_per_seq * block_size exceeds INT32_MAX");
-  const int64_t row_bytes = (int64_t)num_kv_heads * head_size * 2;
-  if (row_bytes > INT32_MAX) return fail(PA_ERR_NOT_IMPLEMENTED, "row too large");
+  const int64_t row_elems = (int64_t)num_kv_heads * head_size;
+  if (row_elems * 2 > INT32_MAX) return fail(PA_ERR_NOT_IMPLEMENTED, "row too large");
   if (num_tokens == 0) return PA_OK;
   if (!k_new || !v_new || !cu_seqlens_q || !seqlens_kv || !block_table || !k_cache || !v_cache)
     return fail(PA_ERR_INVALID_ARGUMENT, "null pointer argument");
-  if (!aligned16({k_new, v_new, k_cache, v_cache}))
+  if (kv8 && (!k_scale || !v_scale)) return fail(PA_ERR_INVALID_ARGUMENT, "null scale pointer");
+  if (!aligned16({k_new, v_new, k_cache, v_cache}) || (kv8 && !aligned16({k_scale, v_scale})))
     return fail(PA_ERR_INVALID_ARGUMENT, "tensor pointers must be 16-byte aligned");
   hipStream_t st = (hipStream_t)stream;
   hipError_t e = timed(0, st, [&] {
     return pa::launch_scatter_paged(k_new, v_new, cu_seqlens_q, seqlens_kv, block_table, k_cache,
-                                    v_cache, num_seqs, num_tokens, max_blocks_per_seq, block_size,
-                                    (int32_t)row_bytes, st);
+                                    v_cache, k_scale, v_scale, num_seqs, num_tokens,
+                                    max_blocks_per_seq, block_size, (int32_t)row_elems, dtype,
+                                    kv8, st);
   });
   if (e != hipSuccess) return hip_fail(e, "scatter launch");
   return PA_OK;
+}
+
+pa_status_t pa_scatter_kv_paged(const void* k_new, const void* v_new, const int32_t* cu_seqlens_q,
+                                const int32_t* seqlens_kv, const int32_t* block_table,
+                                void* k_cache, void* v_cache, int32_t num_seqs,
+                                int64_t num_tokens, int32_t max_blocks_per_seq, int64_t num_blocks,
+                                int32_t num_kv_heads, int32_t head_size, int32_t block_size,
+                                int32_t dtype, void* stream) {
+  g_err[0] = 0;
+  return scatter_paged_impl(k_new, v_new, cu_seqlens_q, seqlens_kv, block_table, nullptr, nullptr,
+                            k_cache, v_cache, num_seqs, num_tokens, max_blocks_per_seq, num_blocks,
+                            num_kv_heads, head_size, block_size, dtype, stream, false);
+}
+
+pa_status_t pa_scatter_kv_paged_fp8(const void* k_new, const void* v_new,
+                                    const int32_t* cu_seqlens_q, const int32_t* seqlens_kv,
+                                    const int32_t* block_table, const float* k_scale,
+                                    const float* v_scale, void* k_cache, void* v_cache,
+                                    int32_t num_seqs, int64_t num_tokens,
+                                    int32_t max_blocks_per_seq, int64_t num_blocks,
+                                    int32_t num_kv_heads, int32_t head_size, int32_t block_size,
+                                    int32_t dtype, void* stream) {
+  g_err[0] = 0;
+  return scatter_paged_impl(k_new, v_new, cu_seqlens_q, seqlens_kv, block_table, k_scale, v_scale,
+                            k_cache, v_cache, num_seqs, num_tokens, max_blocks_per_seq, num_blocks,
+                            num_kv_heads, head_size, block_size, dtype, stream, true);
 }
 
 static pa_status_t rotary_impl(const void* query, const void* key, const void* value,
@@ -639,17 +668,12 @@ pa_status_t pa_attention(const void* q, const int32_t* cu_seqlens_q, const int32
                         workspace_bytes, stream, false);
 }
 
-pa_status_t pa_attention_rope(const void* q, int64_t q_row_stride, const void* cos_cache,
-                              const void* sin_cache, int32_t max_position, int32_t rotary_dim,
-                              int32_t interleaved, const int32_t* cu_seqlens_q,
-                              const int32_t* seqlens_kv, const int32_t* block_table,
-                              const void* k_cache, const void* v_cache, void* out,
-                              int32_t num_seqs, int64_t num_tokens, int32_t max_blocks_per_seq,
-                              int64_t num_blocks, float scale, float softcap,
-                              int32_t local_window_size, int32_t num_heads, int32_t num_kv_heads,
-                              int32_t head_size, int32_t block_size, int32_t dtype,
-                              void* workspace, size_t workspace_bytes, void* stream) {
-  g_err[0] = 0;
+// Checks of the Q-source arguments shared by pa_attention_rope and
+// pa_attention_rope_fp8; fills *qs on success.
+static pa_status_t rope_source(const void* cos_cache, const void* sin_cache, int32_t max_position,
+                               int32_t rotary_dim, int32_t interleaved, int64_t q_row_stride,
+                               int64_t num_tokens, int32_t num_heads, int32_t head_size,
+                               QSource* qs) {
   if (num_heads >= 1 && head_size >= 1 && q_row_stride < (int64_t)num_heads * head_size)
     return fail(PA_ERR_INVALID_ARGUMENT, "q_row_stride=%lld < num_heads * head_size",
                 (long long)q_row_stride);
@@ -671,11 +695,66 @@ pa_status_t pa_attention_rope(const void* q, int64_t q_row_stride, const void* c
     if (!aligned16({cos_cache, sin_cache}))
       return fail(PA_ERR_INVALID_ARGUMENT, "tensor pointers must be 16-byte aligned");
   }
-  const QSource qs{q_row_stride, cos_cache, sin_cache, max_position, rotary_dim, interleaved};
+  *qs = QSource{q_row_stride, cos_cache, sin_cache, max_position, rotary_dim, interleaved};
+  return PA_OK;
+}
+
+// fp8 caches serve decode-shaped batches only: max_q_len * G within one tile.
+static pa_status_t fp8_q_len_bound(int32_t max_q_len, int32_t num_heads, int32_t num_kv_heads) {
+  if (max_q_len < 0) return fail(PA_ERR_INVALID_ARGUMENT, "max_q_len < 0");
+  if (num_kv_heads >= 1 && num_heads >= 1 && num_heads % num_kv_heads == 0 &&
+      (int64_t)max_q_len * (num_heads / num_kv_heads) > pa::kDecodeCols)
+    return fail(PA_ERR_NOT_IMPLEMENTED,
+                "fp8 caches: max_q_len * G = %lld exceeds %d (decode-shaped batches only)",
+                (long long)max_q_len * (num_heads / num_kv_heads), pa::kDecodeCols);
+  return PA_OK;
+}
+
+pa_status_t pa_attention_rope(const void* q, int64_t q_row_stride, const void* cos_cache,
+                              const void* sin_cache, int32_t max_position, int32_t rotary_dim,
+                              int32_t interleaved, const int32_t* cu_seqlens_q,
+                              const int32_t* seqlens_kv, const int32_t* block_table,
+                              const void* k_cache, const void* v_cache, void* out,
+                              int32_t num_seqs, int64_t num_tokens, int32_t max_blocks_per_seq,
+                              int64_t num_blocks, float scale, float softcap,
+                              int32_t local_window_size, int32_t num_heads, int32_t num_kv_heads,
+                              int32_t head_size, int32_t block_size, int32_t dtype,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+  g_err[0] = 0;
+  QSource qs{};
+  const pa_status_t rs = rope_source(cos_cache, sin_cache, max_position, rotary_dim, interleaved,
+                                     q_row_stride, num_tokens, num_heads, head_size, &qs);
+  if (rs != PA_OK) return rs;
   return attention_impl(q, cu_seqlens_q, seqlens_kv, block_table, k_cache, v_cache, nullptr,
                         nullptr, out, num_seqs, num_tokens, max_blocks_per_seq, num_blocks, scale,
                         softcap, local_window_size, num_heads, num_kv_heads, head_size,
                         block_size, dtype, workspace, workspace_bytes, stream, false, &qs);
+}
+
+pa_status_t pa_attention_rope_fp8(const void* q, int64_t q_row_stride, const void* cos_cache,
+                                  const void* sin_cache, int32_t max_position,
+                                  int32_t rotary_dim, int32_t interleaved,
+                                  const int32_t* cu_seqlens_q, const int32_t* seqlens_kv,
+                                  const int32_t* block_table, const void* k_cache,
+                                  const void* v_cache, const float* k_scale,
+                                  const float* v_scale, void* out, int32_t num_seqs,
+                                  int64_t num_tokens, int32_t max_q_len,
+                                  int32_t max_blocks_per_seq, int64_t num_blocks, float scale,
+                                  float softcap, int32_t local_window_size, int32_t num_heads,
+                                  int32_t num_kv_heads, int32_t head_size, int32_t block_size,
+                                  int32_t dtype, void* workspace, size_t workspace_bytes,
+                                  void* stream) {
+  g_err[0] = 0;
+  const pa_status_t bs = fp8_q_len_bound(max_q_len, num_heads, num_kv_heads);
+  if (bs != PA_OK) return bs;
+  QSource qs{};
+  const pa_status_t rs = rope_source(cos_cache, sin_cache, max_position, rotary_dim, interleaved,
+                                     q_row_stride, num_tokens, num_heads, head_size, &qs);
+  if (rs != PA_OK) return rs;
+  return attention_impl(q, cu_seqlens_q, seqlens_kv, block_table, k_cache, v_cache, k_scale,
+                        v_scale, out, num_seqs, num_tokens, max_blocks_per_seq, num_blocks, scale,
+                        softcap, local_window_size, num_heads, num_kv_heads, head_size,
+                        block_size, dtype, workspace, workspace_bytes, stream, true, &qs);
 }
 
 // ------------------------------------------------ allocation-free variant
@@ -755,12 +834,8 @@ pa_status_t pa_attention_fp8(const void* q, const int32_t* cu_seqlens_q,
                              int32_t dtype, void* workspace, size_t workspace_bytes,
                              void* stream) {
   g_err[0] = 0;
-  if (max_q_len < 0) return fail(PA_ERR_INVALID_ARGUMENT, "max_q_len < 0");
-  if (num_kv_heads >= 1 && num_heads >= 1 && num_heads % num_kv_heads == 0 &&
-      (int64_t)max_q_len * (num_heads / num_kv_heads) > pa::kDecodeCols)
-    return fail(PA_ERR_NOT_IMPLEMENTED,
-                "fp8 caches: max_q_len * G = %lld exceeds %d (decode-shaped batches only)",
-                (long long)max_q_len * (num_heads / num_kv_heads), pa::kDecodeCols);
+  const pa_status_t bs = fp8_q_len_bound(max_q_len, num_heads, num_kv_heads);
+  if (bs != PA_OK) return bs;
   return attention_impl(q, cu_seqlens_q, seqlens_kv, block_table, k_cache, v_cache, k_scale,
                         v_scale, out, num_seqs, num_tokens, max_blocks_per_seq, num_blocks, scale,
                         softcap, local_window_size, num_heads, num_kv_heads, head_size, block_size, dtype, workspace,

@@ -126,10 +126,18 @@ __device__ __forceinline__ void decode_items(const AttnArgs& a) {
         }
       } else {
         const float* ks = a.k_scale + (int64_t)kh * D;
+        // Q rotated as loaded (pa_attention_rope_fp8) and rounded to the
+        // input dtype, as the rotary scatter's q_out would hold it, before
+        // the K scale is applied.
+        const int pos = past + ng;
+        const bool rot = a.rope_dim > 0 && valid && pos < a.rope_max_pos;
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
           const int d0 = (NS * kq + s) * 8;
-          const u32x4_t x = ld16(qrow + d0);
+          u32x4_t x = ld16(qrow + d0);
+          if (rot && d0 < a.rope_dim)
+            x = rope_chunk<T>(x, qrow, d0, pos, (const uint16_t*)a.rope_cos,
+                              (const uint16_t*)a.rope_sin, a.rope_dim, a.rope_inter != 0);
           const float4_t s0 = *reinterpret_cast<const float4_t*>(ks + d0);
           const float4_t s1 = *reinterpret_cast<const float4_t*>(ks + d0 + 4);
           const float2 f0 = Elt<T>::unpack2(x[0]), f1 = Elt<T>::unpack2(x[1]);

@@ -156,10 +156,13 @@ hipError_t launch_scatter_fp8(const void* k_new, const void* v_new, const int32_
                               const float* k_scale, const float* v_scale, void* kc, void* vc,
                               int64_t num_tokens, int32_t row_elems, int32_t dtype,
                               hipStream_t st);
+// kv8: fp8 caches (codes quantized with k_scale / v_scale); otherwise the
+// scales are unused and the rows are copied.
 hipError_t launch_scatter_paged(const void* k_new, const void* v_new, const int32_t* cu,
                                 const int32_t* lens, const int32_t* table, void* kc, void* vc,
-                                int32_t num_seqs, int64_t num_tokens, int32_t max_blocks,
-                                int32_t block_size, int32_t row_bytes, hipStream_t st);
+                                const float* k_scale, const float* v_scale, int32_t num_seqs,
+                                int64_t num_tokens, int32_t max_blocks, int32_t block_size,
+                                int32_t row_elems, int32_t dtype, bool kv8, hipStream_t st);
 // Rotary embedding + packed-QKV split + scatter of one batch of new tokens.
 struct RotaryArgs {
   const void* query;      // [T, Hq, D], or packed [T, Hq + 2 Hk, D] when key is null

@@ -100,10 +100,15 @@ hipError_t launch_scatter_fp8(const void* k_new, const void* v_new, const int32_
 // pos = past_b + (t - cu[b]) with past_b = seqlens_kv[b] - q_len_b, slot =
 // block_table[b][pos / bs] * bs + pos % bs; then the row copy as above.  A
 // negative table entry skips the token.
+// KV8: the caches hold e4m3 codes; each 8-element chunk is quantized as in
+// scatter_fp8_kernel (quantize8, per-channel scales) instead of copied, so
+// the codes equal those of pa_scatter_kv_fp8 on the same slots.
+template <typename T, bool KV8>
 __global__ __launch_bounds__(256) void scatter_paged_kernel(
     const u32x4_t* __restrict__ k_new, const u32x4_t* __restrict__ v_new,
     const int32_t* __restrict__ cu, const int32_t* __restrict__ lens,
-    const int32_t* __restrict__ table, u32x4_t* __restrict__ kc, u32x4_t* __restrict__ vc,
+    const int32_t* __restrict__ table, void* __restrict__ kc, void* __restrict__ vc,
+    const float4_t* __restrict__ k_scale, const float4_t* __restrict__ v_scale,
     int32_t num_seqs, int64_t num_tokens, int32_t max_blocks, int32_t block_size,
     int32_t row_chunks) {
   const int lane = threadIdx.x & 63;
@@ -127,21 +132,33 @@ __global__ __launch_bounds__(256) void scatter_paged_kernel(
     for (int c = lane; c < row_chunks; c += 64) {
       const int64_t src = t * row_chunks + c;
       const int64_t dst = slot * row_chunks + c;
-      kc[dst] = __builtin_nontemporal_load(&k_new[src]);
-      vc[dst] = __builtin_nontemporal_load(&v_new[src]);
+      const u32x4_t kx = __builtin_nontemporal_load(&k_new[src]);   // new rows are read once
+      const u32x4_t vx = __builtin_nontemporal_load(&v_new[src]);
+      if constexpr (KV8) {
+        reinterpret_cast<u32x2_t*>(kc)[dst] = quantize8<T>(kx, k_scale[2 * c], k_scale[2 * c + 1]);
+        reinterpret_cast<u32x2_t*>(vc)[dst] = quantize8<T>(vx, v_scale[2 * c], v_scale[2 * c + 1]);
+      } else {
+        reinterpret_cast<u32x4_t*>(kc)[dst] = kx;
+        reinterpret_cast<u32x4_t*>(vc)[dst] = vx;
+      }
     }
   }
 }
 
 hipError_t launch_scatter_paged(const void* k_new, const void* v_new, const int32_t* cu,
                                 const int32_t* lens, const int32_t* table, void* kc, void* vc,
-                                int32_t num_seqs, int64_t num_tokens, int32_t max_blocks,
-                                int32_t block_size, int32_t row_bytes, hipStream_t st) {
+                                const float* k_scale, const float* v_scale, int32_t num_seqs,
+                                int64_t num_tokens, int32_t max_blocks, int32_t block_size,
+                                int32_t row_elems, int32_t dtype, bool kv8, hipStream_t st) {
   int64_t blocks = (num_tokens + 3) / 4;   // 4 waves (tokens) per work-group
   if (blocks > 16384) blocks = 16384;
-  hipLaunchKernelGGL(scatter_paged_kernel, dim3((unsigned)blocks), dim3(256), 0, st,
-                     (const u32x4_t*)k_new, (const u32x4_t*)v_new, cu, lens, table, (u32x4_t*)kc,
-                     (u32x4_t*)vc, num_seqs, num_tokens, max_blocks, block_size, row_bytes / 16);
+  // 16-bit caches: a byte copy, the same kernel for both dtypes.
+  auto kern = !kv8 ? scatter_paged_kernel<F16, false>
+              : dtype == 1 ? scatter_paged_kernel<BF16, true> : scatter_paged_kernel<F16, true>;
+  hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(256), 0, st, (const u32x4_t*)k_new,
+                     (const u32x4_t*)v_new, cu, lens, table, kc, vc, (const float4_t*)k_scale,
+                     (const float4_t*)v_scale, num_seqs, num_tokens, max_blocks, block_size,
+                     row_elems / 8);
   return hipGetLastError();
 }
 

@@ -79,6 +79,15 @@ int main() {
          PA_ERR_HIP, "paged scatter valid (stubbed launch)");
   expect(pa_scatter_kv_fp8(P, P, I, nullptr, F, P, P, 5, 8, 2, 64, 16, PA_F16, nullptr),
          PA_ERR_INVALID_ARGUMENT, "fp8 scatter null scale");
+  expect(pa_scatter_kv_paged_fp8(P, P, I, I, I, F, nullptr, P, P, 2, 5, 2, 8, 2, 64, 16, PA_F16,
+                                 nullptr),
+         PA_ERR_INVALID_ARGUMENT, "fp8 paged scatter null scale");
+  expect(pa_scatter_kv_paged_fp8(P, P, I, I, I, F, F, P, P, 2, 5, 1 << 28, 8, 2, 64, 16, PA_F16,
+                                 nullptr),
+         PA_ERR_NOT_IMPLEMENTED, "fp8 paged scatter table beyond INT32_MAX");
+  expect(pa_scatter_kv_paged_fp8(P, P, I, I, I, F, F, P, P, 2, 5, 2, 8, 2, 64, 16, PA_BF16,
+                                 nullptr),
+         PA_ERR_HIP, "fp8 paged scatter valid (stubbed launch)");
   expect(pa_seqlens_from_past(I, nullptr, (int32_t*)P, 3, nullptr), PA_ERR_INVALID_ARGUMENT,
          "lengths null");
 
@@ -138,6 +147,17 @@ int main() {
   expect(pa_attention_rope(P, 8 * 64, P, P, 64, 64, 1, I, I, I, P, P, O, 2, 5, 2, 8, 0.125f,
                            0.f, 0, 4, 2, 64, 16, PA_BF16, P, ws, nullptr),
          PA_ERR_HIP, "rope attention valid (stubbed launch)");
+
+  // pa_attention_rope_fp8: the rotated Q load over fp8 caches.
+  expect(pa_attention_rope_fp8(P, 8 * 64, P, P, 64, 64, 0, I, I, I, P, P, F, F, O, 2, 5, 9, 2, 8,
+                               0.125f, 0.f, 0, 4, 2, 64, 16, PA_F16, P, ws, nullptr),
+         PA_ERR_NOT_IMPLEMENTED, "rope fp8 attention q_len * G > 16");
+  expect(pa_attention_rope_fp8(P, 8 * 64, P, nullptr, 64, 64, 0, I, I, I, P, P, F, F, O, 2, 5, 4,
+                               2, 8, 0.125f, 0.f, 0, 4, 2, 64, 16, PA_F16, P, ws, nullptr),
+         PA_ERR_INVALID_ARGUMENT, "rope fp8 attention cos without sin");
+  expect(pa_attention_rope_fp8(P, 8 * 64, P, P, 64, 64, 1, I, I, I, P, P, F, F, O, 2, 5, 4, 2, 8,
+                               0.125f, 0.f, 0, 4, 2, 64, 16, PA_BF16, P, ws, nullptr),
+         PA_ERR_HIP, "rope fp8 attention valid (stubbed launch)");
 
   // Shapes at the kernels' 32-bit limits, and misaligned tensors.
   if (pa_attention_workspace_size(1, 8, 1, 8191, 8191, 128, 1024) == 0) ++g_failures;

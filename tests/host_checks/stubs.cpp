@@ -18,8 +18,8 @@ hipError_t launch_scatter_fp8(const void*, const void*, const int32_t*, const fl
   return hipErrorNotReady;
 }
 hipError_t launch_scatter_paged(const void*, const void*, const int32_t*, const int32_t*,
-                                const int32_t*, void*, void*, int32_t, int64_t, int32_t, int32_t,
-                                int32_t, hipStream_t) {
+                                const int32_t*, void*, void*, const float*, const float*, int32_t,
+                                int64_t, int32_t, int32_t, int32_t, int32_t, bool, hipStream_t) {
   return hipErrorNotReady;
 }
 hipError_t launch_rotary_scatter(const RotaryArgs&, int, hipStream_t) { return hipErrorNotReady; }

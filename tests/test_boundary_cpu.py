@@ -345,6 +345,77 @@ def test_attention_fp8_empty_call_is_ok(L):
     assert _attn8(L, T=0, mq=0) == _lib.PA_OK
 
 
+def _scatter_paged8(L, **kw):
+    a = dict(k=FAKE, v=FAKE, cu=FAKE, lens=FAKE, table=FAKE, ks=FAKE, vs=FAKE, kc=FAKE, vc=FAKE,
+             B=2, T=5, MB=2, NB=8, hk=2, d=64, bs=16, dtype=0)
+    a.update(kw)
+    return L.pa_scatter_kv_paged_fp8(a["k"], a["v"], a["cu"], a["lens"], a["table"], a["ks"],
+                                     a["vs"], a["kc"], a["vc"], a["B"], a["T"], a["MB"], a["NB"],
+                                     a["hk"], a["d"], a["bs"], a["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(d=60), _lib.PA_ERR_NOT_IMPLEMENTED),
+    (dict(dtype=2), _lib.PA_ERR_NOT_IMPLEMENTED),
+    (dict(T=-1), _lib.PA_ERR_INVALID_ARGUMENT),
+    (dict(B=0), _lib.PA_ERR_INVALID_ARGUMENT),
+    (dict(MB=0), _lib.PA_ERR_INVALID_ARGUMENT),
+    (dict(hk=0), _lib.PA_ERR_INVALID_ARGUMENT),
+    (dict(cu=None), _lib.PA_ERR_INVALID_ARGUMENT),
+    (dict(ks=None), _lib.PA_ERR_INVALID_ARGUMENT),
+    (dict(vs=None), _lib.PA_ERR_INVALID_ARGUMENT),
+    (dict(ks=ctypes.c_void_p(0x1004)), _lib.PA_ERR_INVALID_ARGUMENT),   # unaligned scales
+    (dict(kc=ctypes.c_void_p(0x1008)), _lib.PA_ERR_INVALID_ARGUMENT),   # unaligned cache
+    (dict(NB=1 << 30, bs=16), _lib.PA_ERR_NOT_IMPLEMENTED),
+    (dict(MB=1 << 28, bs=16), _lib.PA_ERR_NOT_IMPLEMENTED),
+])
+def test_scatter_paged_fp8_rejects_on_host(L, kw, status):
+    assert _scatter_paged8(L, **kw) == status
+    assert L.pa_last_error() != b""
+
+
+def test_scatter_paged_fp8_empty_call_is_ok(L):
+    assert _scatter_paged8(L, T=0, k=None, v=None, ks=None, vs=None) == _lib.PA_OK
+
+
+def _attn_rope8(L, **kw):
+    a = dict(q=FAKE, stride=8 * 64, cos=FAKE, sin=FAKE, maxpos=64, rdim=64, inter=0, cu=FAKE,
+             lens=FAKE, table=FAKE, kc=FAKE, vc=FAKE, ks=FAKE, vs=FAKE, out=FAKE_OUT, B=2, T=5,
+             mq=4, MB=2, NB=8, scale=0.125, cap=0.0, win=0, hq=4, hk=2, d=64, bs=16, dtype=0,
+             ws=FAKE, wsb=1 << 30)
+    a.update(kw)
+    return L.pa_attention_rope_fp8(a["q"], a["stride"], a["cos"], a["sin"], a["maxpos"],
+                                   a["rdim"], a["inter"], a["cu"], a["lens"], a["table"], a["kc"],
+                                   a["vc"], a["ks"], a["vs"], a["out"], a["B"], a["T"], a["mq"],
+                                   a["MB"], a["NB"], a["scale"], a["cap"], a["win"], a["hq"],
+                                   a["hk"], a["d"], a["bs"], a["dtype"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(mq=9), _lib.PA_ERR_NOT_IMPLEMENTED),          # 9 * G 2 = 18 columns > 16
+    (dict(mq=-1), _lib.PA_ERR_INVALID_ARGUMENT),
+    (dict(ks=None), _lib.PA_ERR_INVALID_ARGUMENT),
+    (dict(vs=ctypes.c_void_p(0x1004)), _lib.PA_ERR_INVALID_ARGUMENT),   # unaligned scales
+    (dict(stride=4 * 64 - 8), _lib.PA_ERR_INVALID_ARGUMENT),   # below num_heads * head_size
+    (dict(stride=4 * 64 + 4), _lib.PA_ERR_INVALID_ARGUMENT),   # rows not 16-byte aligned
+    (dict(sin=None), _lib.PA_ERR_INVALID_ARGUMENT),            # cos without sin
+    (dict(rdim=80), _lib.PA_ERR_INVALID_ARGUMENT),             # beyond head_size
+    (dict(rdim=24), _lib.PA_ERR_NOT_IMPLEMENTED),              # not a multiple of 16
+    (dict(maxpos=0), _lib.PA_ERR_INVALID_ARGUMENT),
+    (dict(d=96, stride=8 * 96), _lib.PA_ERR_NOT_IMPLEMENTED),  # pa_attention's own limits
+    (dict(wsb=16), _lib.PA_ERR_WORKSPACE_TOO_SMALL),
+    (dict(out=ctypes.c_void_p(0x1000 + 4 * 8 * 64 * 2)), _lib.PA_ERR_INVALID_ARGUMENT),  # in q's rows
+])
+def test_attention_rope_fp8_rejects_on_host(L, kw, status):
+    assert _attn_rope8(L, **kw) == status
+    assert L.pa_last_error() != b""
+
+
+def test_attention_rope_fp8_empty_call_is_ok(L):
+    assert _attn_rope8(L, T=0, q=None, out=None, ws=None, mq=0) == _lib.PA_OK
+    assert _attn_rope8(L, T=0, cos=None, sin=None, rdim=0, maxpos=0, mq=0) == _lib.PA_OK
+
+
 def test_profile_kind_selection(L):
     """Profiling state is host-only: selecting kinds, enabling and reading
     with nothing recorded need no GPU; unknown kind names are rejected."""

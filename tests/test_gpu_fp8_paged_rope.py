@@ -1,0 +1,212 @@
+"""The op-level scatter and the rotated Q load over fp8 (e4m3) caches,
+through the C ABI: pa_scatter_kv_paged_fp8 and pa_attention_rope_fp8.
+
+Bars:
+- pa_scatter_kv_paged_fp8: whole caches bit for bit equal to the oracle's
+  fp8 scatter (oracle/kv_fp8.py) at the slots the oracle's in-op addressing
+  derives (oracle.slots_from_block_table), into NaN-coded caches, a negative
+  table entry skipping its tokens; and equal to pa_scatter_kv_fp8 on those
+  slots.
+- pa_attention_rope_fp8: bitwise the two-step path (pa_rotary_scatter_kv_fp8
+  writing the rotated Q, then pa_attention_fp8 on it), and within the fp8
+  attention bars of the oracle's rotation (rounded to the dtype) followed by
+  the oracle's fp8 attention over the same codes.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_cache_pa_amd as pa
+from oracle import kv_fp8
+from oracle import rotary as R
+from paged_kv_cache_pa_amd import workloads as W
+from gpu_util import FP8_NAN, TOL, max_err, require_gpu
+from pa_testutil import to_np64
+
+pytestmark = pytest.mark.gpu
+
+
+def _log(msg):
+    print(msg, flush=True)
+
+
+def _codes(wl):
+    shape = (wl.num_blocks, wl.block_size, wl.num_kv_heads, wl.head_size)
+    return (torch.full(shape, FP8_NAN, dtype=torch.uint8, device="cuda"),
+            torch.full(shape, FP8_NAN, dtype=torch.uint8, device="cuda"))
+
+
+SCATTER_CASES = [
+    ("tiny f16 D64", W.tiny),
+    ("f16 D128 G4 empty sequence", lambda: W.custom([3, 0, 1, 7], [40, 5, 1, 300], 8, 2, 128, 16)),
+    ("bf16 D128 G8 bs32", lambda: W.custom([9, 1, 33], [1000, 70, 33], 16, 2, 128, 32,
+                                          dtype="bf16")),
+    ("bf16 D64 MHA bs256", lambda: W.small((16, 4), (64, 32), 8, 8, dtype="bf16")),
+]
+
+
+@pytest.mark.parametrize("name,make", SCATTER_CASES, ids=[c[0] for c in SCATTER_CASES])
+def test_scatter_paged_fp8_bit_exact(name, make):
+    wl = make()
+    _log(f"fp8 paged scatter: {name}")
+    require_gpu()
+    vals = {k: v.cuda() for k, v in W.make_values(wl).items()}
+    rows = torch.from_numpy(wl.new_rows).cuda()
+    k_new, v_new = vals["k_all"][rows].contiguous(), vals["v_all"][rows].contiguous()
+    table = wl.block_table.astype(np.int32).copy()
+    # Drop the block of the first new token of the last non-empty sequence.
+    b_last = int(np.flatnonzero(wl.q_lens > 0)[-1])
+    pos0 = int(wl.seqlens_kv[b_last] - wl.q_lens[b_last])
+    table[b_last, pos0 // wl.block_size] = -1
+    slots = oracle.slots_from_block_table(wl.cu_seqlens_q, wl.seqlens_kv, table, wl.block_size)
+    slots[slots < 0] = -1    # tokens whose table entry is negative are skipped
+    assert (slots < 0).any() and (slots >= 0).any()
+    ks, vs = W.fp8_scales(wl)
+    shape = (wl.num_blocks, wl.block_size, wl.num_kv_heads, wl.head_size)
+    kref = np.full(shape, FP8_NAN, dtype=np.uint8)
+    vref = np.full(shape, FP8_NAN, dtype=np.uint8)
+    kv_fp8.scatter_kv_fp8(k_new.float().cpu().numpy(), v_new.float().cpu().numpy(), slots, ks, vs,
+                          kref, vref, wl.block_size)
+    d_ks, d_vs = torch.from_numpy(ks).cuda(), torch.from_numpy(vs).cuda()
+    kc, vc = _codes(wl)
+    pa.pa_scatter_kv_paged_fp8(k_new, v_new, torch.from_numpy(wl.cu_seqlens_q).cuda(),
+                               torch.from_numpy(wl.seqlens_kv.astype(np.int32)).cuda(),
+                               torch.from_numpy(table).cuda(), d_ks, d_vs, kc, vc)
+    kc2, vc2 = _codes(wl)
+    pa.pa_scatter_kv_fp8(k_new, v_new, torch.from_numpy(slots.astype(np.int32)).cuda(), d_ks, d_vs,
+                         kc2, vc2)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(kc.cpu().numpy(), kref)
+    np.testing.assert_array_equal(vc.cpu().numpy(), vref)
+    assert torch.equal(kc, kc2) and torch.equal(vc, vc2)
+
+
+def _rope_setup(wl, rdim, inter):
+    """Device values, packed QKV rows of this step's tokens, rope tables, the
+    fp8 scales, and fp8 caches holding every history key rotated at its
+    position (one K/V-only rotary scatter over all positions) and its value."""
+    require_gpu()
+    vals = W.make_values(wl)
+    dev = {k: v.cuda() for k, v in vals.items()}
+    rows = torch.from_numpy(wl.new_rows).cuda()
+    T = wl.num_tokens
+    q, k_new, v_new = dev["q"], dev["k_all"][rows].contiguous(), dev["v_all"][rows].contiguous()
+    d = dict(q=q, k_all=dev["k_all"], v_all=dev["v_all"],
+             cu=torch.from_numpy(wl.cu_seqlens_q).cuda(),
+             lens=torch.from_numpy(wl.seqlens_kv.astype(np.int32)).cuda(),
+             table=torch.from_numpy(wl.block_table.astype(np.int32)).cuda())
+    d["kc"], d["vc"] = _codes(wl)
+    d["packed"] = torch.cat([q.reshape(T, -1), k_new.reshape(T, -1), v_new.reshape(T, -1)],
+                            dim=1).contiguous()
+    cos, sin = W.rope_tables(int(wl.seqlens_kv.max()), rdim, wl.dtype)
+    d["cos"], d["sin"] = cos.cuda(), sin.cuda()
+    ks, vs = W.fp8_scales(wl)
+    d["ks_np"], d["vs_np"] = ks, vs
+    d["ks"], d["vs"] = torch.from_numpy(ks).cuda(), torch.from_numpy(vs).cuda()
+    kv_cu = torch.from_numpy(wl.kv_cu.astype(np.int32)).cuda()
+    assert pa.pa_rotary_scatter_kv_fp8(None, kv_cu, d["lens"], d["table"], d["ks"], d["vs"],
+                                       d["kc"], d["vc"], wl.num_heads, wl.num_kv_heads,
+                                       key=d["k_all"], value=d["v_all"], cos_cache=d["cos"],
+                                       sin_cache=d["sin"], interleaved=inter,
+                                       write_q=False) is None
+    torch.cuda.synchronize()
+    return d
+
+
+def _two_step(wl, d, inter, **opts):
+    q_rot = pa.pa_rotary_scatter_kv_fp8(d["packed"], d["cu"], d["lens"], d["table"], d["ks"],
+                                        d["vs"], d["kc"], d["vc"], wl.num_heads, wl.num_kv_heads,
+                                        cos_cache=d["cos"], sin_cache=d["sin"], interleaved=inter)
+    out = pa.pa_attention_fp8(q_rot, d["cu"], d["lens"], d["table"], d["kc"], d["vc"], d["ks"],
+                              d["vs"], wl.scale, wl.num_heads, wl.num_kv_heads,
+                              int(wl.q_lens.max()), **opts)
+    torch.cuda.synchronize()
+    return q_rot, out
+
+
+def _fused(wl, d, inter, **opts):
+    assert pa.pa_rotary_scatter_kv_fp8(d["packed"], d["cu"], d["lens"], d["table"], d["ks"],
+                                       d["vs"], d["kc"], d["vc"], wl.num_heads, wl.num_kv_heads,
+                                       cos_cache=d["cos"], sin_cache=d["sin"], interleaved=inter,
+                                       write_q=False) is None
+    out = pa.pa_attention_rope_fp8(d["packed"].view(wl.num_tokens, -1, wl.head_size), d["cu"],
+                                   d["lens"], d["table"], d["kc"], d["vc"], d["ks"], d["vs"],
+                                   wl.scale, wl.num_heads, wl.num_kv_heads, int(wl.q_lens.max()),
+                                   cos_cache=d["cos"], sin_cache=d["sin"], interleaved=inter,
+                                   **opts)
+    torch.cuda.synchronize()
+    return out
+
+
+ROPE_CASES = [
+    # name, workload (decode-shaped: q_len * G <= 16), rotary_dim, interleaved, options
+    ("f16 D128 R128 split G4 multi-split",
+     lambda: W.custom([1, 1, 4, 1], [40, 3000, 300, 17], 16, 4, 128, 16), 128, False, {}),
+    ("f16 D128 R128 interleaved G4",
+     lambda: W.custom([1, 1, 4, 1], [40, 3000, 300, 17], 16, 4, 128, 16), 128, True, {}),
+    ("bf16 D128 R64 split G8 cap30 window500",
+     lambda: W.custom([1, 2, 1, 1], [5000, 33, 700, 2100], 64, 8, 128, 16, dtype="bf16"), 64,
+     False, dict(softcap=30.0, local_window_size=500)),
+    ("bf16 D64 R32 interleaved MHA",
+     lambda: W.custom([3, 9, 1], [3, 50, 800], 4, 4, 64, 16, dtype="bf16"), 32, True, {}),
+    ("f16 D128 R48 split G16 bs64",
+     lambda: W.custom([1, 1, 1], [600, 16, 2000], 32, 2, 128, 64), 48, False, {}),
+]
+
+
+@pytest.mark.parametrize("name,make,rdim,inter,opts", ROPE_CASES, ids=[c[0] for c in ROPE_CASES])
+def test_rope_fp8_matches_two_step_bitwise(name, make, rdim, inter, opts):
+    wl = make()
+    _log(f"fused rope over fp8 caches vs two-step: {name}")
+    d = _rope_setup(wl, rdim, inter)
+    _, ref = _two_step(wl, d, inter, **opts)
+    ref = ref.clone()
+    kc, vc = d["kc"].clone(), d["vc"].clone()
+    out = _fused(wl, d, inter, **opts)
+    # the Q-less scatter rewrote the same codes
+    assert torch.equal(kc, d["kc"]) and torch.equal(vc, d["vc"])
+    assert torch.isfinite(out).all()
+    assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
+
+
+@pytest.mark.parametrize("inter", [False, True])
+def test_rope_fp8_against_oracle(inter):
+    """The fused path against the oracle's rotation of Q (rounded to the
+    dtype, as the kernels round it) and the oracle's fp8 attention over the
+    kernel's codes (the codes themselves are pinned by the rotary fp8
+    scatter tests)."""
+    wl = W.custom([1, 1, 4, 1], [40, 3000, 300, 17], 16, 4, 128, 16)
+    _log(f"fused rope over fp8 caches vs oracle, interleaved={inter}")
+    d = _rope_setup(wl, 96, inter)
+    out = _fused(wl, d, inter)
+    cos, sin = to_np64(d["cos"]), to_np64(d["sin"])
+    rnd = lambda x: to_np64(torch.from_numpy(x).to(torch.float16))  # noqa: E731
+    q_r = rnd(R.rotary_embedding(to_np64(d["q"]), R.token_positions(wl.cu_seqlens_q,
+                                                                     wl.seqlens_kv),
+                                 cos, sin, inter))
+    ref = kv_fp8.attention_fp8(q_r, wl.cu_seqlens_q, wl.seqlens_kv, wl.block_table,
+                               d["kc"].cpu().numpy(), d["vc"].cpu().numpy(), d["ks_np"],
+                               d["vs_np"], wl.scale, wl.num_heads, wl.num_kv_heads,
+                               wl.block_size)
+    err = max_err(out, ref)
+    _log(f"  max error {err:.3g}")
+    assert err <= TOL[wl.dtype]
+
+
+def test_rope_fp8_without_tables_is_pa_attention_fp8():
+    """No tables: pa_attention_rope_fp8 on the packed rows equals
+    pa_attention_fp8 on the Q part copied out, bitwise."""
+    wl = W.custom([1, 1, 2], [700, 33, 1200], 16, 8, 128, 16)
+    _log("fp8 strided Q without tables")
+    d = _rope_setup(wl, 128, False)
+    T = wl.num_tokens
+    q_plain = d["packed"][:, :wl.num_heads * wl.head_size].contiguous()
+    ref = pa.pa_attention_fp8(q_plain.view(T, wl.num_heads, wl.head_size), d["cu"], d["lens"],
+                              d["table"], d["kc"], d["vc"], d["ks"], d["vs"], wl.scale,
+                              wl.num_heads, wl.num_kv_heads, int(wl.q_lens.max()))
+    out = pa.pa_attention_rope_fp8(d["packed"].view(T, -1, wl.head_size), d["cu"], d["lens"],
+                                   d["table"], d["kc"], d["vc"], d["ks"], d["vs"], wl.scale,
+                                   wl.num_heads, wl.num_kv_heads, int(wl.q_lens.max()))
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
