@@ -210,3 +210,29 @@ def test_rope_fp8_without_tables_is_pa_attention_fp8():
                                    wl.num_heads, wl.num_kv_heads, int(wl.q_lens.max()))
     torch.cuda.synchronize()
     assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
+
+
+def test_full_size_pure_decode_fp8_paged_scatter_and_rope_bitwise():
+    """The pure-decode workload (256 sequences, contexts to 8192, 32/8
+    heads) in the launch configuration the benchmark times: the fp8 paged
+    scatter's whole caches equal pa_scatter_kv_fp8's on the workload's own
+    slots, and the rotated Q load equals the two-step path bitwise."""
+    wl = W.by_index(3)
+    _log(f"fp8 paged scatter and rope attention, full size: {wl.name}")
+    d = _rope_setup(wl, wl.head_size, False)
+    rows = torch.from_numpy(wl.new_rows).cuda()
+    k_new, v_new = d["k_all"][rows].contiguous(), d["v_all"][rows].contiguous()
+    kc_a, vc_a = d["kc"].clone(), d["vc"].clone()
+    kc_b, vc_b = d["kc"].clone(), d["vc"].clone()
+    pa.pa_scatter_kv_fp8(k_new, v_new, torch.from_numpy(wl.slot_mapping.astype(np.int32)).cuda(),
+                         d["ks"], d["vs"], kc_a, vc_a)
+    pa.pa_scatter_kv_paged_fp8(k_new, v_new, d["cu"], d["lens"], d["table"], d["ks"], d["vs"],
+                               kc_b, vc_b)
+    torch.cuda.synchronize()
+    assert torch.equal(kc_a, kc_b) and torch.equal(vc_a, vc_b)
+    del kc_a, vc_a, kc_b, vc_b
+    _, ref = _two_step(wl, d, False)
+    ref = ref.clone()
+    out = _fused(wl, d, False)
+    assert torch.isfinite(out).all()
+    assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
